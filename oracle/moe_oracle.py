@@ -1,0 +1,361 @@
+"""CPU oracle of the MoE layer forward -- TEST INFRASTRUCTURE, not product code.
+
+Plain, slow, float64 NumPy.  Only the tests, the smoke check and the bench's
+CPU-baseline leg may import it; the HIP library never calls it and shares no
+code, table or helper with it.
+
+What it computes follows the per-token routing path the pages describe:
+a small linear gate scores every expert, a softmax turns the scores into
+probabilities, the top-k experts are kept, each transforms the token, and their
+outputs are summed weighted by the gate scores ("Expert-Parallel MoE
+Inference: Serving Sparse Models at Scale", §Deeper Analysis: Routing, Balance,
+and a Capacity Worked Example, Figure 2; the same chain router -> top-k ->
+dispatch -> expert FFN -> combine -> original token order in "MoE Expert
+Parallelism in Practice", §Core Principles 1; experts run as grouped GEMMs and
+combine is a weighted sum in "Tensor vs Expert vs Data Parallelism for MoE
+Serving", §Deeper Analysis, Figure 2).  Dispatch is drop-free: no token is
+dropped for capacity (the drop-free path preferred in "Expert-Parallel MoE
+Inference", §Capacity factor and token dropping).
+
+Readings the pages leave open, and the workload definitions fix:
+  * expert FFN is SwiGLU: h = silu(x W1) * (x W3), y = h W2, silu(u) = u*sigmoid(u);
+  * score is softmax or sigmoid; gates renormalised over the chosen k;
+  * optional group limit: E experts in n_group contiguous groups, a group's
+    score is the sum of its two largest expert scores, only the best
+    topk_group groups stay eligible (the single-GPU form of the node-limited
+    routing in "Expert-Parallel MoE Inference", §Load imbalance and how to
+    fight it, and "Expert Parallelism for MoE Serving", §Real-World
+    Implementation);
+  * the router bias is added to the logits and used for both selection and
+    gates;
+  * ties go to the lower expert (group) id; the k outputs are in descending
+    score order;
+  * a shared expert, when present, is always on with coefficient 1 (the
+    "shared expert" of DeepSeek-V3 in "Tensor vs Expert vs Data Parallelism",
+    §Context and Background);
+  * the activation dtype rounding (round to nearest even) is applied exactly
+    where the layer stores an activation tensor: h, y_perm, the shared
+    expert's h and y, and out.  Everything else is exact float64 on the stored
+    input values.
+
+Storage conventions: weights are stored out x in (W1[e][j][i] is the math's
+W1_e[i, j]); bf16 as uint16 bit patterns; e4m3 as uint8 OCP E4M3 codes with a
+float32 scale per output channel.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Storage decoding and activation rounding (exact)
+# --------------------------------------------------------------------------
+
+
+def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 is the top half of a float32)."""
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of every OCP E4M3 code: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    Exponent 0 is subnormal (m * 2^-9); code S.1111.111 is NaN; no infinities.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = s * m * 2.0 ** -9
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    if dtype == "e4m3":
+        return e4m3_to_f64(a)
+    raise ValueError(dtype)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), as float64.
+
+    bf16 keeps 8 significant bits; the smallest normal is 2^-126 and below it
+    the spacing is fixed at 2^-133.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)                      # a = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)
+    r = np.rint(np.ldexp(a, 8 - e))         # exact scaling, then half-to-even
+    out = np.ldexp(r, e - 8)
+    return np.where(np.abs(out) > 3.3895313892515355e38, np.copysign(np.inf, a), out)
+
+
+def round_act(a: np.ndarray, act: str) -> np.ndarray:
+    if act == "f32":
+        return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if act == "bf16":
+        return round_bf16(a)
+    raise ValueError(act)
+
+
+# --------------------------------------------------------------------------
+# Routing
+# --------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class RouteSpec:
+    k: int
+    score: str = "softmax"     # "softmax" | "sigmoid"
+    renorm: bool = True
+    n_group: int = 0
+    topk_group: int = 0
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias: Optional[np.ndarray]) -> np.ndarray:
+    """z[t, e] = sum_i x[t, i] * Wr[e][i] + b[e]: the small linear gate that
+    scores every expert for every token ("Expert-Parallel MoE Inference",
+    §Deeper Analysis, first paragraph).  Wr is stored out x in, [E][d]."""
+    z = x @ w_router.T
+    if bias is not None:
+        z = z + np.asarray(bias, dtype=np.float64)[None, :]
+    return z
+
+
+def expert_scores(z: np.ndarray, score: str) -> np.ndarray:
+    """Softmax over the E logits (same passage), or the element-wise sigmoid."""
+    if score == "softmax":
+        m = z.max(axis=1, keepdims=True)
+        p = np.exp(z - m)
+        return p / p.sum(axis=1, keepdims=True)
+    if score == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-z))
+    raise ValueError(score)
+
+
+def _order_desc(values: np.ndarray) -> np.ndarray:
+    """Per row, indices ordered by (value descending, index ascending)."""
+    ids = np.broadcast_to(np.arange(values.shape[1]), values.shape)
+    return np.lexsort((ids, -values), axis=-1)
+
+
+def group_scores(s: np.ndarray, n_group: int) -> np.ndarray:
+    """Score of each contiguous expert group: the sum of its two largest scores."""
+    T, E = s.shape
+    sg = np.sort(s.reshape(T, n_group, E // n_group), axis=2)
+    return sg[:, :, -1] + sg[:, :, -2]
+
+
+def eligible(s: np.ndarray, spec: RouteSpec) -> np.ndarray:
+    """Boolean [T, E]: experts a token may choose.  With a group limit only the
+    experts of the topk_group best groups (ties to the lower group id)."""
+    T, E = s.shape
+    if spec.n_group == 0:
+        return np.ones((T, E), dtype=bool)
+    gs = group_scores(s, spec.n_group)
+    keep = _order_desc(gs)[:, : spec.topk_group]
+    gmask = np.zeros((T, spec.n_group), dtype=bool)
+    np.put_along_axis(gmask, keep, True, axis=1)
+    return np.repeat(gmask, E // spec.n_group, axis=1)
+
+
+def select_topk(s: np.ndarray, spec: RouteSpec) -> np.ndarray:
+    """The k eligible experts of each token in (score descending, id ascending)
+    order: the top-k the router keeps."""
+    masked = np.where(eligible(s, spec), s, -np.inf)
+    return _order_desc(masked)[:, : spec.k].astype(np.int32)
+
+
+def gate_weights(s: np.ndarray, idx: np.ndarray, renorm: bool) -> np.ndarray:
+    """Gate of each chosen expert: its score, divided by the sum over the chosen
+    k when renormalised."""
+    sel = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True) if renorm else sel
+
+
+def route(x, w_router, bias, spec: RouteSpec):
+    """-> (topk_idx [T,k] int32, topk_w [T,k] float64, scores [T,E] float64)."""
+    s = expert_scores(router_logits(x, w_router, bias), spec.score)
+    idx = select_topk(s, spec)
+    return idx, gate_weights(s, idx, spec.renorm), s
+
+
+def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3) -> np.ndarray:
+    """Rows whose routing decisions are separated by at least ``margin``:
+    the k-th vs (k+1)-th eligible expert score and, with a group limit, the
+    topk_group-th vs next group score.  Used to redraw synthetic token rows so
+    that a float32 router must reach the same decisions as this one."""
+    s = expert_scores(router_logits(x, w_router, bias), spec.score)
+    T, E = s.shape
+    ok = np.ones(T, dtype=bool)
+    masked = np.where(eligible(s, spec), s, -np.inf)
+    srt = -np.sort(-masked, axis=1)
+    if spec.k < E and np.isfinite(srt[:, spec.k]).all():
+        ok &= (srt[:, spec.k - 1] - srt[:, spec.k]) >= margin
+    if spec.n_group and spec.topk_group < spec.n_group:
+        g = -np.sort(-group_scores(s, spec.n_group), axis=1)
+        ok &= (g[:, spec.topk_group - 1] - g[:, spec.topk_group]) >= margin
+    return ok
+
+
+# --------------------------------------------------------------------------
+# Dispatch: counts, offsets, stable permutation, gather
+# --------------------------------------------------------------------------
+
+
+def dispatch(topk_idx: np.ndarray, E: int):
+    """Expert-contiguous layout of the T*k assignments a = t*k + j.
+
+    counts[e] = number of assignments to e; offsets = exclusive prefix sum;
+    assignments are placed in increasing a, each at its expert's next free row.
+    Returns counts[E], offsets[E+1], perm_token[T*k] (row -> token),
+    inv_pos[T*k] (assignment -> row).  This buffer is what the dispatch
+    exchange ships to the expert owners ("Expert-Parallel MoE Inference",
+    §The all-to-all dispatch and combine, step by step, Figure 3).
+    """
+    T, k = topk_idx.shape
+    a_exp = topk_idx.reshape(-1).astype(np.int64)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in a_exp:
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    nxt = offsets[:-1].copy()
+    perm_token = np.empty(T * k, dtype=np.int64)
+    inv_pos = np.empty(T * k, dtype=np.int64)
+    for a, e in enumerate(a_exp):
+        p = nxt[e]
+        nxt[e] += 1
+        inv_pos[a] = p
+        perm_token[p] = a // k
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            perm_token.astype(np.int32), inv_pos.astype(np.int32))
+
+
+def gather_rows(x: np.ndarray, perm_token: np.ndarray) -> np.ndarray:
+    """x_perm[p] = x[perm_token[p]] (the dispatch payload, one copy per
+    assignment)."""
+    return x[np.asarray(perm_token, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# Expert FFN (grouped) and combine
+# --------------------------------------------------------------------------
+
+
+def silu(u: np.ndarray) -> np.ndarray:
+    return u / (1.0 + np.exp(-u))
+
+
+def swiglu_expert(xr, w1, w3, w2, act: str):
+    """One expert on its rows: h = round(silu(x W1) * (x W3)), y = round(h W2).
+    w1, w3: [f][d]; w2: [d][f] (out x in, float64)."""
+    u = xr @ w1.T
+    v = xr @ w3.T
+    h = round_act(silu(u) * v, act)
+    y = round_act(h @ w2.T, act)
+    return h, y
+
+
+ExpertFn = Callable[[int], Sequence[np.ndarray]]  # e -> (w1, w3, w2) float64
+
+
+def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, expert_weights: ExpertFn, act: str,
+                rows: Optional[np.ndarray] = None):
+    """Expert e transforms rows [offsets[e], offsets[e+1]) of x_perm; experts
+    with no rows are skipped.  ``rows`` (optional, sorted) restricts the
+    computation to those rows of the buffer; other rows are left NaN.
+    -> (h [R, f], y_perm [R, d])."""
+    R = x_perm.shape[0]
+    want = np.ones(R, dtype=bool) if rows is None else np.isin(np.arange(R), rows)
+    h = y = None
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        sel = np.nonzero(want[lo:hi])[0] + lo
+        if sel.size == 0:
+            continue
+        w1, w3, w2 = expert_weights(e)
+        he, ye = swiglu_expert(x_perm[sel], w1, w3, w2, act)
+        if h is None:
+            h = np.full((R, he.shape[1]), np.nan)
+            y = np.full((R, ye.shape[1]), np.nan)
+        h[sel] = he
+        y[sel] = ye
+    if h is None:
+        raise ValueError("no rows")
+    return h, y
+
+
+def combine(y_perm: np.ndarray, inv_pos: np.ndarray, topk_w: np.ndarray, act: str,
+            shared_y: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = round(sum_j g[t,j] * y_perm[inv_pos[t*k+j]] (+ shared_y[t])):
+    expert outputs brought back to token order and summed weighted by the
+    gates (the weighted-sum combine of "Tensor vs Expert vs Data Parallelism",
+    §Deeper Analysis, Figure 2)."""
+    T, k = topk_w.shape
+    out = np.zeros((T, y_perm.shape[1]))
+    pos = np.asarray(inv_pos, dtype=np.int64).reshape(T, k)
+    for j in range(k):
+        out += topk_w[:, j: j + 1] * y_perm[pos[:, j]]
+    if shared_y is not None:
+        out += shared_y
+    return round_act(out, act)
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class LayerResult:
+    topk_idx: np.ndarray
+    topk_w: np.ndarray
+    counts: np.ndarray
+    offsets: np.ndarray
+    perm_token: np.ndarray
+    inv_pos: np.ndarray
+    x_perm: np.ndarray
+    h: np.ndarray
+    y_perm: np.ndarray
+    shared_h: Optional[np.ndarray]
+    shared_y: Optional[np.ndarray]
+    out: np.ndarray
+
+
+def layer_forward(x, w_router, bias, spec: RouteSpec, E: int, expert_weights: ExpertFn, act: str,
+                  shared: Optional[Sequence[np.ndarray]] = None) -> LayerResult:
+    """The whole layer: route, dispatch, grouped SwiGLU FFN, shared expert,
+    combine.  x, w_router and the weights are float64 values of the stored
+    inputs.  The layer is token-wise: running it on a subset of the tokens
+    gives exactly those tokens' results."""
+    idx, gw, _ = route(x, w_router, bias, spec)
+    counts, offsets, perm_token, inv_pos = dispatch(idx, E)
+    x_perm = gather_rows(x, perm_token)
+    h, y_perm = grouped_ffn(x_perm, offsets, expert_weights, act)
+    sh = sy = None
+    if shared is not None:
+        sh, sy = swiglu_expert(x, shared[0], shared[1], shared[2], act)
+    out = combine(y_perm, inv_pos, gw, act, sy)
+    return LayerResult(idx, gw, counts, offsets, perm_token, inv_pos, x_perm, h, y_perm, sh, sy, out)
