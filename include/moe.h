@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer forward.
+ *
+ * One MoE layer on one GPU, every expert resident in HBM:
+ *   route     : linear gate -> softmax/sigmoid scores -> (group limit) -> top-k
+ *               -> gates                               (moe_route)
+ *   dispatch  : per-expert histogram -> exclusive scan -> stable permutation of
+ *               the T*k assignments into expert-contiguous rows -> row gather
+ *                                                      (moe_dispatch)
+ *   expert FFN: per-expert SwiGLU as a grouped GEMM over the ragged segments
+ *                                                      (moe_grouped_ffn)
+ *   combine   : gate-weighted sum of each token's k expert rows, back in token
+ *               order, plus the shared expert          (moe_combine)
+ *   the whole chain                                    (moe_layer_forward)
+ *
+ * The dataflow is the per-token routing path of "Expert-Parallel MoE
+ * Inference: Serving Sparse Models at Scale" (section "Deeper Analysis:
+ * Routing, Balance, and a Capacity Worked Example", Figure 2) and the
+ * router -> top-k -> dispatch -> expert FFN -> combine chain of "MoE Expert
+ * Parallelism in Practice" (section "Core Principles", item 1).  The
+ * expert-contiguous buffer is the layout the dispatch exchange ships ("Expert-
+ * Parallel MoE Inference", section "The all-to-all dispatch and combine, step
+ * by step", Figure 3); experts run as grouped GEMMs and combine is a weighted
+ * sum ("Tensor vs Expert vs Data Parallelism for MoE Serving", section
+ * "Deeper Analysis", Figure 2).  Dispatch is drop-free: every assignment is
+ * processed (section "Capacity factor and token dropping" of the first page).
+ *
+ * Conventions (all entry points)
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library allocates nothing and keeps no state.
+ *   - Row-major, contiguous.  Weights are stored out x in (K contiguous):
+ *       w_router [E][d], w1/w3 [E][f][d], w2 [E][d][f],
+ *       shared w1/w3 [f_shared][d], shared w2 [d][f_shared].
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     with no host synchronisation, so a call can be captured in a HIP graph.
+ *     Outputs are valid once the stream reaches the end of the call.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a bad argument returns a negative moe_status and enqueues
+ *     nothing.  A launch failure returns MOE_ERR_DEVICE.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.  Nothing is printed
+ *     and nothing aborts.  A workspace smaller than the size the matching
+ *     moe_workspace_size query returns gives MOE_ERR_WORKSPACE: the library
+ *     never drops tokens to fit a buffer (fixed buffers fail loudly, as the
+ *     low-latency dispatch of "Tensor vs Expert vs Data Parallelism", section
+ *     "Two kernel modes for two phases", does).
+ *   - Entry points are reentrant; calls that share output or workspace
+ *     buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,      /* null/misaligned pointer, inconsistent sizes   */
+  MOE_ERR_UNSUPPORTED = -2,  /* shape or dtype combination not implemented    */
+  MOE_ERR_WORKSPACE = -3,    /* workspace smaller than the size query returns */
+  MOE_ERR_DEVICE = -4        /* a HIP call or kernel launch failed            */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+typedef enum {
+  MOE_STAGE_ROUTE = 0, MOE_STAGE_DISPATCH = 1, MOE_STAGE_FFN = 2, MOE_STAGE_LAYER = 3
+} moe_stage;
+
+/* Host struct describing one layer, passed by pointer. */
+typedef struct {
+  int32_t T;          /* tokens, >= 0 (0: only counts/offsets are written, as 0)  */
+  int32_t d;          /* hidden size, multiple of 128                             */
+  int32_t f;          /* routed-expert FFN width, multiple of 128                 */
+  int32_t E;          /* routed experts, 1..512                                   */
+  int32_t k;          /* experts per token, 1..min(E, 16)                         */
+  int32_t score;      /* moe_score                                                */
+  int32_t renorm;     /* 1: gates divided by their sum over the chosen k          */
+  int32_t n_group;    /* 0 = no group limit; else divides E, E/n_group >= 2       */
+  int32_t topk_group; /* groups kept (1..n_group), topk_group*E/n_group >= k      */
+  int32_t f_shared;   /* 0 = no shared expert; else multiple of 128               */
+  int32_t act;        /* moe_dtype of activations: MOE_F32 or MOE_BF16            */
+  int32_t wdtype;     /* moe_dtype of routed weights: act, or MOE_FP8_E4M3 when
+                         act is MOE_BF16 (per-output-channel fp32 scales)         */
+} moe_desc;
+
+/* Number of hipEvents moe_layer_forward records when given a trace array. */
+#define MOE_TRACE_EVENTS 7
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status s);
+
+/* Validates `desc` (host) without touching the GPU.  MOE_OK if supported. */
+moe_status moe_validate(const moe_desc* desc);
+
+/* Workspace bytes needed by moe_route, moe_dispatch, moe_grouped_ffn or
+ * moe_layer_forward for `desc`; written to *bytes (host). */
+moe_status moe_workspace_size(const moe_desc* desc, moe_stage stage, size_t* bytes);
+
+/* Router.  Scores every expert for every token with the linear gate
+ *   z[t,e] = sum_i x[t,i] * w_router[e][i] + bias[e]   (fp32 accumulate)
+ * then s = softmax(z) over the E experts or s = sigmoid(z); with n_group > 0
+ * only the experts of the topk_group groups with the largest group score
+ * (sum of the group's two largest s) are eligible; keeps the k eligible experts
+ * with the largest s (ties: lower id first) in descending order; gate
+ * g = s (renorm = 0) or s / sum of the k chosen s (renorm = 1).
+ *   x        [T][d]   act dtype
+ *   w_router [E][d]   act dtype
+ *   bias     [E]      fp32, nullable (no bias)
+ *   topk_idx [T][k]   int32 out
+ *   topk_w   [T][k]   fp32  out
+ *   ws: moe_workspace_size(MOE_STAGE_ROUTE) bytes (holds the fp32 logits).
+ * ("Expert-Parallel MoE Inference", section "Deeper Analysis", first
+ * paragraph and Figure 2.) */
+moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch.  For the T*k assignments a = t*k + j (expert topk_idx[t][j]):
+ *   counts[e]      = number of assignments to expert e          int32 [E]
+ *   offsets[e]     = sum of counts[e'] for e' < e; offsets[E] = T*k   [E+1]
+ *   inv_pos[a]     = row of assignment a: offsets[e] + number of earlier
+ *                    assignments (smaller a) to the same expert  int32 [T*k]
+ *   perm_token[p]  = token of row p (so perm_token[inv_pos[a]] = a / k) [T*k]
+ *   x_perm[p][:]   = x[perm_token[p]][:]                  act dtype [T*k][d]
+ * Rows of one expert are contiguous and in increasing token order; the result
+ * is deterministic.  topk_idx entries must lie in [0, E).
+ * ws: device workspace of moe_workspace_size(MOE_STAGE_DISPATCH) bytes. */
+moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const void* x,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                        int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Grouped expert FFN over the expert-contiguous rows.  Expert e transforms
+ * rows [offsets[e], offsets[e+1]) of x_perm:
+ *   u = x W1_e^T, v = x W3_e^T (fp32 accumulate, times s1/s3 for fp8),
+ *   h = silu(u) * v   stored in the act dtype                    [T*k][f]
+ *   y = h W2_e^T      (times s2 for fp8) stored in the act dtype [T*k][d]
+ * SwiGLU, silu(u) = u / (1 + exp(-u)).
+ *   offsets  [E+1] int32 (device), as produced by moe_dispatch; offsets[E]
+ *            must equal T*k
+ *   w1, w3   [E][f][d], w2 [E][d][f] in wdtype
+ *   s1, s3   [E][f], s2 [E][d] fp32 per-output-channel scales when wdtype is
+ *            MOE_FP8_E4M3, else NULL
+ *   h, y_perm outputs; ws: moe_workspace_size(MOE_STAGE_FFN) bytes. */
+moe_status moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
+                           const void* w1, const void* w3, const void* w2,
+                           const float* s1, const float* s3, const float* s2,
+                           void* h, void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine.  out[t][:] = sum_{j<k} topk_w[t][j] * y_perm[inv_pos[t*k+j]][:]
+ *                       (+ shared_y[t][:]), fp32 accumulation in that order,
+ * stored in the act dtype.  No atomics: each token reads its own k rows.
+ *   shared_y [T][d] act dtype, nullable. */
+moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* inv_pos,
+                       const float* topk_w, const void* shared_y, void* out, void* stream);
+
+/* The whole layer: route, dispatch, grouped FFN, shared expert (when
+ * f_shared > 0: the SwiGLU expert of every token with gate 1, weights in the
+ * act dtype), combine.  Intermediates (perm_token, inv_pos, offsets, x_perm,
+ * h, y_perm, shared h and y) live in ws (moe_workspace_size(MOE_STAGE_LAYER)).
+ *   out [T][d] act dtype; topk_idx [T][k], topk_w [T][k], counts [E] outputs.
+ *   sw1, sw3, sw2: shared expert, NULL when f_shared == 0.
+ *   trace: NULL, or MOE_TRACE_EVENTS hipEvent_t (host array of handles)
+ *          recorded on `stream` before the router and after the router,
+ *          dispatch, routed gate-up GEMM, routed down GEMM, shared expert and
+ *          combine, for per-stage timing. */
+moe_status moe_layer_forward(const moe_desc* desc, const void* x, const void* w_router,
+                             const float* bias, const void* w1, const void* w3, const void* w2,
+                             const float* s1, const float* s3, const float* s2,
+                             const void* sw1, const void* sw3, const void* sw2,
+                             void* out, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                             void* ws, size_t ws_bytes, void* stream, void* const* trace);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

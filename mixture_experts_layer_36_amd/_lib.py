@@ -1,0 +1,168 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module turns torch
+tensors into device pointers and the current HIP stream, and raises MoeError on
+a non-zero status.  There is no fallback: if libmoe.so is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+SOFTMAX, SIGMOID = 0, 1
+STAGE_ROUTE, STAGE_DISPATCH, STAGE_FFN, STAGE_LAYER = 0, 1, 2, 3
+TRACE_EVENTS = 7
+TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "combine")
+
+# the exported symbols include/moe.h declares
+EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
+           "moe_grouped_ffn", "moe_combine", "moe_layer_forward")
+
+_DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().moe_status_str(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{where}: {msg}")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "f", "E", "k", "score", "renorm", "n_group", "topk_group",
+                 "f_shared", "act", "wdtype")]
+
+    @classmethod
+    def make(cls, T, d, f, E, k, score="softmax", renorm=True, n_group=0, topk_group=0,
+             f_shared=0, act="bf16", wdtype="bf16") -> "Desc":
+        return cls(T, d, f, E, k, SOFTMAX if score == "softmax" else SIGMOID, int(bool(renorm)),
+                   n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype])
+
+    @classmethod
+    def from_attrs(cls, w) -> "Desc":
+        """From any object with T, d, f, E, k, score, renorm, n_group,
+        topk_group, f_shared, act and wdt attributes."""
+        return cls.make(w.T, w.d, w.f, w.E, w.k, w.score, w.renorm, w.n_group, w.topk_group,
+                        w.f_shared, w.act, w.wdt)
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mixture_experts_layer_36_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(Desc)
+        lib.moe_status_str.restype = ctypes.c_char_p
+        lib.moe_status_str.argtypes = [ctypes.c_int]
+        lib.moe_validate.argtypes = [D]
+        lib.moe_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_route.argtypes = [D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.moe_dispatch.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.moe_grouped_ffn.argtypes = [D] + [_P] * 11 + [ctypes.c_size_t, _P]
+        lib.moe_combine.argtypes = [D, _P, _P, _P, _P, _P, _P]
+        lib.moe_layer_forward.argtypes = [D] + [_P] * 17 + [ctypes.c_size_t, _P, _P]
+        for name in EXPORTS[1:]:
+            getattr(lib, name).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def loaded_path() -> str:
+    _lib()
+    return LIB_PATH
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or None")
+    if t.numel() and not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def validate(desc: Desc) -> int:
+    return _lib().moe_validate(ctypes.byref(desc))
+
+
+def workspace_size(desc: Desc, stage: int = STAGE_LAYER) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib().moe_workspace_size(ctypes.byref(desc), stage, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(desc: Desc, stage: int = STAGE_LAYER, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_size(desc, stage), 16), dtype=torch.uint8, device=device)
+
+
+def route(desc, x, w_router, bias, topk_idx, topk_w, ws, stream=None):
+    _check(_lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_idx),
+                            _ptr(topk_w), _ptr(ws), ws.numel() if ws is not None else 0,
+                            _stream(stream)), "moe_route")
+
+
+def dispatch(desc, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, ws, stream=None):
+    _check(_lib().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+                               _ptr(perm_token), _ptr(inv_pos), _ptr(x_perm), _ptr(ws),
+                               ws.numel() if ws is not None else 0, _stream(stream)), "moe_dispatch")
+
+
+def grouped_ffn(desc, x_perm, offsets, w1, w3, w2, s1, s3, s2, h, y_perm, ws, stream=None):
+    _check(_lib().moe_grouped_ffn(ctypes.byref(desc), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3),
+                                  _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(h), _ptr(y_perm),
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_grouped_ffn")
+
+
+def combine(desc, y_perm, inv_pos, topk_w, shared_y, out, stream=None):
+    _check(_lib().moe_combine(ctypes.byref(desc), _ptr(y_perm), _ptr(inv_pos), _ptr(topk_w),
+                              _ptr(shared_y), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def layer_forward(desc, x, w_router, bias, w1, w3, w2, s1, s3, s2, sw1, sw3, sw2,
+                  out, topk_idx, topk_w, counts, ws, stream=None,
+                  trace: Optional[Sequence] = None):
+    """trace: None or TRACE_EVENTS torch.cuda.Event objects (timing enabled)."""
+    tr = None
+    if trace is not None:
+        if len(trace) != TRACE_EVENTS:
+            raise ValueError(f"trace needs {TRACE_EVENTS} events")
+        handles = []
+        for ev in trace:
+            if ev.cuda_event == 0:  # torch creates the HIP event lazily
+                ev.record()
+            handles.append(ev.cuda_event)
+        tr = (ctypes.c_void_p * TRACE_EVENTS)(*handles)
+    _check(_lib().moe_layer_forward(
+        ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2),
+        _ptr(s1), _ptr(s3), _ptr(s2), _ptr(sw1), _ptr(sw3), _ptr(sw2), _ptr(out), _ptr(topk_idx),
+        _ptr(topk_w), _ptr(counts), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(stream), tr), "moe_layer_forward")

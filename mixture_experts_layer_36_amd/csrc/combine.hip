@@ -1,0 +1,99 @@
+// Combine: each token's k expert rows, weighted by its gates, summed in fp32
+// back in token order (plus the shared expert's row), then stored in the
+// activation dtype.
+//
+// The weighted sum of the expert outputs is the combine step of "Tensor vs
+// Expert vs Data Parallelism for MoE Serving" (section "Deeper Analysis:
+// Communication, Overlap and Load Balance", Figure 2) and of "Expert-Parallel
+// MoE Inference: Serving Sparse Models at Scale" (section "Deeper Analysis",
+// Figure 2).  No atomics: a token gathers its own k rows through inv_pos, so
+// the result is deterministic.  The sum runs j = 0..k-1, then the shared row.
+// One block per token row; 16-byte loads and stores, HBM-bound.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxK = 16;
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_g[kMaxK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < a.k) {
+    s_row[threadIdx.x] = a.inv_pos[(size_t)t * a.k + threadIdx.x];
+    s_g[threadIdx.x] = a.topk_w[(size_t)t * a.k + threadIdx.x];
+  }
+  __syncthreads();
+  const int nvec = a.d / 8;  // 8 bf16 per 16 bytes
+  const u32x4* y = (const u32x4*)a.y_perm;
+  const u32x4* ys = (const u32x4*)a.shared_y;
+  u32x4* out = (u32x4*)a.out;
+  for (int v = threadIdx.x; v < nvec; v += 256) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) {
+      const u32x4 r = y[(size_t)s_row[j] * nvec + v];
+      const float g = s_g[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += g * bf16_to_f32(r[q] & 0xffffu);
+        acc[2 * q + 1] += g * bf16_to_f32(r[q] >> 16);
+      }
+    }
+    if (ys) {
+      const u32x4 r = ys[(size_t)t * nvec + v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(r[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(r[q] >> 16);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    out[(size_t)t * nvec + v] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(CombineArgs a) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_g[kMaxK];
+  const int t = blockIdx.x;
+  if (threadIdx.x < a.k) {
+    s_row[threadIdx.x] = a.inv_pos[(size_t)t * a.k + threadIdx.x];
+    s_g[threadIdx.x] = a.topk_w[(size_t)t * a.k + threadIdx.x];
+  }
+  __syncthreads();
+  const int nvec = a.d / 4;
+  const f32x4* y = (const f32x4*)a.y_perm;
+  const f32x4* ys = (const f32x4*)a.shared_y;
+  f32x4* out = (f32x4*)a.out;
+  for (int v = threadIdx.x; v < nvec; v += 256) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < a.k; ++j) {
+      const f32x4 r = y[(size_t)s_row[j] * nvec + v];
+      const float g = s_g[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += g * r[q];
+    }
+    if (ys) {
+      const f32x4 r = ys[(size_t)t * nvec + v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += r[q];
+    }
+    out[(size_t)t * nvec + v] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.act == GD_BF16)
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(a.T), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,143 @@
+// Dispatch: per-expert histogram, exclusive scan, stable permutation into
+// expert-contiguous rows, and the row gather that fills the dispatch buffer.
+//
+// The expert-contiguous buffer is the layout the dispatch exchange ships to
+// the expert owners ("Expert-Parallel MoE Inference: Serving Sparse Models at
+// Scale", section "The all-to-all dispatch and combine, step by step",
+// Figure 3); counts[e] are the per-expert token counts that page's checklist
+// asks to export (section "Trade-offs, Gotchas, and What Goes Wrong").
+//
+// Three index kernels, all deterministic (no result depends on atomic order):
+//   1. histogram: one wavefront per chunk of kDispatchChunk assignments,
+//      LDS-privatised bins -> chunk_cnt[chunk][e];
+//   2. scan (one block): per-expert running sums over chunks give each
+//      chunk's first row per expert; an exclusive scan over experts gives
+//      offsets;
+//   3. scatter: one wavefront per chunk walks its assignments in order, 64 at
+//      a time; a lane's rank among earlier lanes with the same expert comes
+//      from ballot equality masks, so rows within an expert follow the
+//      assignment order a = t*k + j (increasing token).
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = 512;
+constexpr int kIdBits = 10;  // ids 0..512 (512 marks an idle lane)
+
+__global__ __launch_bounds__(64) void histogram_kernel(DispatchArgs a) {
+  __shared__ int bins[kMaxE];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.E; e += 64) bins[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kDispatchChunk;
+  const int end = min(base + kDispatchChunk, a.n_assign);
+  for (int i = base + lane; i < end; i += 64) atomicAdd(&bins[a.topk_idx[i]], 1);
+  __syncthreads();
+  for (int e = lane; e < a.E; e += 64) a.chunk_cnt[(size_t)blockIdx.x * a.E + e] = bins[e];
+}
+
+__global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunks) {
+  __shared__ int tot[kMaxE];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < a.E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      int* p = a.chunk_cnt + (size_t)c * a.E + e;
+      const int v = *p;
+      *p = run;  // rows of e before chunk c (relative to offsets[e])
+      run += v;
+    }
+    a.counts[e] = run;
+  }
+  tot[e] = (e < a.E) ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over kMaxE entries
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = (e >= off) ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  const int excl = tot[e] - ((e < a.E) ? run : 0);
+  if (e < a.E) {
+    a.offsets[e] = excl;
+    for (int c = 0; c < n_chunks; ++c) a.chunk_cnt[(size_t)c * a.E + e] += excl;
+  }
+  if (e == a.E - 1) a.offsets[a.E] = tot[e];
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
+  __shared__ int next_row[kMaxE];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.E; e += 64) next_row[e] = a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
+  __syncthreads();
+  const int base = blockIdx.x * kDispatchChunk;
+  const int end = min(base + kDispatchChunk, a.n_assign);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = base; s < end; s += 64) {
+    const int i = s + lane;
+    const bool valid = i < end;
+    const int e = valid ? a.topk_idx[i] : kMaxE;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
+    const int row = valid ? next_row[e] + rank : 0;
+    __syncthreads();  // every lane has read next_row before any update
+    const bool last = (same >> lane) == 1ull;  // highest lane of its group
+    if (valid && last) next_row[e] = row + 1;
+    __syncthreads();
+    if (valid) {
+      a.inv_pos[i] = row;
+      a.perm_token[row] = i / a.k;
+    }
+  }
+}
+
+// x_perm[p][:] = x[perm_token[p]][:], 16-byte vectors; one block per 8 rows.
+__global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
+                                                     const int32_t* __restrict__ perm,
+                                                     int rows, int vec_per_row,
+                                                     u32x4* __restrict__ out) {
+  const int r0 = blockIdx.x * 8;
+  for (int r = r0; r < min(r0 + 8, rows); ++r) {
+    const size_t src = (size_t)perm[r] * vec_per_row;
+    const size_t dst = (size_t)r * vec_per_row;
+    for (int v = threadIdx.x; v < vec_per_row; v += 256) out[dst + v] = x[src + v];
+  }
+}
+
+__global__ void zero_counts_kernel(DispatchArgs a) {
+  const int e = threadIdx.x;
+  if (e < a.E) a.counts[e] = 0;
+  if (a.offsets != nullptr && e <= a.E) a.offsets[e] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
+  if (a.n_assign == 0) {  // a fill kernel, not a memset node (graph-safe)
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kMaxE + 64), 0, s, a);
+    return hipGetLastError();
+  }
+  const int n_chunks = (a.n_assign + kDispatchChunk - 1) / kDispatchChunk;
+  hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, n_chunks);
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, int row_bytes,
+                              void* x_perm, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3((rows + 7) / 8), dim3(256), 0, s,
+                     (const u32x4*)x, perm_token, rows, row_bytes / 16, (u32x4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,435 @@
+// Grouped GEMM over ragged expert segments, with the SwiGLU, plain-store and
+// router-bias epilogues.
+//
+// The experts of an MoE layer run as grouped GEMMs ("Tensor vs Expert vs Data
+// Parallelism for MoE Serving", section "Deeper Analysis", Figure 2; "Expert
+// Parallelism for MoE Serving", section "The Future of Expert Parallelism for
+// MoE Serving").  Expert e owns rows [offsets[e], offsets[e+1]) of the
+// expert-contiguous activation buffer; a device-built tile table maps each
+// m-tile slot of the grid to (expert, m-tile), so the host never reads counts.
+//
+// bf16 / fp8-weight path (gfx950 MFMA):
+//   * block tile BM activation rows x BN weight rows x BK=64, 4 wavefronts in
+//     a 2x2 grid, LDS double-buffered, 16-byte chunks XOR-swizzled by row so
+//     the MFMA operand reads spread over the LDS banks;
+//   * v_mfma_f32_32x32x16_bf16 with the WEIGHT rows as the MFMA row operand
+//     and activation rows as its column operand: each lane then owns runs of
+//     4 consecutive output columns of one activation row, which become 8-byte
+//     (bf16) or 16-byte (fp32) stores;
+//   * fp8 (OCP E4M3) weights are widened to bf16 exactly while being staged
+//     into LDS; the per-output-channel scale multiplies the fp32 accumulator
+//     in the epilogue, so y = s_n * sum_k x_k q_nk exactly as dequantised;
+//   * SwiGLU: each wavefront's weight rows are half W1 rows and half W3 rows
+//     of the same output columns, so u and v meet in one lane and
+//     h = silu(u) * v is formed before the store.
+// fp32 path: an LDS-tiled FMA kernel (small layers; exact fp32 arithmetic).
+//
+// Grid: m-tile slots x n-tiles, remapped so that each XCD (blocks are dealt
+// round-robin to the 8 XCDs) runs a contiguous run of slots of one n-tile and
+// its L2 holds the weight tile those slots share.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTableExpertShift = 22;
+constexpr int kTableTileMask = (1 << kTableExpertShift) - 1;
+
+struct TileInfo {
+  int e, row0, nrows;
+};
+
+__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti) {
+  if (a.tile_table == nullptr) {
+    ti.e = 0;
+    ti.row0 = mt * BM;
+    ti.nrows = min(BM, a.rows - ti.row0);
+    return ti.nrows > 0;
+  }
+  const int code = a.tile_table[mt];
+  if (code < 0) return false;
+  ti.e = code >> kTableExpertShift;
+  const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
+  ti.row0 = lo + (code & kTableTileMask) * BM;
+  ti.nrows = min(BM, hi - ti.row0);
+  return ti.nrows > 0;
+}
+
+// block id -> (m-slot, n-tile), XCD-aware
+__device__ __forceinline__ void block_coords(int n_slots, int n_tiles, int& mt, int& nt) {
+  const int nb = gridDim.x;  // a multiple of 8
+  const int b = blockIdx.x;
+  const int L = (b & 7) * (nb >> 3) + (b >> 3);
+  mt = L % n_slots;
+  nt = L / n_slots;
+  if (nt >= n_tiles) mt = -1;
+}
+
+__device__ __forceinline__ float silu(float u) { return u / (1.f + expf(-u)); }
+
+// ============================================================== MFMA kernel
+template <int BM, int BN, int WDT, int EPI>
+struct MfmaCfg {
+  static constexpr int BK = 64;
+  static constexpr int WM = 2, WN = 2, NTHR = 256;
+  static constexpr int RA = BM / WM;        // activation rows per wave
+  static constexpr int RW = BN / WN;        // weight rows per wave
+  static constexpr int TA = RA / 32, TW = RW / 32;
+  static constexpr int A_CHUNKS = BM * BK / 8 / NTHR;  // 16-byte chunks per thread
+  static constexpr int B_CHUNKS = (WDT == GD_FP8) ? BN * BK / 16 / NTHR : BN * BK / 8 / NTHR;
+  static constexpr int NCOL = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
+  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+  static_assert(EPI != EPI_SWIGLU || TW % 2 == 0, "SwiGLU needs paired weight blocks");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) {  // element offset in a 64-wide row
+  return row * 64 + ((chunk ^ (row & 7)) << 3);
+}
+
+template <int BM, int BN, int WDT, int EPI>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots, int n_tiles) {
+  using C = MfmaCfg<BM, BN, WDT, EPI>;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][(BM + BN) * C::BK];
+
+  int mt, nt;
+  block_coords(n_slots, n_tiles, mt, nt);
+  if (mt < 0) return;
+  TileInfo ti;
+  if (!tile_info(a, mt, BM, ti)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int K = a.K;
+  const size_t wsz = (size_t)(EPI == EPI_SWIGLU ? a.N : a.N) * K;  // elements per expert matrix
+  const int ncol0 = nt * C::NCOL;
+
+  // ---- global source pointers of this thread's chunks (k offset added per tile)
+  const uint16_t* a_src[C::A_CHUNKS];
+  int a_dst[C::A_CHUNKS];
+#pragma unroll
+  for (int j = 0; j < C::A_CHUNKS; ++j) {
+    const int q = tid + j * C::NTHR;
+    const int r = q >> 3, c = q & 7;
+    const int rr = min(r, ti.nrows - 1);
+    a_src[j] = (const uint16_t*)a.A + (size_t)(ti.row0 + rr) * K + c * 8;
+    a_dst[j] = swz(r, c);
+  }
+  const uint8_t* b_src[C::B_CHUNKS];
+  int b_dst[C::B_CHUNKS];
+#pragma unroll
+  for (int j = 0; j < C::B_CHUNKS; ++j) {
+    const int q = tid + j * C::NTHR;
+    int r, c;  // LDS row, first LDS chunk
+    if (WDT == GD_FP8) { r = q >> 2; c = (q & 3) * 2; } else { r = q >> 3; c = q & 7; }
+    const void* base;
+    int n;
+    if (EPI == EPI_SWIGLU) {
+      const int half = C::RW / 2;
+      const int w = r / C::RW, rr = r % C::RW;
+      base = (rr < half) ? a.B0 : a.B1;
+      n = ncol0 + w * half + (rr % half);
+    } else {
+      base = a.B0;
+      n = min(ncol0 + r, a.N - 1);
+    }
+    const int esz = (WDT == GD_FP8) ? 1 : 2;
+    b_src[j] = (const uint8_t*)base + ((size_t)ti.e * wsz + (size_t)n * K + c * 8) * esz;
+    b_dst[j] = BM * C::BK + swz(r, c);
+  }
+
+  u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < C::A_CHUNKS; ++j) ra[j] = *(const u32x4*)(a_src[j] + k0);
+#pragma unroll
+    for (int j = 0; j < C::B_CHUNKS; ++j)
+      rb[j] = *(const u32x4*)(b_src[j] + (size_t)k0 * (WDT == GD_FP8 ? 1 : 2));
+  };
+  auto store = [&](int buf) {
+    __bf16* L = lds[buf];
+#pragma unroll
+    for (int j = 0; j < C::A_CHUNKS; ++j) *(u32x4*)(L + a_dst[j]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < C::B_CHUNKS; ++j) {
+      if (WDT == GD_FP8) {
+        // 16 e4m3 bytes -> two chunks of 8 bf16; the second chunk is c+1
+        u32x4 lo, hi;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = rb[j][w];
+          const uint32_t p0 = e4m3_to_bf16(v & 0xff) | (e4m3_to_bf16((v >> 8) & 0xff) << 16);
+          const uint32_t p1 = e4m3_to_bf16((v >> 16) & 0xff) | (e4m3_to_bf16(v >> 24) << 16);
+          if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
+        }
+        const int off = b_dst[j] - BM * C::BK;
+        const int r = off >> 6;
+        const int c = ((off & 63) >> 3) ^ (r & 7);
+        *(u32x4*)(L + BM * C::BK + swz(r, c)) = lo;
+        *(u32x4*)(L + BM * C::BK + swz(r, c + 1)) = hi;
+      } else {
+        *(u32x4*)(L + b_dst[j]) = rb[j];
+      }
+    }
+  };
+
+  f32x16 acc[C::TW][C::TA];
+#pragma unroll
+  for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int KT = K / C::BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load((kt + 1) * C::BK);
+    const __bf16* L = lds[cur];
+#pragma unroll
+    for (int kk = 0; kk < C::BK / 16; ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      bf16x8 fw[C::TW], fa[C::TA];
+#pragma unroll
+      for (int i = 0; i < C::TW; ++i)
+        fw[i] = *(const bf16x8*)(L + BM * C::BK + swz(wn * C::RW + i * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j)
+        fa[j] = *(const bf16x8*)(L + swz(wm * C::RA + j * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TA; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds, per 32x32 block and group g, output columns
+  // 4 consecutive (g*8 + (lane/32)*4 + 0..3) of activation row (lane % 32).
+  const int r_in = lane & 31;
+#pragma unroll
+  for (int j = 0; j < C::TA; ++j) {
+    const int lrow = wm * C::RA + j * 32 + r_in;
+    if (lrow >= ti.nrows) continue;
+    const size_t row = (size_t)(ti.row0 + lrow);
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < C::TW / 2; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ncol0 + wn * (C::RW / 2) + i * 32 + g * 8 + (lane >> 5) * 4;
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float u = acc[i][j][g * 4 + q];
+            float v = acc[i + C::TW / 2][j][g * 4 + q];
+            if (WDT == GD_FP8) {
+              u *= a.s0[(size_t)ti.e * a.N + n + q];
+              v *= a.s1[(size_t)ti.e * a.N + n + q];
+            }
+            hv[q] = silu(u) * v;
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(hv[0], hv[1]);
+          o[1] = pack_bf16x2(hv[2], hv[3]);
+          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+        }
+      }
+    } else if (EPI == EPI_STORE) {
+#pragma unroll
+      for (int i = 0; i < C::TW; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ncol0 + wn * C::RW + i * 32 + g * 8 + (lane >> 5) * 4;
+          float yv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            yv[q] = acc[i][j][g * 4 + q];
+            if (WDT == GD_FP8) yv[q] *= a.s0[(size_t)ti.e * a.N + n + q];
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(yv[0], yv[1]);
+          o[1] = pack_bf16x2(yv[2], yv[3]);
+          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+        }
+      }
+    } else {  // EPI_BIAS_F32: router logits
+#pragma unroll
+      for (int i = 0; i < C::TW; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ncol0 + wn * C::RW + i * 32 + g * 8 + (lane >> 5) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (n + q < a.N) {
+              float z = acc[i][j][g * 4 + q];
+              if (a.bias) z += a.bias[n + q];
+              ((float*)a.C)[row * a.N + n + q] = z;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ============================================================== fp32 kernel
+// 64 activation rows x 64 weight rows per block, BK = 16, 4x4 outputs per
+// thread.  For SwiGLU the 64 weight rows are 32 W1 rows and the matching 32
+// W3 rows, and a thread's 4 weight rows are {2c, 2c+1} of W1 and of W3.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, int n_tiles) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  constexpr int NCOL = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  int mt, nt;
+  block_coords(n_slots, n_tiles, mt, nt);
+  if (mt < 0) return;
+  TileInfo ti;
+  if (!tile_info(a, mt, BM, ti)) return;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int K = a.K;
+  const int ncol0 = nt * NCOL;
+  const float* A = (const float*)a.A;
+  const size_t wsz = (size_t)a.N * K;
+
+  int wrow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wrow[q] = (EPI == EPI_SWIGLU) ? ((q < 2) ? 2 * tx + q : 32 + 2 * tx + q - 2) : 4 * tx + q;
+
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    // stage: 64 rows x 16 k for A and B (4 elements per thread each)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + q * 256;
+      const int r = idx >> 4, kk = idx & 15;
+      const int ar = min(r, ti.nrows - 1);
+      As[kk][r] = A[(size_t)(ti.row0 + ar) * K + k0 + kk];
+      const float* base;
+      int n;
+      if (EPI == EPI_SWIGLU) {
+        base = (const float*)((r < 32) ? a.B0 : a.B1);
+        n = ncol0 + (r & 31);
+      } else {
+        base = (const float*)a.B0;
+        n = min(ncol0 + r, a.N - 1);
+      }
+      Bs[kk][r] = base[(size_t)ti.e * wsz + (size_t)n * K + k0 + kk];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(As[kk][ty * 4 + i], Bs[kk][wrow[q]], acc[i][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lrow = ty * 4 + i;
+    if (lrow >= ti.nrows) continue;
+    const size_t row = (size_t)(ti.row0 + lrow);
+    float* Cr = (float*)a.C + row * a.N;
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) Cr[ncol0 + 2 * tx + q] = silu(acc[i][q]) * acc[i][q + 2];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = ncol0 + 4 * tx + q;
+        if (n < a.N) Cr[n] = acc[i][q] + ((EPI == EPI_BIAS_F32 && a.bias) ? a.bias[n] : 0.f);
+      }
+    }
+  }
+}
+
+// ============================================================== tile tables
+__global__ __launch_bounds__(512) void tile_table_kernel(TileTableArgs t) {
+  __shared__ int pre[2][512];
+  const int e = threadIdx.x;
+  const int cnt = (e < t.E) ? t.offsets[e + 1] - t.offsets[e] : 0;
+  for (int w = 0; w < 2; ++w) {
+    const int bm = w == 0 ? t.bm0 : t.bm1;
+    if (bm == 0) break;
+    const int tiles = (cnt + bm - 1) / bm;
+    pre[w][e] = tiles;
+    __syncthreads();
+    for (int off = 1; off < 512; off <<= 1) {
+      const int v = (e >= off) ? pre[w][e - off] : 0;
+      __syncthreads();
+      pre[w][e] += v;
+      __syncthreads();
+    }
+    const int incl = pre[w][e], total = pre[w][511];
+    int32_t* table = w == 0 ? t.table0 : t.table1;
+    const int n_slots = w == 0 ? t.n_slots0 : t.n_slots1;
+    for (int i = 0; i < tiles; ++i) table[incl - tiles + i] = (e << kTableExpertShift) | i;
+    for (int s = total + e; s < n_slots; s += 512) table[s] = -1;
+  }
+}
+
+template <int BM, int BN, int WDT, int EPI>
+hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
+  using C = MfmaCfg<BM, BN, WDT, EPI>;
+  const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
+  const int n_tiles = (a.N + C::NCOL - 1) / C::NCOL;
+  int nb = n_slots * n_tiles;
+  nb = (nb + 7) & ~7;
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WDT, EPI>), dim3(nb), dim3(C::NTHR), 0, s, a, n_slots, n_tiles);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_f32(const GemmArgs& a, hipStream_t s) {
+  const int ncol = (EPI == EPI_SWIGLU) ? 32 : 64;
+  const int n_slots = a.tile_table ? a.n_slots : (a.rows + 63) / 64;
+  const int n_tiles = (a.N + ncol - 1) / ncol;
+  int nb = n_slots * n_tiles;
+  nb = (nb + 7) & ~7;
+  hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(nb), dim3(256), 0, s, a, n_slots, n_tiles);
+  return hipGetLastError();
+}
+
+template <int WDT>
+hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
+  switch (a.epi) {
+    case EPI_SWIGLU: return launch_mfma<128, 128, WDT, EPI_SWIGLU>(a, s);
+    case EPI_STORE: return launch_mfma<128, 128, WDT, EPI_STORE>(a, s);
+    default: return launch_mfma<128, 128, WDT, EPI_BIAS_F32>(a, s);
+  }
+}
+
+}  // namespace
+
+int gemm_block_m(const GemmArgs& a) { return a.act == GD_F32 ? 64 : 128; }
+
+int gemm_max_slots(int rows, int E, int block_m) {
+  return (rows + block_m - 1) / block_m + E;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.act == GD_F32) {
+    switch (a.epi) {
+      case EPI_SWIGLU: return launch_f32<EPI_SWIGLU>(a, s);
+      case EPI_STORE: return launch_f32<EPI_STORE>(a, s);
+      default: return launch_f32<EPI_BIAS_F32>(a, s);
+    }
+  }
+  return a.wdt == GD_FP8 ? launch_mfma_epi<GD_FP8>(a, s) : launch_mfma_epi<GD_BF16>(a, s);
+}
+
+hipError_t launch_tile_tables(const TileTableArgs& t, hipStream_t s) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(512), 0, s, t);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,395 @@
+// C ABI of the MoE layer forward: host-side validation, workspace carving and
+// launch order.  Every entry point validates all arguments before it enqueues
+// anything, never allocates, never synchronises, and reports failures as
+// moe_status codes.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 16;
+constexpr int kMaxGroups = 64;
+constexpr int64_t kMaxAssign = int64_t(1) << 28;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+size_t act_bytes(const moe_desc* d) { return d->act == MOE_F32 ? 4 : 2; }
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a required pointer: non-null and 16-byte aligned
+bool need(const void* p) { return p != nullptr && aligned(p); }
+// a nullable pointer: null, or 16-byte aligned
+bool maybe(const void* p) { return p == nullptr || aligned(p); }
+
+moe_status check_desc(const moe_desc* d) {
+  if (d == nullptr) return MOE_ERR_INVALID;
+  if (d->T < 0 || d->d <= 0 || d->f <= 0 || d->E <= 0 || d->k <= 0 || d->f_shared < 0)
+    return MOE_ERR_INVALID;
+  if (d->k > d->E) return MOE_ERR_INVALID;
+  if (d->score != MOE_SCORE_SOFTMAX && d->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID;
+  if (d->renorm != 0 && d->renorm != 1) return MOE_ERR_INVALID;
+  if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->wdtype != MOE_F32 && d->wdtype != MOE_BF16 && d->wdtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID;
+  if (d->act == MOE_F32 && d->wdtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (d->act == MOE_BF16 && d->wdtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (d->n_group < 0 || d->topk_group < 0) return MOE_ERR_INVALID;
+  if (d->n_group > 0) {
+    if (d->E % d->n_group != 0 || d->E / d->n_group < 2) return MOE_ERR_INVALID;
+    if (d->topk_group < 1 || d->topk_group > d->n_group) return MOE_ERR_INVALID;
+    if (int64_t(d->topk_group) * (d->E / d->n_group) < d->k) return MOE_ERR_INVALID;
+    if (d->n_group > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+  }
+  if (d->E > kMaxE || d->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (d->d % 128 != 0 || d->f % 128 != 0 || d->f_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (int64_t(d->T) * d->k >= kMaxAssign) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t n_assign(const moe_desc* d) { return int64_t(d->T) * d->k; }
+
+int gemm_dtype(int moe_dt) {
+  return moe_dt == MOE_F32 ? GD_F32 : moe_dt == MOE_BF16 ? GD_BF16 : GD_FP8;
+}
+
+int block_m(const moe_desc* d) {
+  GemmArgs g{};
+  g.act = gemm_dtype(d->act);
+  return gemm_block_m(g);
+}
+
+// ---------------------------------------------------------------- workspace
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+struct RouteWs {
+  float* z;
+};
+struct DispatchWs {
+  int32_t* chunk_cnt;
+};
+struct FfnWs {
+  int32_t* table;
+  int n_slots;
+};
+struct LayerWs {
+  RouteWs route;
+  DispatchWs disp;
+  FfnWs ffn;
+  int32_t* perm_token;
+  int32_t* inv_pos;
+  int32_t* offsets;
+  void* x_perm;
+  void* h;
+  void* y_perm;
+  void* sh;
+  void* sy;
+};
+
+RouteWs carve_route(Carve& c, const moe_desc* d) {
+  return RouteWs{c.take<float>(sizeof(float) * size_t(d->T) * d->E)};
+}
+DispatchWs carve_dispatch(Carve& c, const moe_desc* d) {
+  const int64_t chunks = (n_assign(d) + kDispatchChunk - 1) / kDispatchChunk;
+  return DispatchWs{c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E)};
+}
+FfnWs carve_ffn(Carve& c, const moe_desc* d) {
+  FfnWs w;
+  w.n_slots = gemm_max_slots(int(n_assign(d)), d->E, block_m(d));
+  w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots));
+  return w;
+}
+LayerWs carve_layer(Carve& c, const moe_desc* d) {
+  LayerWs w;
+  const size_t A = n_assign(d), ab = act_bytes(d);
+  w.route = carve_route(c, d);
+  w.disp = carve_dispatch(c, d);
+  w.ffn = carve_ffn(c, d);
+  w.perm_token = c.take<int32_t>(sizeof(int32_t) * A);
+  w.inv_pos = c.take<int32_t>(sizeof(int32_t) * A);
+  w.offsets = c.take<int32_t>(sizeof(int32_t) * (d->E + 1));
+  w.x_perm = c.take<char>(A * d->d * ab);
+  w.h = c.take<char>(A * d->f * ab);
+  w.y_perm = c.take<char>(A * d->d * ab);
+  w.sh = d->f_shared ? c.take<char>(size_t(d->T) * d->f_shared * ab) : nullptr;
+  w.sy = d->f_shared ? c.take<char>(size_t(d->T) * d->d * ab) : nullptr;
+  return w;
+}
+
+size_t stage_bytes(const moe_desc* d, moe_stage stage) {
+  Carve c(nullptr);
+  switch (stage) {
+    case MOE_STAGE_ROUTE: carve_route(c, d); break;
+    case MOE_STAGE_DISPATCH: carve_dispatch(c, d); break;
+    case MOE_STAGE_FFN: carve_ffn(c, d); break;
+    default: carve_layer(c, d); break;
+  }
+  return c.used;
+}
+
+moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+#define MOE_TRY(expr)                     \
+  do {                                    \
+    moe_status st_ = (expr);              \
+    if (st_ != MOE_OK) return st_;        \
+  } while (0)
+
+// ---------------------------------------------------------------- stages
+moe_status run_route(const moe_desc* d, const void* x, const void* wr, const float* bias,
+                     int32_t* idx, float* w, const RouteWs& ws, hipStream_t s) {
+  GemmArgs g{};
+  g.A = x;
+  g.rows = d->T;
+  g.B0 = wr;
+  g.bias = bias;
+  g.N = d->E;
+  g.K = d->d;
+  g.C = ws.z;
+  g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->act);
+  g.epi = EPI_BIAS_F32;
+  MOE_TRY(dev(launch_gemm(g, s)));
+  RouteSelectArgs r{ws.z, d->T, d->E, d->k, d->score, d->renorm, d->n_group, d->topk_group, idx, w};
+  return dev(launch_route_select(r, s));
+}
+
+moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
+                        const DispatchWs& ws, hipStream_t s) {
+  DispatchArgs a{idx, int(n_assign(d)), d->E, d->k, ws.chunk_cnt, counts, offsets, perm_token, inv_pos};
+  MOE_TRY(dev(launch_dispatch_index(a, s)));
+  return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), int(d->d * act_bytes(d)), x_perm, s));
+}
+
+moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* offsets,
+                         const void* w1, const void* w3, const float* s1, const float* s3, void* h,
+                         const FfnWs& ws, hipStream_t s) {
+  GemmArgs g{};
+  g.A = x_perm;
+  g.rows = int(n_assign(d));
+  g.tile_table = ws.table;
+  g.offsets = offsets;
+  g.n_slots = ws.n_slots;
+  g.B0 = w1;
+  g.B1 = w3;
+  g.s0 = s1;
+  g.s1 = s3;
+  g.N = d->f;
+  g.K = d->d;
+  g.C = h;
+  g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->wdtype);
+  g.epi = EPI_SWIGLU;
+  return dev(launch_gemm(g, s));
+}
+
+moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offsets, const void* w2,
+                         const float* s2, void* y, const FfnWs& ws, hipStream_t s) {
+  GemmArgs g{};
+  g.A = h;
+  g.rows = int(n_assign(d));
+  g.tile_table = ws.table;
+  g.offsets = offsets;
+  g.n_slots = ws.n_slots;
+  g.B0 = w2;
+  g.s0 = s2;
+  g.N = d->d;
+  g.K = d->f;
+  g.C = y;
+  g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->wdtype);
+  g.epi = EPI_STORE;
+  return dev(launch_gemm(g, s));
+}
+
+moe_status run_tables(const moe_desc* d, const int32_t* offsets, const FfnWs& ws, hipStream_t s) {
+  TileTableArgs t{offsets, d->E, block_m(d), ws.n_slots, ws.table, 0, 0, nullptr};
+  return dev(launch_tile_tables(t, s));
+}
+
+moe_status run_shared(const moe_desc* d, const void* x, const void* sw1, const void* sw3,
+                      const void* sw2, void* sh, void* sy, hipStream_t s) {
+  GemmArgs g{};
+  g.A = x;
+  g.rows = d->T;
+  g.B0 = sw1;
+  g.B1 = sw3;
+  g.N = d->f_shared;
+  g.K = d->d;
+  g.C = sh;
+  g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->act);
+  g.epi = EPI_SWIGLU;
+  MOE_TRY(dev(launch_gemm(g, s)));
+  GemmArgs g2{};
+  g2.A = sh;
+  g2.rows = d->T;
+  g2.B0 = sw2;
+  g2.N = d->d;
+  g2.K = d->f_shared;
+  g2.C = sy;
+  g2.act = gemm_dtype(d->act);
+  g2.wdt = gemm_dtype(d->act);
+  g2.epi = EPI_STORE;
+  return dev(launch_gemm(g2, s));
+}
+
+bool fp8(const moe_desc* d) { return d->wdtype == MOE_FP8_E4M3; }
+
+// scales must be present exactly when the weights are fp8
+bool scales_ok(const moe_desc* d, const float* s1, const float* s3, const float* s2) {
+  if (fp8(d)) return need(s1) && need(s3) && need(s2);
+  return s1 == nullptr && s3 == nullptr && s2 == nullptr;
+}
+
+moe_status record(void* const* trace, int i, hipStream_t s) {
+  if (trace == nullptr) return MOE_OK;
+  return dev(hipEventRecord(static_cast<hipEvent_t>(trace[i]), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: HIP call or kernel launch failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_validate(const moe_desc* desc) { return check_desc(desc); }
+
+moe_status moe_workspace_size(const moe_desc* desc, moe_stage stage, size_t* bytes) {
+  MOE_TRY(check_desc(desc));
+  if (bytes == nullptr) return MOE_ERR_INVALID;
+  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_LAYER) return MOE_ERR_INVALID;
+  *bytes = stage_bytes(desc, stage);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (d->T == 0) return MOE_OK;
+  if (!need(x) || !need(w_router) || !maybe(bias) || !need(topk_idx) || !need(topk_w) || !need(ws))
+    return MOE_ERR_INVALID;
+  if (ws_bytes < stage_bytes(d, MOE_STAGE_ROUTE)) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  const RouteWs w = carve_route(c, d);
+  return run_route(d, x, w_router, bias, topk_idx, topk_w, w, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
+                        void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!need(counts) || !need(offsets)) return MOE_ERR_INVALID;
+  if (d->T > 0 && (!need(topk_idx) || !need(x) || !need(perm_token) || !need(inv_pos) ||
+                   !need(x_perm) || !need(ws)))
+    return MOE_ERR_INVALID;
+  if (d->T > 0 && ws_bytes < stage_bytes(d, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  const DispatchWs w = carve_dispatch(c, d);
+  return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w,
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets,
+                           const void* w1, const void* w3, const void* w2, const float* s1,
+                           const float* s3, const float* s2, void* h, void* y_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (d->T == 0) return MOE_OK;
+  if (!need(x_perm) || !need(offsets) || !need(w1) || !need(w3) || !need(w2) || !need(h) ||
+      !need(y_perm) || !need(ws) || !scales_ok(d, s1, s3, s2))
+    return MOE_ERR_INVALID;
+  if (ws_bytes < stage_bytes(d, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  const FfnWs w = carve_ffn(c, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(run_tables(d, offsets, w, s));
+  MOE_TRY(run_ffn_gemm1(d, x_perm, offsets, w1, w3, s1, s3, h, w, s));
+  return run_ffn_gemm2(d, h, offsets, w2, s2, y_perm, w, s);
+}
+
+moe_status moe_combine(const moe_desc* d, const void* y_perm, const int32_t* inv_pos,
+                       const float* topk_w, const void* shared_y, void* out, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (d->T == 0) return MOE_OK;
+  if (!need(y_perm) || !need(inv_pos) || !need(topk_w) || !maybe(shared_y) || !need(out))
+    return MOE_ERR_INVALID;
+  CombineArgs a{y_perm, inv_pos, topk_w, shared_y, out, d->T, d->d, d->k, gemm_dtype(d->act)};
+  return dev(launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_router,
+                             const float* bias, const void* w1, const void* w3, const void* w2,
+                             const float* s1, const float* s3, const float* s2, const void* sw1,
+                             const void* sw3, const void* sw2, void* out, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, void* ws, size_t ws_bytes,
+                             void* stream, void* const* trace) {
+  MOE_TRY(check_desc(d));
+  if (!need(counts)) return MOE_ERR_INVALID;
+  const bool shared = d->f_shared > 0;
+  if (d->T > 0) {
+    if (!need(x) || !need(w_router) || !maybe(bias) || !need(w1) || !need(w3) || !need(w2) ||
+        !scales_ok(d, s1, s3, s2) || !need(out) || !need(topk_idx) || !need(topk_w) || !need(ws))
+      return MOE_ERR_INVALID;
+    if (shared ? !(need(sw1) && need(sw3) && need(sw2)) : (sw1 || sw3 || sw2))
+      return MOE_ERR_INVALID;
+  }
+  if (d->T > 0 && (ws_bytes < stage_bytes(d, MOE_STAGE_LAYER) || ws == nullptr))
+    return MOE_ERR_WORKSPACE;
+  if (trace) {
+    for (int i = 0; i < MOE_TRACE_EVENTS; ++i)
+      if (trace[i] == nullptr) return MOE_ERR_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->T == 0) {  // nothing routed: counts are all zero
+    DispatchArgs a{nullptr, 0, d->E, d->k, nullptr, counts, nullptr, nullptr, nullptr};
+    return dev(launch_dispatch_index(a, s));
+  }
+  Carve c(ws);
+  const LayerWs w = carve_layer(c, d);
+  MOE_TRY(record(trace, 0, s));
+  MOE_TRY(run_route(d, x, w_router, bias, topk_idx, topk_w, w.route, s));
+  MOE_TRY(record(trace, 1, s));
+  MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos, w.x_perm, w.disp, s));
+  MOE_TRY(record(trace, 2, s));
+  MOE_TRY(run_tables(d, w.offsets, w.ffn, s));
+  MOE_TRY(run_ffn_gemm1(d, w.x_perm, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s));
+  MOE_TRY(record(trace, 3, s));
+  MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s));
+  MOE_TRY(record(trace, 4, s));
+  if (shared) MOE_TRY(run_shared(d, x, sw1, sw3, sw2, w.sh, w.sy, s));
+  MOE_TRY(record(trace, 5, s));
+  CombineArgs a{w.y_perm, w.inv_pos, topk_w, shared ? w.sy : nullptr, out, d->T, d->d, d->k,
+                gemm_dtype(d->act)};
+  MOE_TRY(dev(launch_combine(a, s)));
+  return record(trace, 6, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal interfaces between the C ABI (moe_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- device utils
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// OCP E4M3 byte -> bf16 bits (exact: every E4M3 value is a bf16 value).
+// Normal: exponent rebias 7 -> 127, mantissa moves up 4 bits.
+// Subnormal (exp 0): value m * 2^-9, built from the integer m.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 8;
+  const uint32_t em = b & 0x7fu;
+  uint32_t mag;
+  if (em >= 0x08u) {
+    mag = (em << 4) + (120u << 7);
+  } else {
+    mag = __float_as_uint((float)em * 0.001953125f) >> 16;  // m * 2^-9, exact
+  }
+  return sign | mag;
+}
+
+// ------------------------------------------------------------------ launchers
+struct RouteSelectArgs {
+  const float* z;        // [T][E] router logits (bias included)
+  int T, E, k, score, renorm, n_group, topk_group;
+  int32_t* topk_idx;     // [T][k]
+  float* topk_w;         // [T][k]
+};
+hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s);
+
+// Dispatch: assignments are processed in chunks of kDispatchChunk.
+constexpr int kDispatchChunk = 1024;
+struct DispatchArgs {
+  const int32_t* topk_idx;  // [T*k]
+  int n_assign, E, k;
+  int32_t* chunk_cnt;       // [n_chunks][E] workspace (counts, then bases)
+  int32_t* counts;          // [E]
+  int32_t* offsets;         // [E+1]
+  int32_t* perm_token;      // [n_assign]
+  int32_t* inv_pos;         // [n_assign]
+};
+hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
+
+// x_perm[p] = x[perm_token[p]], rows of row_bytes (multiple of 16).
+hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, int row_bytes,
+                              void* x_perm, hipStream_t s);
+
+// Combine.
+struct CombineArgs {
+  const void* y_perm;
+  const int32_t* inv_pos;
+  const float* topk_w;
+  const void* shared_y;  // nullable
+  void* out;
+  int T, d, k, act;      // act: 0 f32, 1 bf16
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Grouped GEMM over ragged expert segments.
+//   C[m][n] = epilogue( sum_k A[m][k] * B_e[n][k] )
+// A rows are activations (row-major, K contiguous); B_e is the weight matrix
+// of the segment's expert (out x in, K contiguous).
+enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_BIAS_F32 = 2 };
+enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };
+
+struct GemmArgs {
+  const void* A;               // [rows][K] activations
+  int rows;                    // rows of A (all segments)
+  const int32_t* tile_table;   // [n_slots] (expert << 16 | m-tile in expert) or -1; NULL: one segment
+  const int32_t* offsets;      // [E+1] segment starts (NULL: one segment of `rows`)
+  int n_slots;                 // m-tile slots in the grid
+  const void* B0;              // [E][N][K] weights (gate projection W1 for SwiGLU)
+  const void* B1;              // [E][N][K] up projection W3 (SwiGLU only)
+  const float* s0;             // [E][N] fp8 scales of B0 (NULL otherwise)
+  const float* s1;             // [E][N] fp8 scales of B1
+  const float* bias;           // [N] (EPI_BIAS_F32)
+  int N;                       // output columns (h columns for SwiGLU)
+  int K;
+  void* C;                     // [rows][N] output
+  int act;                     // GemmDtype of A and C (F32 or BF16); EPI_BIAS_F32 stores f32
+  int wdt;                     // GemmDtype of B
+  int epi;                     // GemmEpilogue
+};
+
+// Rows per m-tile the grouped GEMM uses for this problem (the tile table must
+// be built with the same value).
+int gemm_block_m(const GemmArgs& a);
+// Upper bound of m-tile slots for `rows` rows in E segments.
+int gemm_max_slots(int rows, int E, int block_m);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// Tile tables for up to two tile heights from segment offsets.
+struct TileTableArgs {
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int bm0, n_slots0;
+  int32_t* table0;         // [n_slots0]
+  int bm1, n_slots1;       // bm1 = 0: only one table
+  int32_t* table1;
+};
+hipError_t launch_tile_tables(const TileTableArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,169 @@
+// Router selection: scores, optional group limit, top-k and gates, one
+// wavefront per token.
+//
+// The logits z = x Wr^T + b come from the grouped-GEMM kernel (EPI_BIAS_F32).
+// Following the per-token routing path of "Expert-Parallel MoE Inference:
+// Serving Sparse Models at Scale" (section "Deeper Analysis", first paragraph,
+// Figure 2): scores are softmax over the E logits or the element-wise sigmoid,
+// the k best eligible experts are kept, and their gates are the scores,
+// optionally divided by their sum over the chosen k.
+//
+// Selection compares packed 64-bit keys (order-preserving bits of the fp32
+// logit << 32 | ~expert id), so the largest key is the largest score with ties
+// going to the lower id.  Softmax and sigmoid are strictly increasing in the
+// logit, so ranking logits ranks scores.  Each lane holds experts
+// lane, lane+64, ... (up to 8 for E <= 512); the wave-wide maximum is a
+// butterfly of DPP/ds_swizzle shuffles.  With a group limit (the single-GPU
+// form of node-limited routing, same page, section "Load imbalance and how to
+// fight it"), group scores (sum of each contiguous group's two largest scores)
+// go through LDS and groups outside the best topk_group are masked out.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxV = 8;       // experts per lane (E <= 512)
+constexpr int kMaxE = 512;
+constexpr int kMaxGroups = 64;
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectArgs a) {
+  __shared__ float s_score[kWaves][kMaxE];
+  __shared__ float s_gscore[kWaves][kMaxGroups];
+  __shared__ int s_keep[kWaves][kMaxGroups];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kWaves + wave;
+  const bool live = t < a.T;                 // whole-wave condition
+  const int tt = live ? t : a.T - 1;         // dead waves still reach every barrier
+  const float* zrow = a.z + (size_t)tt * a.E;
+
+  float z[kMaxV];
+  uint64_t key[kMaxV];
+#pragma unroll
+  for (int v = 0; v < kMaxV; ++v) {
+    const int e = lane + 64 * v;
+    z[v] = (e < a.E) ? zrow[e] : -INFINITY;
+    key[v] = (e < a.E) ? (((uint64_t)ordered_bits(z[v]) << 32) | (uint32_t)(~e)) : 0ull;
+  }
+
+  // softmax statistics over all E experts (max and sum of exp)
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kMaxV; ++v) zmax = fmaxf(zmax, z[v]);
+  zmax = wave_max(zmax);
+  float esum = 0.f;
+  if (a.score == 0) {
+#pragma unroll
+    for (int v = 0; v < kMaxV; ++v)
+      if (lane + 64 * v < a.E) esum += expf(z[v] - zmax);
+    esum = wave_sum(esum);
+  }
+
+  if (a.n_group > 0) {
+    const int G = a.E / a.n_group;
+#pragma unroll
+    for (int v = 0; v < kMaxV; ++v) {
+      const int e = lane + 64 * v;
+      if (e < a.E)
+        s_score[wave][e] = (a.score == 0) ? expf(z[v] - zmax) / esum : 1.f / (1.f + expf(-z[v]));
+    }
+    __syncthreads();
+    if (lane < a.n_group) {
+      float b0 = -INFINITY, b1 = -INFINITY;  // two largest scores of the group
+      for (int i = 0; i < G; ++i) {
+        const float s = s_score[wave][lane * G + i];
+        if (s > b0) { b1 = b0; b0 = s; } else if (s > b1) { b1 = s; }
+      }
+      s_gscore[wave][lane] = b0 + b1;
+    }
+    __syncthreads();
+    if (lane < a.n_group) {
+      const float mine = s_gscore[wave][lane];
+      int rank = 0;
+      for (int g = 0; g < a.n_group; ++g) {
+        const float o = s_gscore[wave][g];
+        rank += (o > mine) || (o == mine && g < lane);
+      }
+      s_keep[wave][lane] = rank < a.topk_group;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kMaxV; ++v) {
+      const int e = lane + 64 * v;
+      if (e < a.E && !s_keep[wave][e / G]) key[v] = 0ull;
+    }
+  }
+
+  // top-k: k rounds of wave-wide maximum; the owner retires the winner
+  uint64_t mine_key = 0ull;  // lane j keeps the j-th winner
+  for (int j = 0; j < a.k; ++j) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int v = 0; v < kMaxV; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int v = 0; v < kMaxV; ++v)
+      if (key[v] == best) key[v] = 0ull;
+    if (lane == j) mine_key = best;
+  }
+
+  const bool sel = lane < a.k;
+  const int e_sel = (int)(~(uint32_t)mine_key);
+  const float z_sel = from_ordered_bits((uint32_t)(mine_key >> 32));
+  float g;
+  if (a.score == 0) {
+    g = sel ? expf(z_sel - zmax) : 0.f;
+    const float denom = a.renorm ? wave_sum(g) : esum;
+    g = g / denom;
+  } else {
+    g = sel ? 1.f / (1.f + expf(-z_sel)) : 0.f;
+    if (a.renorm) g = g / wave_sum(g);
+  }
+  if (live && sel) {
+    a.topk_idx[(size_t)t * a.k + lane] = e_sel;
+    a.topk_w[(size_t)t * a.k + lane] = g;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int blocks = (a.T + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(route_select_kernel, dim3(blocks), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,263 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Sizes here are ones the oracle finishes in seconds while still spanning
+several GEMM tiles, ragged segment tails and empty experts.  Routing indices,
+counts, offsets and the permutation must be bit-exact; values must be within
+the tolerances in tests/helpers.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_36_amd as moe
+import oracle as O
+from synth import LayerInputs
+from synth.workloads import (DSV3_DECODE, DSV3_PREFILL_SKEW, MIXTRAL_PREFILL, QWEN_FP8_SKEW,
+                             TINY_F32)
+from tests.helpers import (DeviceLayer, assert_dispatch, assert_routing, assert_values,
+                           from_torch, oracle_layer, to_torch)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_f32": TINY_F32,
+    "tiny_f32_ragged": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3),
+    "mixtral_small": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384),
+    "mixtral_tiles": MIXTRAL_PREFILL.scaled(T=700, d=512, f=640),
+    "dsv3_decode_small": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256),
+    "dsv3_skew_small": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128),
+    "qwen_fp8_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32),
+}
+
+_CACHE = {}
+
+
+def _setup(name, seed=1):
+    key = (name, seed)
+    if key not in _CACHE:
+        w = CASES[name]
+        L = LayerInputs(w, seed, accept=O.margin_acceptor())
+        _CACHE[key] = (w, L, DeviceLayer(L), oracle_layer(L))
+    return _CACHE[key]
+
+
+def _scores(L):
+    x, wr, b = O.decoded_inputs(L)
+    return O.expert_scores(O.router_logits(x, wr, b), L.w.score)
+
+
+def _run_layer(w, dev, desc=None):
+    desc = desc or moe.Desc.from_attrs(w)
+    T = w.T
+    out = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
+    idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    ws = moe.workspace(desc)
+    moe.layer_forward(desc, dev.x, dev.w_router, dev.bias, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3,
+                      dev.s2, dev.sw1, dev.sw3, dev.sw2, out, idx, gw, counts, ws)
+    torch.cuda.synchronize()
+    return out, idx, gw, counts
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_forward(name):
+    w, L, dev, ref = _setup(name)
+    out, idx, gw, counts = _run_layer(w, dev)
+    idx_h = idx.cpu().numpy()
+    assert_routing(idx_h, gw.cpu().numpy(), ref, _scores(L))
+    assert np.array_equal(counts.cpu().numpy(), ref.counts)
+    err = assert_values(from_torch(out, w.act), ref.out, w, "out")
+    print(f"{name}: out err {err:.3g}")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_stages_chain(name):
+    """route -> dispatch -> grouped_ffn -> combine, each output checked."""
+    w, L, dev, ref = _setup(name)
+    desc = moe.Desc.from_attrs(w)
+    T, A = w.T, w.T * w.k
+    idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+    moe.route(desc, dev.x, dev.w_router, dev.bias, idx, gw, moe.workspace(desc, moe.STAGE_ROUTE))
+    torch.cuda.synchronize()
+    assert_routing(idx.cpu().numpy(), gw.cpu().numpy(), ref, _scores(L))
+
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(A, dtype=torch.int32, device="cuda")
+    inv = torch.empty(A, dtype=torch.int32, device="cuda")
+    x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.dispatch(desc, idx, dev.x, counts, offsets, perm, inv, x_perm,
+                 moe.workspace(desc, moe.STAGE_DISPATCH))
+    torch.cuda.synchronize()
+    assert_dispatch(idx.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(),
+                    perm.cpu().numpy(), inv.cpu().numpy(), ref)
+    assert torch.equal(x_perm, dev.x[perm.long()])  # bitwise row copies
+
+    h = torch.empty((A, w.f), dtype=dev.x.dtype, device="cuda")
+    y = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.grouped_ffn(desc, x_perm, offsets, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3, dev.s2, h, y,
+                    moe.workspace(desc, moe.STAGE_FFN))
+    torch.cuda.synchronize()
+    eh = assert_values(from_torch(h, w.act), ref.h, w, "h")
+    ey = assert_values(from_torch(y, w.act), ref.y_perm, w, "y_perm")
+
+    out = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.combine(desc, y, inv, gw, None, out)
+    torch.cuda.synchronize()
+    # combine alone: compare with the oracle combine of the GPU's own y_perm
+    ref_c = O.combine(from_torch(y, w.act), inv.cpu().numpy(), gw.cpu().numpy().astype(np.float64),
+                      w.act)
+    ec = assert_values(from_torch(out, w.act), ref_c, w, "combine")
+    print(f"{name}: h {eh:.3g} y {ey:.3g} combine {ec:.3g}")
+
+
+@pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small"])
+def test_grouped_ffn_from_oracle_inputs(name):
+    """The FFN stage fed the oracle's own x_perm and offsets."""
+    w, L, dev, ref = _setup(name)
+    desc = moe.Desc.from_attrs(w)
+    A = w.T * w.k
+    if w.act == "bf16":
+        xp = to_torch(O_encode_bf16(ref.x_perm), "bf16")
+    else:
+        xp = to_torch(ref.x_perm.astype(np.float32), "f32")
+    offsets = torch.from_numpy(ref.offsets).cuda()
+    h = torch.empty((A, w.f), dtype=xp.dtype, device="cuda")
+    y = torch.empty((A, w.d), dtype=xp.dtype, device="cuda")
+    moe.grouped_ffn(desc, xp, offsets, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3, dev.s2, h, y,
+                    moe.workspace(desc, moe.STAGE_FFN))
+    torch.cuda.synchronize()
+    assert_values(from_torch(h, w.act), ref.h, w, "h")
+    assert_values(from_torch(y, w.act), ref.y_perm, w, "y_perm")
+
+
+def O_encode_bf16(a):
+    """float64 values that are exactly bf16 -> bf16 bit patterns."""
+    f = a.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), a)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_shared_expert_and_combine_from_oracle_inputs():
+    w, L, dev, ref = _setup("dsv3_decode_small")
+    desc = moe.Desc.from_attrs(w)
+    y = to_torch(O_encode_bf16(ref.y_perm), "bf16")
+    ys = to_torch(O_encode_bf16(ref.shared_y), "bf16")
+    inv = torch.from_numpy(ref.inv_pos).cuda()
+    gw = torch.from_numpy(ref.topk_w.astype(np.float32)).cuda()
+    out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    moe.combine(desc, y, inv, gw, ys, out)
+    torch.cuda.synchronize()
+    ref_out = O.combine(ref.y_perm, ref.inv_pos, gw.cpu().numpy().astype(np.float64), "bf16",
+                        ref.shared_y)
+    # same inputs, fp32 vs fp64 accumulation: at most one bf16 rounding apart
+    got = from_torch(out, "bf16")
+    assert np.max(np.abs(got - ref_out)) <= 2.0 ** -7 * np.max(np.abs(ref_out))
+
+
+@pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small"])
+def test_deterministic(name):
+    w, L, dev, ref = _setup(name)
+    a = _run_layer(w, dev)
+    b = _run_layer(w, dev)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+# ----------------------------------------------------------------- edge cases
+
+def _custom(w, seed=3, bias=None, wr=None, accept=True):
+    L = LayerInputs(w, seed)
+    if bias is not None:
+        L.bias = np.asarray(bias, dtype=np.float32)
+    if wr is not None:
+        L.w_router = wr
+    if accept:
+        L._redraw(O.margin_acceptor())
+    return L
+
+
+def _check_custom(L, exact_order=False):
+    w = L.w
+    dev = DeviceLayer(L)
+    ref = oracle_layer(L)
+    out, idx, gw, counts = _run_layer(w, dev)
+    idx_h = idx.cpu().numpy()
+    if exact_order:
+        assert np.array_equal(idx_h, ref.topk_idx)
+        assert np.allclose(gw.cpu().numpy(), ref.topk_w, rtol=0, atol=1e-6)
+    else:
+        assert_routing(idx_h, gw.cpu().numpy(), ref, _scores(L))
+    assert np.array_equal(counts.cpu().numpy(), ref.counts)
+    assert_values(from_torch(out, w.act), ref.out, w, "out")
+    return ref
+
+
+@pytest.mark.parametrize("T", [1, 2, 129])
+def test_token_counts(T):
+    _check_custom(_custom(MIXTRAL_PREFILL.scaled(T=T, d=256, f=256)))
+
+
+def test_zero_tokens():
+    w = MIXTRAL_PREFILL.scaled(T=0, d=256, f=256)
+    desc = moe.Desc.from_attrs(w)
+    counts = torch.full((w.E,), 7, dtype=torch.int32, device="cuda")
+    e = torch.empty(0, device="cuda")
+    moe.layer_forward(desc, e, e, None, e, e, e, None, None, None, None, None, None, e, e, e,
+                      counts, None)
+    torch.cuda.synchronize()
+    assert (counts.cpu() == 0).all()
+
+
+def test_single_expert_dense():
+    _check_custom(_custom(MIXTRAL_PREFILL.scaled(T=100, d=256, f=256, E=1, k=1)))
+
+
+def test_k_equals_e():
+    _check_custom(_custom(MIXTRAL_PREFILL.scaled(T=64, d=256, f=256, E=8, k=8)))
+
+
+def test_all_tokens_one_expert():
+    w = QWEN_FP8_SKEW.scaled(T=200, d=256, f=256, E=16, k=2, bias_scale=0.0)
+    b = np.zeros(16, dtype=np.float32)
+    b[11] = 100.0
+    ref = _check_custom(_custom(w, bias=b))
+    assert ref.counts[11] == 200
+
+
+def test_empty_experts():
+    w = DSV3_PREFILL_SKEW.scaled(T=8, d=256, f=256, E=128, n_group=8, topk_group=4, f_shared=0)
+    ref = _check_custom(_custom(w))
+    assert (ref.counts == 0).sum() > 0
+
+
+def test_ties_zero_router():
+    w = MIXTRAL_PREFILL.scaled(T=50, d=256, f=256, E=8, k=3)
+    L = _custom(w, wr=np.zeros((8, 256), dtype=np.uint16), accept=False)
+    ref = _check_custom(L, exact_order=True)
+    assert (ref.topk_idx == np.arange(3)).all()
+
+
+def test_ties_duplicate_router_rows():
+    w = MIXTRAL_PREFILL.scaled(T=64, d=256, f=256, E=8, k=2)
+    L = LayerInputs(w, 5)
+    wr = L.w_router.copy()
+    wr[5] = wr[2]
+    bias = np.full(8, -10.0, dtype=np.float32)
+    bias[2] = bias[5] = 10.0
+    L = _custom(w, seed=5, bias=bias, wr=wr, accept=False)
+    ref = _check_custom(L, exact_order=True)
+    assert (ref.topk_idx == np.array([2, 5])).all()
+
+
+def test_sigmoid_no_renorm():
+    w = DSV3_DECODE.scaled(T=64, d=256, f=256, E=32, f_shared=0, renorm=False)
+    _check_custom(_custom(w))
+
+
+def test_softmax_no_renorm_group_limit():
+    w = QWEN_FP8_SKEW.scaled(T=96, d=256, f=256, E=32, renorm=False, n_group=4, topk_group=2,
+                             wdt="bf16")
+    _check_custom(_custom(w))
