@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (router, dispatch, grouped SwiGLU FFN, shared
+expert when present, combine) over one batch of seeded synthetic tokens, with
+inputs already resident in HBM.  Prints one JSON line:
+
+  value       tokens/s = T * steps / wall time of the timed steps
+  roofline    the routed gate-up GEMM (+SwiGLU) kernel against the bf16 MFMA
+              peak, or, for decode-shaped layers, the whole layer's
+              algorithmic bytes against HBM bandwidth; its duration comes from
+              HIP events the library records around each stage inside the
+              timed steps, on the stream the kernels run on
+  cpu_baseline the float64 oracle on a bounded token sample, host cores
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s per MI355X; grouped-GEMM % MFMA peak; decode % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DEFAULT_WORKLOAD = "mixtral8x7b_prefill_bf16"
+DECODE_WORKLOADS = {"dsv3_decode_bf16"}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=None, help="tokens for the oracle timing")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_36_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def layer_bytes(w, counts) -> float:
+    """Algorithmic HBM bytes of one layer forward: x, router weight and bias,
+    the touched experts' weights (+ scales), the shared expert, out, and the
+    routing outputs (topk idx + w)."""
+    ab = 4 if w.act == "f32" else 2
+    wb = {"f32": 4, "bf16": 2, "e4m3": 1}[w.wdt]
+    touched = int((counts > 0).sum())
+    per_expert = 3 * w.d * w.f * wb + (2 * w.f + w.d) * 4 * (w.wdt == "e4m3")
+    b = w.T * w.d * ab * 2 + w.E * w.d * ab + w.E * 4 + touched * per_expert
+    b += 3 * w.d * w.f_shared * ab + 8 * w.T * w.k
+    return float(b)
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def cpu_baseline(w, L, host_experts, sample):
+    """The float64 oracle on the first `sample` tokens (the layer is
+    token-wise, so this is exactly those tokens' forward)."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    x, wr, b = O.decoded_inputs(L)
+    xs = x[:sample]
+
+    def expert(e):
+        ew = host_experts[e]
+        w1, w3, w2 = O.decode(ew.w1, w.wdt), O.decode(ew.w3, w.wdt), O.decode(ew.w2, w.wdt)
+        if w.wdt == "e4m3":
+            w1 = w1 * ew.s1.astype(np.float64)[:, None]
+            w3 = w3 * ew.s3.astype(np.float64)[:, None]
+            w2 = w2 * ew.s2.astype(np.float64)[:, None]
+        return w1, w3, w2
+
+    shared = O.adapters.decoded_shared(L)
+    t0 = time.perf_counter()
+    O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {sample} of {w.T} tokens, full layer forward in float64 "
+                      f"(routing, dispatch, experts, combine), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_layer_36_amd as moe
+    from synth import DEFAULT_SEED, BY_NAME, LayerInputs
+    from synth.device import DeviceLayer
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    w = BY_NAME[args.workload]
+    seed = DEFAULT_SEED[w.name] if args.seed is None else args.seed
+    L = LayerInputs(w, seed)
+    host_experts = {}
+
+    # upload expert by expert, keeping host copies for the CPU baseline
+    orig = L.expert
+
+    def keep(e):
+        ew = orig(e)
+        if not args.no_cpu_baseline:
+            host_experts[e] = ew
+        return ew
+
+    L.expert = keep
+    dev = DeviceLayer(L)
+    L.expert = orig
+
+    desc = moe.Desc.from_attrs(w)
+    out = torch.empty((w.T, w.d), dtype=dev.x.dtype, device="cuda")
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    ws = moe.workspace(desc)
+
+    def step(trace=None):
+        moe.layer_forward(desc, dev.x, dev.w_router, dev.bias, dev.w1, dev.w3, dev.w2, dev.s1,
+                          dev.s3, dev.s2, dev.sw1, dev.sw3, dev.sw2, out, idx, gw, counts, ws,
+                          trace=trace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    traces = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)]
+              for _ in range(args.steps)]
+    for tr in traces:  # create the HIP events before the timed region
+        for ev in tr:
+            ev.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(traces[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
+                         for tr in traces])
+    stage_us = {name: round(float(stage_ms[:, j].mean()) * 1e3, 2)
+                for j, name in enumerate(moe.TRACE_STAGES)}
+    step_event_ms = float(np.mean([tr[0].elapsed_time(tr[-1]) for tr in traces]))
+    c = counts.cpu().numpy()
+    n_assign = int(c.sum())
+    assert n_assign == w.T * w.k, "routing lost assignments"
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = w.T * args.steps / elapsed
+    gemm1_s = stage_ms[:, 2].mean() * 1e-3
+    flops_gemm1 = 4.0 * w.d * w.f * n_assign
+    flops_all = 6.0 * w.d * w.f * n_assign + 6.0 * w.d * w.f_shared * w.T
+    if w.name in DECODE_WORKLOADS:
+        layer_s = step_event_ms * 1e-3
+        achieved = layer_bytes(w, c) / layer_s / 1e9
+        roof = {"bound": "hbm", "kernel": "whole layer (all kernels)", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes": layer_bytes(w, c)}
+    else:
+        achieved = flops_gemm1 / gemm1_s / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_mfma_kernel<EPI_SWIGLU> (routed gate-up + SwiGLU)",
+                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops_gemm1,
+                "avg_launch_us": round(gemm1_s * 1e6, 2)}
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        ent = tr.get(w.name)
+        if ent and ent.get("source_hash") == kernel_source_hash():
+            roof["traffic"] = ent.get("bytes_per_launch")
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.act == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
+                   "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
+                   "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed},
+        "roofline": roof,
+        "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
+        "stages_us": stage_us,
+        "step_event_ms": round(step_event_ms, 4),
+        "load": {"max_over_mean": round(float(c.max() / c.mean()), 3),
+                 "experts_touched": int((c > 0).sum()), "experts": w.E},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or {"mixtral8x7b_prefill_bf16": 48, "tiny_f32": 64}.get(w.name, 16)
+        rec["cpu_baseline"] = cpu_baseline(w, L, host_experts, min(sample, w.T))
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

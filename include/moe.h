@@ -167,8 +167,8 @@ moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* 
  *   sw1, sw3, sw2: shared expert, NULL when f_shared == 0.
  *   trace: NULL, or MOE_TRACE_EVENTS hipEvent_t (host array of handles)
  *          recorded on `stream` before the router and after the router,
- *          dispatch, routed gate-up GEMM, routed down GEMM, shared expert and
- *          combine, for per-stage timing. */
+ *          dispatch (with the GEMM tile table), routed gate-up GEMM, routed
+ *          down GEMM, shared expert and combine, for per-stage timing. */
 moe_status moe_layer_forward(const moe_desc* desc, const void* x, const void* w_router,
                              const float* bias, const void* w1, const void* w3, const void* w2,
                              const float* s1, const float* s3, const float* s2,

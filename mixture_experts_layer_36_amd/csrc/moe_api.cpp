@@ -378,8 +378,8 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(run_route(d, x, w_router, bias, topk_idx, topk_w, w.route, s));
   MOE_TRY(record(trace, 1, s));
   MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos, w.x_perm, w.disp, s));
-  MOE_TRY(record(trace, 2, s));
   MOE_TRY(run_tables(d, w.offsets, w.ffn, s));
+  MOE_TRY(record(trace, 2, s));
   MOE_TRY(run_ffn_gemm1(d, w.x_perm, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s));
   MOE_TRY(record(trace, 3, s));
   MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s));

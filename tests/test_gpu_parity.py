@@ -220,7 +220,8 @@ def test_k_equals_e():
 
 
 def test_all_tokens_one_expert():
-    w = QWEN_FP8_SKEW.scaled(T=200, d=256, f=256, E=16, k=2, bias_scale=0.0)
+    # sigmoid scores: the other experts keep usable margins beside the +100 one
+    w = DSV3_DECODE.scaled(T=200, d=256, f=256, E=16, k=2, f_shared=0)
     b = np.zeros(16, dtype=np.float32)
     b[11] = 100.0
     ref = _check_custom(_custom(w, bias=b))
