@@ -27,45 +27,10 @@
 // Grid: m-tile slots x n-tiles, remapped so that each XCD (blocks are dealt
 // round-robin to the 8 XCDs) runs a contiguous run of slots of one n-tile and
 // its L2 holds the weight tile those slots share.
-#include "moe_internal.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 namespace {
-
-constexpr int kTableExpertShift = 22;
-constexpr int kTableTileMask = (1 << kTableExpertShift) - 1;
-
-struct TileInfo {
-  int e, row0, nrows;
-};
-
-__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti) {
-  if (a.tile_table == nullptr) {
-    ti.e = 0;
-    ti.row0 = mt * BM;
-    ti.nrows = min(BM, a.rows - ti.row0);
-    return ti.nrows > 0;
-  }
-  const int code = a.tile_table[mt];
-  if (code < 0) return false;
-  ti.e = code >> kTableExpertShift;
-  const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
-  ti.row0 = lo + (code & kTableTileMask) * BM;
-  ti.nrows = min(BM, hi - ti.row0);
-  return ti.nrows > 0;
-}
-
-// block id -> (m-slot, n-tile), XCD-aware
-__device__ __forceinline__ void block_coords(int n_slots, int n_tiles, int& mt, int& nt) {
-  const int nb = gridDim.x;  // a multiple of 8
-  const int b = blockIdx.x;
-  const int L = (b & 7) * (nb >> 3) + (b >> 3);
-  mt = L % n_slots;
-  nt = L / n_slots;
-  if (nt >= n_tiles) mt = -1;
-}
-
-__device__ __forceinline__ float silu(float u) { return u / (1.f + expf(-u)); }
 
 // ============================================================== MFMA kernel
 template <int BM, int BN, int WDT, int EPI>
@@ -92,7 +57,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][(BM + BN) * C::BK];
 
   int mt, nt;
-  block_coords(n_slots, n_tiles, mt, nt);
+  block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
   if (mt < 0) return;
   TileInfo ti;
   if (!tile_info(a, mt, BM, ti)) return;
@@ -208,73 +173,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds, per 32x32 block and group g, output columns
-  // 4 consecutive (g*8 + (lane/32)*4 + 0..3) of activation row (lane % 32).
-  const int r_in = lane & 31;
-#pragma unroll
-  for (int j = 0; j < C::TA; ++j) {
-    const int lrow = wm * C::RA + j * 32 + r_in;
-    if (lrow >= ti.nrows) continue;
-    const size_t row = (size_t)(ti.row0 + lrow);
-    if (EPI == EPI_SWIGLU) {
-#pragma unroll
-      for (int i = 0; i < C::TW / 2; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = ncol0 + wn * (C::RW / 2) + i * 32 + g * 8 + (lane >> 5) * 4;
-          float hv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float u = acc[i][j][g * 4 + q];
-            float v = acc[i + C::TW / 2][j][g * 4 + q];
-            if (WDT == GD_FP8) {
-              u *= a.s0[(size_t)ti.e * a.N + n + q];
-              v *= a.s1[(size_t)ti.e * a.N + n + q];
-            }
-            hv[q] = silu(u) * v;
-          }
-          u32x2 o;
-          o[0] = pack_bf16x2(hv[0], hv[1]);
-          o[1] = pack_bf16x2(hv[2], hv[3]);
-          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
-        }
-      }
-    } else if (EPI == EPI_STORE) {
-#pragma unroll
-      for (int i = 0; i < C::TW; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = ncol0 + wn * C::RW + i * 32 + g * 8 + (lane >> 5) * 4;
-          float yv[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            yv[q] = acc[i][j][g * 4 + q];
-            if (WDT == GD_FP8) yv[q] *= a.s0[(size_t)ti.e * a.N + n + q];
-          }
-          u32x2 o;
-          o[0] = pack_bf16x2(yv[0], yv[1]);
-          o[1] = pack_bf16x2(yv[2], yv[3]);
-          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
-        }
-      }
-    } else {  // EPI_BIAS_F32: router logits
-#pragma unroll
-      for (int i = 0; i < C::TW; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = ncol0 + wn * C::RW + i * 32 + g * 8 + (lane >> 5) * 4;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (n + q < a.N) {
-              float z = acc[i][j][g * 4 + q];
-              if (a.bias) z += a.bias[n + q];
-              ((float*)a.C)[row * a.N + n + q] = z;
-            }
-          }
-        }
-      }
-    }
-  }
+  const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
+  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, acc, wm * C::RA, col0, lane);
 }
 
 // ============================================================== fp32 kernel
@@ -288,7 +188,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
   int mt, nt;
-  block_coords(n_slots, n_tiles, mt, nt);
+  block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
   if (mt < 0) return;
   TileInfo ti;
   if (!tile_info(a, mt, BM, ti)) return;
@@ -373,6 +273,7 @@ __global__ __launch_bounds__(512) void tile_table_kernel(TileTableArgs t) {
     const int n_slots = w == 0 ? t.n_slots0 : t.n_slots1;
     for (int i = 0; i < tiles; ++i) table[incl - tiles + i] = (e << kTableExpertShift) | i;
     for (int s = total + e; s < n_slots; s += 512) table[s] = -1;
+    if (e == 0) table[n_slots] = total;  // real m-tiles, read by every GEMM block
   }
 }
 
@@ -409,7 +310,18 @@ hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int gemm_block_m(const GemmArgs& a) { return a.act == GD_F32 ? 64 : 128; }
+// Prefill-shaped bf16 problems (enough rows per expert to fill 256-row tiles)
+// go to the direct-to-LDS 256-row kernel; the rest use 128-row tiles.
+static bool use_big(const GemmArgs& a) {
+  if (a.act != GD_BF16 || a.wdt != GD_BF16 || a.epi == EPI_BIAS_F32) return false;
+  const int segs = a.E > 0 ? a.E : 1;
+  return a.rows >= 1024 && a.rows / segs >= 128;
+}
+
+int gemm_block_m(const GemmArgs& a) {
+  if (a.act == GD_F32) return 64;
+  return use_big(a) ? 256 : 128;
+}
 
 int gemm_max_slots(int rows, int E, int block_m) {
   return (rows + block_m - 1) / block_m + E;
@@ -424,6 +336,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       default: return launch_f32<EPI_BIAS_F32>(a, s);
     }
   }
+  if (use_big(a)) return launch_gemm_big(a, s);
   return a.wdt == GD_FP8 ? launch_mfma_epi<GD_FP8>(a, s) : launch_mfma_epi<GD_BF16>(a, s);
 }
 

@@ -1,0 +1,245 @@
+// Prefill-shaped grouped GEMM for gfx950: 256 x BN block tiles fed by
+// direct-to-LDS loads through a 4-stage pipeline.
+//
+// Experts run as grouped GEMMs over their expert-contiguous rows ("Tensor vs
+// Expert vs Data Parallelism for MoE Serving", section "Deeper Analysis",
+// Figure 2); in the large-batch regime each expert sees enough rows for the
+// GEMM to be compute-bound (same page, section "Why sparsity demands a large
+// batch").  This kernel is built for that regime:
+//   * block tile 256 activation rows x BN weight rows (BN = 256 or 128),
+//     BK = 32, four wavefronts in a 2 x 2 grid, so each wavefront owns a
+//     128 x (BN/2) tile: 16 (or 8) v_mfma_f32_32x32x16_bf16 per 8 (or 6)
+//     128-bit LDS fragment reads, with the accumulators in AGPRs;
+//   * global -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
+//     4-deep ring of 32 KB stages, refilled four stages ahead; each wave
+//     waits only for its own loads of the next stage (vmcnt) and a bare
+//     s_barrier publishes them, so later stages stay in flight;
+//   * the LDS fragments of the next k16 step are read while the current
+//     step's MFMAs run (two fragment sets, interleaved by
+//     sched_group_barrier), across the stage boundary too;
+//   * LDS rows of BK elements with 16-byte chunks XOR-swizzled by row
+//     ((r >> 2) & 3 for 64-byte rows, (r ^ (r >> 3)) & 7 for 128-byte rows):
+//     measured on gfx950 (64 banks; a 128-bit read is served 16 lanes at a
+//     time), these make the fragment reads of 32 rows x 1 chunk
+//     conflict-free.  A direct load writes 64 consecutive 16-byte slots, so
+//     each lane fetches the global chunk that belongs in its slot.
+#include "gemm_common.hpp"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_BIG_BK
+#define MOE_BIG_BK 32
+#endif
+#ifndef MOE_BIG_STAGES
+#define MOE_BIG_STAGES 4
+#endif
+constexpr int BM = 256, BK = MOE_BIG_BK, STAGES = MOE_BIG_STAGES, NTHR = 256;
+constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
+constexpr int KK = BK / 16;       // k16 MFMA steps per stage
+static_assert(BK == 32 || BK == 64, "BK");
+
+template <int BN>
+struct BigCfg {
+  static constexpr int RA = BM / 2;   // activation rows per wave
+  static constexpr int RW = BN / 2;   // weight rows per wave
+  static constexpr int TA = RA / 32;
+  static constexpr int TW = RW / 32;
+  static constexpr int A_ELEMS = BM * BK;
+  static constexpr int B_ELEMS = BN * BK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;          // bf16 elements per stage
+  static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS");
+  static constexpr int A_LOADS = BM * BK / 8 / NTHR;       // 16-byte loads per thread
+  static constexpr int B_LOADS = BN * BK / 8 / NTHR;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+};
+
+// Chunk swizzle: the rows read by one fragment load (32 consecutive rows, one
+// logical chunk) spread over distinct LDS bank groups.
+__device__ __forceinline__ int swz(int r) {
+  return CH == 4 ? ((r >> 2) & 3) : ((r ^ (r >> 3)) & 7);
+}
+// element offset of (row r, logical 16-byte chunk c) in a BK-wide tile
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BN, int EPI>
+__global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slots, int n_tiles) {
+  using C = BigCfg<BN>;
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * C::STAGE];
+
+  int mt, nt;
+  block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
+  if (mt < 0) return;
+  TileInfo ti;
+  if (!tile_info(a, mt, BM, ti)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.K;
+  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+  const size_t wsz = (size_t)a.N * K;
+
+  // Sources of this lane's direct loads.  Slot s of a stage's tile is row
+  // s / CH, physical chunk s % CH, which holds logical chunk (s % CH) ^ swz(row).
+  const __bf16* a_src[C::A_LOADS];
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int s = (wave * C::A_LOADS + j) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ swz(r);
+    const int rr = min(r, ti.nrows - 1);
+    a_src[j] = (const __bf16*)a.A + (size_t)(ti.row0 + rr) * K + c * 8;
+  }
+  const __bf16* b_src[C::B_LOADS];
+#pragma unroll
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int s = (wave * C::B_LOADS + j) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ swz(r);
+    const __bf16* base;
+    int n;
+    if (EPI == EPI_SWIGLU) {  // each wave's RW rows: RW/2 of W1, then the same columns of W3
+      const int half = C::RW / 2;
+      const int w = r / C::RW, rr = r % C::RW;
+      base = (const __bf16*)((rr < half) ? a.B0 : a.B1);
+      n = ncol0 + w * half + (rr % half);
+    } else {
+      base = (const __bf16*)a.B0;
+      n = ncol0 + r;
+    }
+    b_src[j] = base + (size_t)ti.e * wsz + (size_t)n * K + c * 8;
+  }
+
+  const int KT = K / BK;
+  // Stages past the end re-load the last stage into a buffer that is never
+  // read again: every iteration then issues the same loads, the vmcnt waits
+  // are constants and the refill can be scheduled between the MFMAs.
+  auto issue = [&](int kt, int buf) {
+    __bf16* st = lds + buf * C::STAGE;
+    const int k0 = min(kt, KT - 1) * BK;
+#pragma unroll
+    for (int j = 0; j < C::A_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + k0),
+                                       (lds_ptr_t)(st + (wave * C::A_LOADS + j) * 512), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::B_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + k0),
+                                       (lds_ptr_t)(st + C::A_ELEMS + (wave * C::B_LOADS + j) * 512),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[C::TW][C::TA];
+#pragma unroll
+  for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  // Fragments of one k16 step: the wave's weight blocks and activation blocks.
+  struct Frags {
+    bf16x8 w[C::TW], x[C::TA];
+  };
+  auto read_frags = [&](Frags& F, const __bf16* L, int kk) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::TW; ++i)
+      F.w[i] = *(const bf16x8*)(L + C::A_ELEMS + lds_off(wn * C::RW + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+      F.x[j] = *(const bf16x8*)(L + lds_off(wm * C::RA + j * 32 + (lane & 31), c));
+  };
+  auto mfmas = [&](const Frags& F) {
+#pragma unroll
+    for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[i], F.x[j], acc[i][j], 0, 0, 0);
+  };
+  // Interleave the next step's fragment reads with this step's MFMAs; in the
+  // step that also refills a stage, spread the global->LDS loads between the
+  // MFMAs too, so issuing them never leaves the MFMA pipe idle.
+  constexpr int NMF = C::TW * C::TA, NDS = C::TW + C::TA;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / NDS, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
+    }
+  };
+  auto interleave_refill = [&]() {
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * NDS) > 0 ? NMF / (2 * NDS) : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, C::LOADS / NDS > 0 ? C::LOADS / NDS : 1, 0);  // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * NDS) > 0 ? NMF / (2 * NDS) : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // Pipeline: the first STAGES stages are issued up front.  Iteration kt
+  // computes stage kt in KK k16 steps, each overlapping the next step's
+  // fragment reads.  Before its last step it waits for stage kt+1, passes the
+  // barrier (after which every wave holds its stage-kt fragments in
+  // registers), refills stage kt's buffer with stage kt+STAGES and starts
+  // reading stage kt+1.
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue(s, s);
+  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  barrier_only();
+
+  Frags F[2];
+  read_frags(F[0], lds, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const __bf16* L = lds + (kt % STAGES) * C::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+        read_frags(F[(kk + 1) & 1], L, kk + 1);
+        mfmas(F[kk & 1]);
+        interleave();
+      } else {
+        // own loads of stage kt+1 done and this wave's reads of stage kt
+        // retired; the barrier makes both true for every wave
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        wait_vmcnt<(STAGES - 2) * C::LOADS>();
+        barrier_only();
+        issue(kt + STAGES, kt % STAGES);
+        read_frags(F[(kk + 1) & 1], lds + ((kt + 1) % STAGES) * C::STAGE, 0);
+        mfmas(F[kk & 1]);
+        interleave_refill();
+      }
+    }
+  }
+
+  const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
+  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, acc, wm * C::RA, col0, lane);
+}
+
+template <int BN, int EPI>
+hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+  const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
+  const int ncol = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int n_tiles = a.N / ncol;
+  int nb = n_slots * n_tiles;
+  nb = (nb + 7) & ~7;
+  hipLaunchKernelGGL((gemm_big_kernel<BN, EPI>), dim3(nb), dim3(NTHR), 0, s, a, n_slots, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
+  if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU>(a, s);
+  return (a.N % 256 == 0) ? launch_big<256, EPI_STORE>(a, s) : launch_big<128, EPI_STORE>(a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,145 @@
+// Shared pieces of the grouped-GEMM kernels: tile table decoding, XCD-aware
+// block mapping and the MFMA-layout epilogues.
+#pragma once
+
+#include "moe_internal.hpp"
+
+namespace moe {
+
+constexpr int kTableExpertShift = 22;
+constexpr int kTableTileMask = (1 << kTableExpertShift) - 1;
+
+struct TileInfo {
+  int e, row0, nrows;
+};
+
+// m-tile slot -> (expert, first row, rows in the tile); false for empty slots.
+__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti) {
+  if (a.tile_table == nullptr) {
+    ti.e = 0;
+    ti.row0 = mt * BM;
+    ti.nrows = min(BM, a.rows - ti.row0);
+    return ti.nrows > 0;
+  }
+  const int code = a.tile_table[mt];
+  if (code < 0) return false;
+  ti.e = code >> kTableExpertShift;
+  const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
+  ti.row0 = lo + (code & kTableTileMask) * BM;
+  ti.nrows = min(BM, hi - ti.row0);
+  return ti.nrows > 0;
+}
+
+// Number of real m-tiles: the tile table stores it after its n_slots entries.
+__device__ __forceinline__ int real_mtiles(const GemmArgs& a, int BM) {
+  return a.tile_table ? a.tile_table[a.n_slots] : (a.rows + BM - 1) / BM;
+}
+
+// Block -> (m-tile slot, n-tile).  Blocks are dealt round-robin to the 8 XCDs
+// (block b runs on XCD b % 8), so XCD x owns an equal contiguous share of the
+// real tiles; within it tiles go in groups of kGroupM m-slots x all n-tiles
+// (m fastest), so the blocks an XCD runs at once share A and B tiles in its
+// L2.  gridDim.x is a multiple of 8 and covers the upper bound of tiles;
+// blocks beyond the real count exit.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void block_coords(int m_real, int n_tiles, int& mt, int& nt) {
+  const int per_xcd = (gridDim.x >> 3);
+  const int R = m_real * n_tiles;
+  const int share = (R + 7) >> 3;
+  const int i = blockIdx.x >> 3;
+  const int L = (blockIdx.x & 7) * share + i;
+  mt = -1;
+  if (i >= share || L >= R || i >= per_xcd) return;
+  const int g = L / (kGroupM * n_tiles), within = L % (kGroupM * n_tiles);
+  const int gm = min(kGroupM, m_real - g * kGroupM);
+  mt = g * kGroupM + within % gm;
+  nt = within / gm;
+}
+
+// silu(u) = u * sigmoid(u) with the hardware exp2 and reciprocal: relative
+// error ~1e-6, far below the bf16 rounding applied to the result.
+__device__ __forceinline__ float silu(float u) {
+  return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
+}
+
+// Epilogue of a wave's TW x TA grid of 32x32 MFMA blocks computed as
+// (weight rows) x (activation rows).  In block (i, j), lane l holds weight rows
+// g*8 + (l/32)*4 + q (q = 0..3, group g = 0..3) of activation row l % 32, i.e.
+// runs of 4 consecutive output columns.
+//   col0: first output column of this wave's weight rows
+//   SwiGLU: blocks i < TW/2 are W1 (u), blocks i + TW/2 the matching W3 (v).
+template <int TW, int TA, int WDT, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti,
+                                           f32x16 (&acc)[TW][TA], int row_base, int col0,
+                                           int lane) {
+  const int r_in = lane & 31;
+#pragma unroll
+  for (int j = 0; j < TA; ++j) {
+    const int lrow = row_base + j * 32 + r_in;
+    if (lrow >= ti.nrows) continue;
+    const size_t row = (size_t)(ti.row0 + lrow);
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < TW / 2; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float u = acc[i][j][g * 4 + q];
+            float v = acc[i + TW / 2][j][g * 4 + q];
+            if (WDT == GD_FP8) {
+              u *= a.s0[(size_t)ti.e * a.N + n + q];
+              v *= a.s1[(size_t)ti.e * a.N + n + q];
+            }
+            hv[q] = silu(u) * v;
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(hv[0], hv[1]);
+          o[1] = pack_bf16x2(hv[2], hv[3]);
+          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+        }
+      }
+    } else if (EPI == EPI_STORE) {
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+          float yv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            yv[q] = acc[i][j][g * 4 + q];
+            if (WDT == GD_FP8) yv[q] *= a.s0[(size_t)ti.e * a.N + n + q];
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2(yv[0], yv[1]);
+          o[1] = pack_bf16x2(yv[2], yv[3]);
+          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+        }
+      }
+    } else {  // EPI_BIAS_F32: router logits
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (n + q < a.N) {
+              float z = acc[i][j][g * 4 + q];
+              if (a.bias) z += a.bias[n + q];
+              ((float*)a.C)[row * a.N + n + q] = z;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Launchers of the individual kernel families (gemm.hip, gemm_big.hip).
+hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -60,9 +60,14 @@ int gemm_dtype(int moe_dt) {
   return moe_dt == MOE_F32 ? GD_F32 : moe_dt == MOE_BF16 ? GD_BF16 : GD_FP8;
 }
 
+// m-tile height of the routed grouped GEMMs (must match the launch)
 int block_m(const moe_desc* d) {
   GemmArgs g{};
   g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->wdtype);
+  g.rows = int(int64_t(d->T) * d->k);
+  g.E = d->E;
+  g.epi = EPI_SWIGLU;
   return gemm_block_m(g);
 }
 
@@ -113,7 +118,7 @@ DispatchWs carve_dispatch(Carve& c, const moe_desc* d) {
 FfnWs carve_ffn(Carve& c, const moe_desc* d) {
   FfnWs w;
   w.n_slots = gemm_max_slots(int(n_assign(d)), d->E, block_m(d));
-  w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots));
+  w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots + 1));
   return w;
 }
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
@@ -185,6 +190,7 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* o
   GemmArgs g{};
   g.A = x_perm;
   g.rows = int(n_assign(d));
+  g.E = d->E;
   g.tile_table = ws.table;
   g.offsets = offsets;
   g.n_slots = ws.n_slots;
@@ -206,6 +212,7 @@ moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offset
   GemmArgs g{};
   g.A = h;
   g.rows = int(n_assign(d));
+  g.E = d->E;
   g.tile_table = ws.table;
   g.offsets = offsets;
   g.n_slots = ws.n_slots;

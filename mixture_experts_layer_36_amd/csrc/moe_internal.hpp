@@ -92,7 +92,9 @@ enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };
 struct GemmArgs {
   const void* A;               // [rows][K] activations
   int rows;                    // rows of A (all segments)
-  const int32_t* tile_table;   // [n_slots] (expert << 16 | m-tile in expert) or -1; NULL: one segment
+  int E;                       // segments (experts); 0 or 1: one segment
+  const int32_t* tile_table;   // [n_slots + 1]: (expert << 22 | m-tile in expert) or -1, then the
+                               // number of real m-tiles; NULL: one segment
   const int32_t* offsets;      // [E+1] segment starts (NULL: one segment of `rows`)
   int n_slots;                 // m-tile slots in the grid
   const void* B0;              // [E][N][K] weights (gate projection W1 for SwiGLU)
@@ -120,7 +122,7 @@ struct TileTableArgs {
   const int32_t* offsets;  // [E+1]
   int E;
   int bm0, n_slots0;
-  int32_t* table0;         // [n_slots0]
+  int32_t* table0;         // [n_slots0 + 1]
   int bm1, n_slots1;       // bm1 = 0: only one table
   int32_t* table1;
 };

@@ -24,6 +24,9 @@ CASES = {
     "tiny_f32_ragged": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3),
     "mixtral_small": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384),
     "mixtral_tiles": MIXTRAL_PREFILL.scaled(T=700, d=512, f=640),
+    # 256-row direct-to-LDS kernel: ragged tails, K = 3 * 128, N not a multiple of 256
+    "mixtral_big_tiles": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6),
+    "mixtral_big_k128": MIXTRAL_PREFILL.scaled(T=600, d=128, f=128, E=4),
     "dsv3_decode_small": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256),
     "dsv3_skew_small": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128),
     "qwen_fp8_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32),
@@ -113,7 +116,8 @@ def test_stages_chain(name):
     print(f"{name}: h {eh:.3g} y {ey:.3g} combine {ec:.3g}")
 
 
-@pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small"])
+@pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small",
+                                  "mixtral_big_tiles"])
 def test_grouped_ffn_from_oracle_inputs(name):
     """The FFN stage fed the oracle's own x_perm and offsets."""
     w, L, dev, ref = _setup(name)
@@ -157,7 +161,7 @@ def test_shared_expert_and_combine_from_oracle_inputs():
     assert np.max(np.abs(got - ref_out)) <= 2.0 ** -7 * np.max(np.abs(ref_out))
 
 
-@pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small"])
+@pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
