@@ -28,16 +28,9 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_BIG_BK
-#define MOE_BIG_BK 32
-#endif
-#ifndef MOE_BIG_STAGES
-#define MOE_BIG_STAGES 4
-#endif
-constexpr int BM = 256, BK = MOE_BIG_BK, STAGES = MOE_BIG_STAGES, NTHR = 256;
+constexpr int BM = 256, BK = 32, STAGES = 4, NTHR = 256;
 constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
 constexpr int KK = BK / 16;       // k16 MFMA steps per stage
-static_assert(BK == 32 || BK == 64, "BK");
 
 template <int BN>
 struct BigCfg {
@@ -71,9 +64,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Buffer descriptor word 3 for raw 32-bit-format buffers on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int BN, int EPI>
 __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slots, int n_tiles) {
+  // device pass only: the host pass needs just the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
   using C = BigCfg<BN>;
   __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * C::STAGE];
 
@@ -83,57 +80,80 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
   TileInfo ti;
   if (!tile_info(a, mt, BM, ti)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K;
   const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   const size_t wsz = (size_t)a.N * K;
 
-  // Sources of this lane's direct loads.  Slot s of a stage's tile is row
-  // s / CH, physical chunk s % CH, which holds logical chunk (s % CH) ^ swz(row).
-  const __bf16* a_src[C::A_LOADS];
+  // Direct loads go through buffer resources: a block-uniform descriptor
+  // (SGPRs) per operand, a 32-bit per-lane byte offset fixed across stages
+  // and the stage's k offset as the scalar offset, so each load is a single
+  // buffer_load_dwordx4 ... lds with no per-stage address arithmetic.  The
+  // descriptor's size bounds every access to the tile's own rows.  Slot s of
+  // a stage's tile is row s / CH, physical chunk s % CH, which holds logical
+  // chunk (s % CH) ^ swz(row).
+  const int KT = K / BK;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)a.A + (size_t)ti.row0 * K * 2), (short)0, ti.nrows * K * 2, kBufferFlags);
+  uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int s = (wave * C::A_LOADS + j) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
-    a_src[j] = (const __bf16*)a.A + (size_t)(ti.row0 + rr) * K + c * 8;
+    a_off[j] = (uint32_t)(rr * K + c * 8) * 2u;
   }
-  const __bf16* b_src[C::B_LOADS];
+  // B: SwiGLU tiles take each wave's RW rows as RW/2 rows of W1 then the same
+  // columns of W3 (one descriptor each); the 64 slots of one load are 64/CH
+  // consecutive rows inside one half, so the choice is uniform per load.
+  const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const size_t b_start = ((size_t)ti.e * wsz + (size_t)ncol0 * K) * 2;
+  const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)a.B0 + b_start), (short)0, b_rows * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)(EPI == EPI_SWIGLU ? a.B1 : a.B0) + b_start), (short)0, b_rows * K * 2,
+      kBufferFlags);
+  uint32_t b_off[C::B_LOADS];
+  bool b_w3[C::B_LOADS];
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int s = (wave * C::B_LOADS + j) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz(r);
-    const __bf16* base;
-    int n;
-    if (EPI == EPI_SWIGLU) {  // each wave's RW rows: RW/2 of W1, then the same columns of W3
+    int n = r;  // row offset from ncol0
+    b_w3[j] = false;
+    if (EPI == EPI_SWIGLU) {
       const int half = C::RW / 2;
-      const int w = r / C::RW, rr = r % C::RW;
-      base = (const __bf16*)((rr < half) ? a.B0 : a.B1);
-      n = ncol0 + w * half + (rr % half);
-    } else {
-      base = (const __bf16*)a.B0;
-      n = ncol0 + r;
+      const int r0 = (wave * C::B_LOADS + j) * 64 / CH;
+      b_w3[j] = (r0 % C::RW) >= half;
+      n = (r / C::RW) * half + (r % C::RW) % half;
     }
-    b_src[j] = base + (size_t)ti.e * wsz + (size_t)n * K + c * 8;
+    b_off[j] = (uint32_t)(n * K + c * 8) * 2u;
   }
 
-  const int KT = K / BK;
   // Stages past the end re-load the last stage into a buffer that is never
   // read again: every iteration then issues the same loads, the vmcnt waits
   // are constants and the refill can be scheduled between the MFMAs.
-  auto issue = [&](int kt, int buf) {
+  // part 0 = the A loads of a stage, part 1 = its B loads
+  auto issue_part = [&](int kt, int buf, int part) {
     __bf16* st = lds + buf * C::STAGE;
-    const int k0 = min(kt, KT - 1) * BK;
+    const int kb = min(kt, KT - 1) * BK * 2;  // byte offset of the stage's k-slice
+    if (part == 0) {
 #pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + k0),
-                                       (lds_ptr_t)(st + (wave * C::A_LOADS + j) * 512), 16, 0, 0);
+      for (int j = 0; j < C::A_LOADS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_ptr_t)(st + (wave * C::A_LOADS + j) * 512), 16, a_off[j], kb, 0, 0);
+    } else {
 #pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[j] + k0),
-                                       (lds_ptr_t)(st + C::A_ELEMS + (wave * C::B_LOADS + j) * 512),
-                                       16, 0, 0);
+      for (int j = 0; j < C::B_LOADS; ++j) {
+        const lds_ptr_t dst = (lds_ptr_t)(st + C::A_ELEMS + (wave * C::B_LOADS + j) * 512);
+        if (b_w3[j])
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], kb, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], kb, 0, 0);
+      }
+    }
   };
 
   f32x16 acc[C::TW][C::TA];
@@ -179,49 +199,53 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
 #pragma unroll
     for (int i = 0; i < NDS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * NDS) > 0 ? NMF / (2 * NDS) : 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, C::LOADS / NDS > 0 ? C::LOADS / NDS : 1, 0);  // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (a half refill: <= NDS loads)
       __builtin_amdgcn_sched_group_barrier(0x008, NMF / (2 * NDS) > 0 ? NMF / (2 * NDS) : 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
-  // Pipeline: the first STAGES stages are issued up front.  Iteration kt
-  // computes stage kt in KK k16 steps, each overlapping the next step's
-  // fragment reads.  Before its last step it waits for stage kt+1, passes the
-  // barrier (after which every wave holds its stage-kt fragments in
-  // registers), refills stage kt's buffer with stage kt+STAGES and starts
-  // reading stage kt+1.
-#pragma unroll
-  for (int s = 0; s < STAGES; ++s) issue(s, s);
-  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  // Pipeline over a ring of STAGES = 4 buffers, stage kt in buffer kt % 4.
+  // Iteration kt computes stage kt in two k16 steps, each overlapping the
+  // next step's fragment reads.  Between the steps it waits for its own loads
+  // of stage kt+1 and passes the barrier, after which every wave holds its
+  // stage-kt fragments in registers, so buffer kt % 4 is free.  Refills are
+  // split to keep the address unit from bursting: the A half of stage kt+4 is
+  // issued right after that barrier, its B half during step 0 of the next
+  // iteration -- still two iterations before the stage is needed.  Stages
+  // past the end re-load the last k-slice into buffers never read again, so
+  // every wait is a constant.
+  static_assert(STAGES == 4 && KK == 2, "pipeline is laid out for 4 stages of two k16 steps");
+  issue_part(0, 0, 0); issue_part(0, 0, 1);
+  issue_part(1, 1, 0); issue_part(1, 1, 1);
+  issue_part(2, 2, 0); issue_part(2, 2, 1);
+  issue_part(3, 3, 0);
+  wait_vmcnt<2 * C::LOADS + C::A_LOADS>();  // stage 0 done
   barrier_only();
 
   Frags F[2];
   read_frags(F[0], lds, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const __bf16* L = lds + (kt % STAGES) * C::STAGE;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) {
-        read_frags(F[(kk + 1) & 1], L, kk + 1);
-        mfmas(F[kk & 1]);
-        interleave();
-      } else {
-        // own loads of stage kt+1 done and this wave's reads of stage kt
-        // retired; the barrier makes both true for every wave
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        wait_vmcnt<(STAGES - 2) * C::LOADS>();
-        barrier_only();
-        issue(kt + STAGES, kt % STAGES);
-        read_frags(F[(kk + 1) & 1], lds + ((kt + 1) % STAGES) * C::STAGE, 0);
-        mfmas(F[kk & 1]);
-        interleave_refill();
-      }
-    }
+    // step 0: next fragments of this stage, B half of stage kt+3
+    read_frags(F[1], L, 1);
+    issue_part(kt + 3, (kt + 3) % STAGES, 1);
+    mfmas(F[0]);
+    interleave_refill();
+    // step 1: stage kt+1 resident and stage kt retired everywhere, then the
+    // A half of stage kt+4 into buffer kt % 4 and stage kt+1's first fragments
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    wait_vmcnt<2 * C::LOADS>();
+    barrier_only();
+    issue_part(kt + 4, kt % STAGES, 0);
+    read_frags(F[0], lds + ((kt + 1) % STAGES) * C::STAGE, 0);
+    mfmas(F[1]);
+    interleave_refill();
   }
 
   const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
   store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, acc, wm * C::RA, col0, lane);
+#endif
 }
 
 template <int BN, int EPI>
