@@ -196,10 +196,12 @@ def main():
                 "algorithmic_bytes": layer_bytes(w, c)}
     else:
         achieved = flops_gemm1 / gemm1_s / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_mfma_kernel<EPI_SWIGLU> (routed gate-up + SwiGLU)",
+        roof = {"bound": "mfma", "kernel": "routed gate-up GEMM + SwiGLU (gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU)",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops_gemm1,
                 "avg_launch_us": round(gemm1_s * 1e6, 2)}
+    # HBM bytes per launch of that kernel from the committed rocprofv3
+    # FETCH_SIZE / WRITE_SIZE passes, valid only while the kernels are unchanged
     roof["traffic"] = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:

@@ -60,13 +60,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
   block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
   if (mt < 0) return;
   TileInfo ti;
-  if (!tile_info(a, mt, BM, ti)) return;
+  Seg sg;
+  if (!tile_info(a, mt, BM, ti, sg)) return;
+  const int ncol0 = nt * C::NCOL;
+  if (ncol0 >= sg.N) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int K = a.K;
-  const size_t wsz = (size_t)(EPI == EPI_SWIGLU ? a.N : a.N) * K;  // elements per expert matrix
-  const int ncol0 = nt * C::NCOL;
+  const int K = sg.K;
+  // split-K (router logits): this block sums k in [k_begin, k_begin + kspan)
+  const int kspan = K / a.ksplit, k_begin = blockIdx.y * kspan;
 
   // ---- global source pointers of this thread's chunks (k offset added per tile)
   const uint16_t* a_src[C::A_CHUNKS];
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
     const int q = tid + j * C::NTHR;
     const int r = q >> 3, c = q & 7;
     const int rr = min(r, ti.nrows - 1);
-    a_src[j] = (const uint16_t*)a.A + (size_t)(ti.row0 + rr) * K + c * 8;
+    a_src[j] = (const uint16_t*)sg.A + (size_t)(ti.row0 + rr) * K + k_begin + c * 8;
     a_dst[j] = swz(r, c);
   }
   const uint8_t* b_src[C::B_CHUNKS];
@@ -86,19 +89,19 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
     const int q = tid + j * C::NTHR;
     int r, c;  // LDS row, first LDS chunk
     if (WDT == GD_FP8) { r = q >> 2; c = (q & 3) * 2; } else { r = q >> 3; c = q & 7; }
-    const void* base;
+    const char* base;
     int n;
     if (EPI == EPI_SWIGLU) {
       const int half = C::RW / 2;
       const int w = r / C::RW, rr = r % C::RW;
-      base = (rr < half) ? a.B0 : a.B1;
+      base = (rr < half) ? sg.B0 : sg.B1;
       n = ncol0 + w * half + (rr % half);
     } else {
-      base = a.B0;
-      n = min(ncol0 + r, a.N - 1);
+      base = sg.B0;
+      n = min(ncol0 + r, sg.N - 1);
     }
     const int esz = (WDT == GD_FP8) ? 1 : 2;
-    b_src[j] = (const uint8_t*)base + ((size_t)ti.e * wsz + (size_t)n * K + c * 8) * esz;
+    b_src[j] = (const uint8_t*)base + ((size_t)n * K + k_begin + c * 8) * esz;
     b_dst[j] = BM * C::BK + swz(r, c);
   }
 
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  const int KT = K / C::BK;
+  const int KT = kspan / C::BK;
   load(0);
   store(0);
   __syncthreads();
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
   }
 
   const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
-  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, acc, wm * C::RA, col0, lane);
+  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, wm * C::RA, col0, lane);
 }
 
 // ============================================================== fp32 kernel
@@ -191,19 +194,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
   block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
   if (mt < 0) return;
   TileInfo ti;
-  if (!tile_info(a, mt, BM, ti)) return;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int K = a.K;
+  Seg sg;
+  if (!tile_info(a, mt, BM, ti, sg)) return;
   const int ncol0 = nt * NCOL;
-  const float* A = (const float*)a.A;
-  const size_t wsz = (size_t)a.N * K;
+  if (ncol0 >= sg.N) return;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int K = sg.K;
+  const int kspan = K / a.ksplit, k_begin = blockIdx.y * kspan;
+  const float* A = (const float*)sg.A;
 
   int wrow[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) wrow[q] = (EPI == EPI_SWIGLU) ? ((q < 2) ? 2 * tx + q : 32 + 2 * tx + q - 2) : 4 * tx + q;
 
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = k_begin; k0 < k_begin + kspan; k0 += BK) {
     // stage: 64 rows x 16 k for A and B (4 elements per thread each)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -214,13 +219,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
       const float* base;
       int n;
       if (EPI == EPI_SWIGLU) {
-        base = (const float*)((r < 32) ? a.B0 : a.B1);
+        base = (const float*)((r < 32) ? sg.B0 : sg.B1);
         n = ncol0 + (r & 31);
       } else {
-        base = (const float*)a.B0;
-        n = min(ncol0 + r, a.N - 1);
+        base = (const float*)sg.B0;
+        n = min(ncol0 + r, sg.N - 1);
       }
-      Bs[kk][r] = base[(size_t)ti.e * wsz + (size_t)n * K + k0 + kk];
+      Bs[kk][r] = base[(size_t)n * K + k0 + kk];
     }
     __syncthreads();
 #pragma unroll
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
     const int lrow = ty * 4 + i;
     if (lrow >= ti.nrows) continue;
     const size_t row = (size_t)(ti.row0 + lrow);
-    float* Cr = (float*)a.C + row * a.N;
+    float* Cr = (float*)sg.C + ((size_t)blockIdx.y * a.rows + row) * sg.N;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) Cr[ncol0 + 2 * tx + q] = silu(acc[i][q]) * acc[i][q + 2];
@@ -245,7 +250,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = ncol0 + 4 * tx + q;
-        if (n < a.N) Cr[n] = acc[i][q] + ((EPI == EPI_BIAS_F32 && a.bias) ? a.bias[n] : 0.f);
+        const bool bias = EPI == EPI_BIAS_F32 && a.bias && blockIdx.y == 0;
+        if (n < sg.N) Cr[n] = acc[i][q] + (bias ? a.bias[n] : 0.f);
       }
     }
   }
@@ -272,8 +278,10 @@ __global__ __launch_bounds__(512) void tile_table_kernel(TileTableArgs t) {
     int32_t* table = w == 0 ? t.table0 : t.table1;
     const int n_slots = w == 0 ? t.n_slots0 : t.n_slots1;
     for (int i = 0; i < tiles; ++i) table[incl - tiles + i] = (e << kTableExpertShift) | i;
-    for (int s = total + e; s < n_slots; s += 512) table[s] = -1;
-    if (e == 0) table[n_slots] = total;  // real m-tiles, read by every GEMM block
+    const int sh_tiles = (t.sh_rows + bm - 1) / bm;  // the extra segment E, after the experts
+    for (int i = e; i < sh_tiles; i += 512) table[total + i] = (t.E << kTableExpertShift) | i;
+    for (int s = total + sh_tiles + e; s < n_slots; s += 512) table[s] = -1;
+    if (e == 0) table[n_slots] = total + sh_tiles;  // real m-tiles, read by every GEMM block
   }
 }
 
@@ -281,10 +289,11 @@ template <int BM, int BN, int WDT, int EPI>
 hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
   using C = MfmaCfg<BM, BN, WDT, EPI>;
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
-  const int n_tiles = (a.N + C::NCOL - 1) / C::NCOL;
+  const int n_tiles = (gemm_max_cols(a) + C::NCOL - 1) / C::NCOL;
   int nb = n_slots * n_tiles;
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WDT, EPI>), dim3(nb), dim3(C::NTHR), 0, s, a, n_slots, n_tiles);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WDT, EPI>), dim3(nb, a.ksplit), dim3(C::NTHR), 0, s,
+                     a, n_slots, n_tiles);
   return hipGetLastError();
 }
 
@@ -292,10 +301,11 @@ template <int EPI>
 hipError_t launch_f32(const GemmArgs& a, hipStream_t s) {
   const int ncol = (EPI == EPI_SWIGLU) ? 32 : 64;
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + 63) / 64;
-  const int n_tiles = (a.N + ncol - 1) / ncol;
+  const int n_tiles = (gemm_max_cols(a) + ncol - 1) / ncol;
   int nb = n_slots * n_tiles;
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(nb), dim3(256), 0, s, a, n_slots, n_tiles);
+  hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3(nb, a.ksplit), dim3(256), 0, s, a, n_slots,
+                     n_tiles);
   return hipGetLastError();
 }
 
@@ -323,8 +333,8 @@ int gemm_block_m(const GemmArgs& a) {
   return use_big(a) ? 256 : 128;
 }
 
-int gemm_max_slots(int rows, int E, int block_m) {
-  return (rows + block_m - 1) / block_m + E;
+int gemm_max_slots(int rows, int E, int block_m, int sh_rows) {
+  return (rows + block_m - 1) / block_m + E + (sh_rows + block_m - 1) / block_m;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

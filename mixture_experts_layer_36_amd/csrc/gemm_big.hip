@@ -28,14 +28,19 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BK = 32, STAGES = 4, NTHR = 256;
+#ifndef MOE_BIG_WN
+#define MOE_BIG_WN 2
+#endif
+constexpr int BM = 256, BK = 32, STAGES = 4;
 constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
-constexpr int KK = BK / 16;       // k16 MFMA steps per stage
+[[maybe_unused]] constexpr int KK = BK / 16;       // k16 MFMA steps per stage
 
-template <int BN>
+// WN wavefronts along the weight rows, 2 along the activation rows.
+template <int BN, int WN>
 struct BigCfg {
+  static constexpr int NTHR = 128 * WN;
   static constexpr int RA = BM / 2;   // activation rows per wave
-  static constexpr int RW = BN / 2;   // weight rows per wave
+  static constexpr int RW = BN / WN;  // weight rows per wave
   static constexpr int TA = RA / 32;
   static constexpr int TW = RW / 32;
   static constexpr int A_ELEMS = BM * BK;
@@ -53,7 +58,7 @@ __device__ __forceinline__ int swz(int r) {
   return CH == 4 ? ((r >> 2) & 3) : ((r ^ (r >> 3)) & 7);
 }
 // element offset of (row r, logical 16-byte chunk c) in a BK-wide tile
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+[[maybe_unused]] __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
 
 template <int N>
@@ -61,31 +66,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+[[maybe_unused]] __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Buffer descriptor word 3 for raw 32-bit-format buffers on gfx9-family GPUs.
-constexpr int kBufferFlags = 0x00020000;
+[[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
 
-template <int BN, int EPI>
-__global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slots, int n_tiles) {
+template <int BN, int WN, int EPI>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n_slots,
+                                                                          int n_tiles) {
   // device pass only: the host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = BigCfg<BN>;
+  using C = BigCfg<BN, WN>;
   __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * C::STAGE];
 
   int mt, nt;
   block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
   if (mt < 0) return;
   TileInfo ti;
-  if (!tile_info(a, mt, BM, ti)) return;
+  Seg sg;
+  if (!tile_info(a, mt, BM, ti, sg)) return;
+  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+  if (ncol0 >= sg.N) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
-  const int wm = wave >> 1, wn = wave & 1;
-  const int K = a.K;
-  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
-  const size_t wsz = (size_t)a.N * K;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = sg.K;
 
   // Direct loads go through buffer resources: a block-uniform descriptor
   // (SGPRs) per operand, a 32-bit per-lane byte offset fixed across stages
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
   // chunk (s % CH) ^ swz(row).
   const int KT = K / BK;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)a.A + (size_t)ti.row0 * K * 2), (short)0, ti.nrows * K * 2, kBufferFlags);
+      (void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0, ti.nrows * K * 2, kBufferFlags);
   uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
@@ -109,12 +116,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
   // columns of W3 (one descriptor each); the 64 slots of one load are 64/CH
   // consecutive rows inside one half, so the choice is uniform per load.
   const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const size_t b_start = ((size_t)ti.e * wsz + (size_t)ncol0 * K) * 2;
+  const size_t b_start = (size_t)ncol0 * K * 2;
   const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)a.B0 + b_start), (short)0, b_rows * K * 2, kBufferFlags);
+      (void*)(sg.B0 + b_start), (short)0, b_rows * K * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const char*)(EPI == EPI_SWIGLU ? a.B1 : a.B0) + b_start), (short)0, b_rows * K * 2,
-      kBufferFlags);
+      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K * 2, kBufferFlags);
   uint32_t b_off[C::B_LOADS];
   bool b_w3[C::B_LOADS];
 #pragma unroll
@@ -184,17 +190,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
       for (int j = 0; j < C::TA; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[i], F.x[j], acc[i][j], 0, 0, 0);
   };
-  // Interleave the next step's fragment reads with this step's MFMAs; in the
-  // step that also refills a stage, spread the global->LDS loads between the
-  // MFMAs too, so issuing them never leaves the MFMA pipe idle.
+  // Interleave the next step's fragment reads and half a stage refill with
+  // this step's MFMAs, so issuing them never leaves the MFMA pipe idle.
   constexpr int NMF = C::TW * C::TA, NDS = C::TW + C::TA;
-  auto interleave = [&]() {
-#pragma unroll
-    for (int i = 0; i < NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NMF / NDS, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
-    }
-  };
   auto interleave_refill = [&]() {
 #pragma unroll
     for (int i = 0; i < NDS; ++i) {
@@ -244,18 +242,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_big_kernel(GemmArgs a, int n_slo
   }
 
   const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
-  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, acc, wm * C::RA, col0, lane);
+  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, wm * C::RA, col0, lane);
 #endif
 }
 
-template <int BN, int EPI>
+template <int BN, int EPI, int WN = MOE_BIG_WN>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
   const int ncol = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int n_tiles = a.N / ncol;
+  const int n_tiles = gemm_max_cols(a) / ncol;
   int nb = n_slots * n_tiles;
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, EPI>), dim3(nb), dim3(NTHR), 0, s, a, n_slots, n_tiles);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI>), dim3(nb), dim3(BigCfg<BN, WN>::NTHR), 0, s, a,
+                     n_slots, n_tiles);
   return hipGetLastError();
 }
 

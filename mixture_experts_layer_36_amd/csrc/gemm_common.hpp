@@ -6,27 +6,68 @@
 
 namespace moe {
 
-constexpr int kTableExpertShift = 22;
+constexpr int kTableExpertShift = 21;
 constexpr int kTableTileMask = (1 << kTableExpertShift) - 1;
 
 struct TileInfo {
   int e, row0, nrows;
 };
 
-// m-tile slot -> (expert, first row, rows in the tile); false for empty slots.
-__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti) {
+// Operands of the segment a tile belongs to.
+struct Seg {
+  const char* A;            // activation rows of the segment's buffer (row 0 = buffer row 0)
+  const char* B0;           // this expert's weight matrices
+  const char* B1;
+  const float* s0;          // this expert's per-channel scales (fp8) or NULL
+  const float* s1;
+  char* C;
+  int N, K;
+};
+
+__device__ __forceinline__ int dtype_bytes(int dt) { return dt == GD_F32 ? 4 : dt == GD_BF16 ? 2 : 1; }
+
+// m-tile slot -> (segment, first row, rows in the tile) and its operands;
+// false for empty slots.
+__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti, Seg& sg) {
+  int tile;
   if (a.tile_table == nullptr) {
     ti.e = 0;
-    ti.row0 = mt * BM;
-    ti.nrows = min(BM, a.rows - ti.row0);
+    tile = mt;
+  } else {
+    const int code = a.tile_table[mt];
+    if (code < 0) return false;
+    ti.e = code >> kTableExpertShift;
+    tile = code & kTableTileMask;
+  }
+  if (a.tile_table != nullptr && ti.e == a.E) {  // the extra (shared) segment
+    ti.row0 = tile * BM;
+    ti.nrows = min(BM, a.sh_rows - ti.row0);
+    sg.A = (const char*)a.shA;
+    sg.B0 = (const char*)a.shB0;
+    sg.B1 = (const char*)a.shB1;
+    sg.s0 = sg.s1 = nullptr;
+    sg.C = (char*)a.shC;
+    sg.N = a.shN;
+    sg.K = a.shK;
     return ti.nrows > 0;
   }
-  const int code = a.tile_table[mt];
-  if (code < 0) return false;
-  ti.e = code >> kTableExpertShift;
-  const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
-  ti.row0 = lo + (code & kTableTileMask) * BM;
-  ti.nrows = min(BM, hi - ti.row0);
+  if (a.tile_table == nullptr) {
+    ti.row0 = tile * BM;
+    ti.nrows = min(BM, a.rows - ti.row0);
+  } else {
+    const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
+    ti.row0 = lo + tile * BM;
+    ti.nrows = min(BM, hi - ti.row0);
+  }
+  const size_t woff = (size_t)ti.e * a.N * a.K * dtype_bytes(a.wdt);
+  sg.A = (const char*)a.A;
+  sg.B0 = (const char*)a.B0 + woff;
+  sg.B1 = a.B1 ? (const char*)a.B1 + woff : nullptr;
+  sg.s0 = a.s0 ? a.s0 + (size_t)ti.e * a.N : nullptr;
+  sg.s1 = a.s1 ? a.s1 + (size_t)ti.e * a.N : nullptr;
+  sg.C = (char*)a.C;
+  sg.N = a.N;
+  sg.K = a.K;
   return ti.nrows > 0;
 }
 
@@ -69,7 +110,7 @@ __device__ __forceinline__ float silu(float u) {
 //   col0: first output column of this wave's weight rows
 //   SwiGLU: blocks i < TW/2 are W1 (u), blocks i + TW/2 the matching W3 (v).
 template <int TW, int TA, int WDT, int EPI>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti,
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
                                            f32x16 (&acc)[TW][TA], int row_base, int col0,
                                            int lane) {
   const int r_in = lane & 31;
@@ -89,16 +130,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
           for (int q = 0; q < 4; ++q) {
             float u = acc[i][j][g * 4 + q];
             float v = acc[i + TW / 2][j][g * 4 + q];
-            if (WDT == GD_FP8) {
-              u *= a.s0[(size_t)ti.e * a.N + n + q];
-              v *= a.s1[(size_t)ti.e * a.N + n + q];
+            if (WDT == GD_FP8 && sg.s0) {
+              u *= sg.s0[n + q];
+              v *= sg.s1[n + q];
             }
             hv[q] = silu(u) * v;
           }
           u32x2 o;
           o[0] = pack_bf16x2(hv[0], hv[1]);
           o[1] = pack_bf16x2(hv[2], hv[3]);
-          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+          *(u32x2*)((uint16_t*)sg.C + row * sg.N + n) = o;
         }
       }
     } else if (EPI == EPI_STORE) {
@@ -111,15 +152,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             yv[q] = acc[i][j][g * 4 + q];
-            if (WDT == GD_FP8) yv[q] *= a.s0[(size_t)ti.e * a.N + n + q];
+            if (WDT == GD_FP8 && sg.s0) yv[q] *= sg.s0[n + q];
           }
           u32x2 o;
           o[0] = pack_bf16x2(yv[0], yv[1]);
           o[1] = pack_bf16x2(yv[2], yv[3]);
-          *(u32x2*)((uint16_t*)a.C + row * a.N + n) = o;
+          *(u32x2*)((uint16_t*)sg.C + row * sg.N + n) = o;
         }
       }
-    } else {  // EPI_BIAS_F32: router logits
+    } else {  // EPI_BIAS_F32: router logits (partial sums of one K range)
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
 #pragma unroll
@@ -127,10 +168,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
           const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (n + q < a.N) {
+            if (n + q < sg.N) {
               float z = acc[i][j][g * 4 + q];
-              if (a.bias) z += a.bias[n + q];
-              ((float*)a.C)[row * a.N + n + q] = z;
+              if (a.bias && blockIdx.y == 0) z += a.bias[n + q];
+              ((float*)sg.C)[((size_t)blockIdx.y * a.rows + row) * sg.N + n + q] = z;
             }
           }
         }
@@ -138,6 +179,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
     }
   }
 }
+
+// Widest output among the segments of a launch.
+inline int gemm_max_cols(const GemmArgs& a) { return (a.sh_rows > 0 && a.shN > a.N) ? a.shN : a.N; }
 
 // Launchers of the individual kernel families (gemm.hip, gemm_big.hip).
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "moe_internal.hpp"
 
 using namespace moe;
@@ -85,8 +87,26 @@ struct Carve {
 };
 
 struct RouteWs {
-  float* z;
+  float* z;    // [ksplit][T][E] partial logits
+  int ksplit;
 };
+
+// Split-K factor of the router GEMM: enough blocks to fill the GPU when T*E
+// is small (decode, few experts), bounded so the fp32 partial sums stay small
+// next to the inputs.  K / ksplit stays a multiple of the 64-wide k step.
+int route_splits(const moe_desc* d) {
+  if (d->act == MOE_F32) return 1;
+  const int64_t tiles = int64_t((d->T + 127) / 128) * ((d->E + 127) / 128);
+  const int64_t kmax = d->d / 64;
+  const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
+  const int64_t part_bytes = int64_t(d->T) * d->E * 4;
+  int64_t want = (1024 + tiles - 1) / tiles;
+  want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
+  int s = 1;
+  for (int64_t c = 1; c <= std::min(want, kmax); ++c)
+    if (kmax % c == 0) s = int(c);
+  return s;
+}
 struct DispatchWs {
   int32_t* chunk_cnt;
 };
@@ -109,15 +129,20 @@ struct LayerWs {
 };
 
 RouteWs carve_route(Carve& c, const moe_desc* d) {
-  return RouteWs{c.take<float>(sizeof(float) * size_t(d->T) * d->E)};
+  const int ks = route_splits(d);
+  return RouteWs{c.take<float>(sizeof(float) * size_t(ks) * d->T * d->E), ks};
 }
 DispatchWs carve_dispatch(Carve& c, const moe_desc* d) {
   const int64_t chunks = (n_assign(d) + kDispatchChunk - 1) / kDispatchChunk;
   return DispatchWs{c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E)};
 }
-FfnWs carve_ffn(Carve& c, const moe_desc* d) {
+// The shared expert joins the routed grouped GEMMs as one more segment when
+// its weights have the routed weights' dtype.
+bool fuse_shared(const moe_desc* d) { return d->f_shared > 0 && d->wdtype == d->act; }
+
+FfnWs carve_ffn(Carve& c, const moe_desc* d, bool with_shared) {
   FfnWs w;
-  w.n_slots = gemm_max_slots(int(n_assign(d)), d->E, block_m(d));
+  w.n_slots = gemm_max_slots(int(n_assign(d)), d->E, block_m(d), with_shared ? d->T : 0);
   w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots + 1));
   return w;
 }
@@ -126,7 +151,7 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   const size_t A = n_assign(d), ab = act_bytes(d);
   w.route = carve_route(c, d);
   w.disp = carve_dispatch(c, d);
-  w.ffn = carve_ffn(c, d);
+  w.ffn = carve_ffn(c, d, fuse_shared(d));
   w.perm_token = c.take<int32_t>(sizeof(int32_t) * A);
   w.inv_pos = c.take<int32_t>(sizeof(int32_t) * A);
   w.offsets = c.take<int32_t>(sizeof(int32_t) * (d->E + 1));
@@ -143,7 +168,7 @@ size_t stage_bytes(const moe_desc* d, moe_stage stage) {
   switch (stage) {
     case MOE_STAGE_ROUTE: carve_route(c, d); break;
     case MOE_STAGE_DISPATCH: carve_dispatch(c, d); break;
-    case MOE_STAGE_FFN: carve_ffn(c, d); break;
+    case MOE_STAGE_FFN: carve_ffn(c, d, false); break;
     default: carve_layer(c, d); break;
   }
   return c.used;
@@ -171,8 +196,10 @@ moe_status run_route(const moe_desc* d, const void* x, const void* wr, const flo
   g.act = gemm_dtype(d->act);
   g.wdt = gemm_dtype(d->act);
   g.epi = EPI_BIAS_F32;
+  g.ksplit = ws.ksplit;
   MOE_TRY(dev(launch_gemm(g, s)));
-  RouteSelectArgs r{ws.z, d->T, d->E, d->k, d->score, d->renorm, d->n_group, d->topk_group, idx, w};
+  RouteSelectArgs r{ws.z, ws.ksplit, d->T, d->E, d->k, d->score, d->renorm, d->n_group, d->topk_group,
+                    idx, w};
   return dev(launch_route_select(r, s));
 }
 
@@ -184,10 +211,30 @@ moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, in
   return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), int(d->d * act_bytes(d)), x_perm, s));
 }
 
+// Optional shared-expert segment of the routed launches (see fuse_shared).
+struct SharedSeg {
+  const void* x = nullptr;  // GEMM1 input: the tokens in order
+  const void* w1 = nullptr;
+  const void* w3 = nullptr;
+  const void* w2 = nullptr;
+  void* h = nullptr;        // GEMM1 output / GEMM2 input
+  void* y = nullptr;        // GEMM2 output
+};
+
 moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* offsets,
                          const void* w1, const void* w3, const float* s1, const float* s3, void* h,
-                         const FfnWs& ws, hipStream_t s) {
+                         const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr) {
   GemmArgs g{};
+  g.ksplit = 1;
+  if (sh) {
+    g.sh_rows = d->T;
+    g.shA = sh->x;
+    g.shB0 = sh->w1;
+    g.shB1 = sh->w3;
+    g.shC = sh->h;
+    g.shN = d->f_shared;
+    g.shK = d->d;
+  }
   g.A = x_perm;
   g.rows = int(n_assign(d));
   g.E = d->E;
@@ -208,8 +255,18 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* o
 }
 
 moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offsets, const void* w2,
-                         const float* s2, void* y, const FfnWs& ws, hipStream_t s) {
+                         const float* s2, void* y, const FfnWs& ws, hipStream_t s,
+                         const SharedSeg* sh = nullptr) {
   GemmArgs g{};
+  g.ksplit = 1;
+  if (sh) {
+    g.sh_rows = d->T;
+    g.shA = sh->h;
+    g.shB0 = sh->w2;
+    g.shC = sh->y;
+    g.shN = d->d;
+    g.shK = d->f_shared;
+  }
   g.A = h;
   g.rows = int(n_assign(d));
   g.E = d->E;
@@ -227,14 +284,17 @@ moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offset
   return dev(launch_gemm(g, s));
 }
 
-moe_status run_tables(const moe_desc* d, const int32_t* offsets, const FfnWs& ws, hipStream_t s) {
-  TileTableArgs t{offsets, d->E, block_m(d), ws.n_slots, ws.table, 0, 0, nullptr};
+moe_status run_tables(const moe_desc* d, const int32_t* offsets, const FfnWs& ws, hipStream_t s,
+                      bool with_shared = false) {
+  TileTableArgs t{offsets, d->E, with_shared ? d->T : 0, block_m(d), ws.n_slots, ws.table, 0, 0,
+                  nullptr};
   return dev(launch_tile_tables(t, s));
 }
 
 moe_status run_shared(const moe_desc* d, const void* x, const void* sw1, const void* sw3,
                       const void* sw2, void* sh, void* sy, hipStream_t s) {
   GemmArgs g{};
+  g.ksplit = 1;
   g.A = x;
   g.rows = d->T;
   g.B0 = sw1;
@@ -247,6 +307,7 @@ moe_status run_shared(const moe_desc* d, const void* x, const void* sw1, const v
   g.epi = EPI_SWIGLU;
   MOE_TRY(dev(launch_gemm(g, s)));
   GemmArgs g2{};
+  g2.ksplit = 1;
   g2.A = sh;
   g2.rows = d->T;
   g2.B0 = sw2;
@@ -335,7 +396,7 @@ moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t*
     return MOE_ERR_INVALID;
   if (ws_bytes < stage_bytes(d, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
   Carve c(ws);
-  const FfnWs w = carve_ffn(c, d);
+  const FfnWs w = carve_ffn(c, d, false);
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(run_tables(d, offsets, w, s));
   MOE_TRY(run_ffn_gemm1(d, x_perm, offsets, w1, w3, s1, s3, h, w, s));
@@ -385,13 +446,23 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(run_route(d, x, w_router, bias, topk_idx, topk_w, w.route, s));
   MOE_TRY(record(trace, 1, s));
   MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos, w.x_perm, w.disp, s));
-  MOE_TRY(run_tables(d, w.offsets, w.ffn, s));
+  const bool fused = fuse_shared(d);
+  SharedSeg sh;
+  if (fused) {
+    sh.x = x;
+    sh.w1 = sw1;
+    sh.w3 = sw3;
+    sh.w2 = sw2;
+    sh.h = w.sh;
+    sh.y = w.sy;
+  }
+  MOE_TRY(run_tables(d, w.offsets, w.ffn, s, fused));
   MOE_TRY(record(trace, 2, s));
-  MOE_TRY(run_ffn_gemm1(d, w.x_perm, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s));
+  MOE_TRY(run_ffn_gemm1(d, w.x_perm, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s, fused ? &sh : nullptr));
   MOE_TRY(record(trace, 3, s));
-  MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s));
+  MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr));
   MOE_TRY(record(trace, 4, s));
-  if (shared) MOE_TRY(run_shared(d, x, sw1, sw3, sw2, w.sh, w.sy, s));
+  if (shared && !fused) MOE_TRY(run_shared(d, x, sw1, sw3, sw2, w.sh, w.sy, s));
   MOE_TRY(record(trace, 5, s));
   CombineArgs a{w.y_perm, w.inv_pos, topk_w, shared ? w.sy : nullptr, out, d->T, d->d, d->k,
                 gemm_dtype(d->act)};

@@ -47,7 +47,8 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b) {
 
 // ------------------------------------------------------------------ launchers
 struct RouteSelectArgs {
-  const float* z;        // [T][E] router logits (bias included)
+  const float* z;        // [ksplit][T][E] partial router logits (bias in part 0)
+  int ksplit;
   int T, E, k, score, renorm, n_group, topk_group;
   int32_t* topk_idx;     // [T][k]
   float* topk_w;         // [T][k]
@@ -91,11 +92,11 @@ enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };
 
 struct GemmArgs {
   const void* A;               // [rows][K] activations
-  int rows;                    // rows of A (all segments)
-  int E;                       // segments (experts); 0 or 1: one segment
-  const int32_t* tile_table;   // [n_slots + 1]: (expert << 22 | m-tile in expert) or -1, then the
-                               // number of real m-tiles; NULL: one segment
-  const int32_t* offsets;      // [E+1] segment starts (NULL: one segment of `rows`)
+  int rows;                    // rows of A (all routed segments)
+  int E;                       // routed segments (experts); 0 or 1: one segment
+  const int32_t* tile_table;   // [n_slots + 1]: (segment << 21 | m-tile in segment) or -1, then
+                               // the number of real m-tiles; NULL: one segment of `rows`
+  const int32_t* offsets;      // [E+1] segment starts (with tile_table)
   int n_slots;                 // m-tile slots in the grid
   const void* B0;              // [E][N][K] weights (gate projection W1 for SwiGLU)
   const void* B1;              // [E][N][K] up projection W3 (SwiGLU only)
@@ -104,23 +105,34 @@ struct GemmArgs {
   const float* bias;           // [N] (EPI_BIAS_F32)
   int N;                       // output columns (h columns for SwiGLU)
   int K;
-  void* C;                     // [rows][N] output
+  void* C;                     // [rows][N] output; EPI_BIAS_F32: [ksplit][rows][N] partial sums
   int act;                     // GemmDtype of A and C (F32 or BF16); EPI_BIAS_F32 stores f32
   int wdt;                     // GemmDtype of B
   int epi;                     // GemmEpilogue
+  int ksplit;                  // EPI_BIAS_F32: K is split into ksplit equal ranges (>= 1)
+  // Optional extra segment E (the shared expert): sh_rows rows of shA in
+  // order, its own weights (wdt == act), output and sizes.
+  int sh_rows;                 // 0: none
+  const void* shA;
+  const void* shB0;
+  const void* shB1;
+  void* shC;
+  int shN, shK;
 };
 
 // Rows per m-tile the grouped GEMM uses for this problem (the tile table must
 // be built with the same value).
 int gemm_block_m(const GemmArgs& a);
-// Upper bound of m-tile slots for `rows` rows in E segments.
-int gemm_max_slots(int rows, int E, int block_m);
+// Upper bound of m-tile slots for `rows` rows in E segments plus an extra
+// segment of sh_rows rows.
+int gemm_max_slots(int rows, int E, int block_m, int sh_rows);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 // Tile tables for up to two tile heights from segment offsets.
 struct TileTableArgs {
   const int32_t* offsets;  // [E+1]
   int E;
+  int sh_rows;             // rows of the extra segment E (0: none)
   int bm0, n_slots0;
   int32_t* table0;         // [n_slots0 + 1]
   int bm1, n_slots1;       // bm1 = 0: only one table

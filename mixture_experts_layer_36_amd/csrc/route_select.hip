@@ -1,7 +1,9 @@
 // Router selection: scores, optional group limit, top-k and gates, one
 // wavefront per token.
 //
-// The logits z = x Wr^T + b come from the grouped-GEMM kernel (EPI_BIAS_F32).
+// The logits z = x Wr^T + b come from the grouped-GEMM kernel (EPI_BIAS_F32)
+// as split-K partial sums, added here in a fixed order so the result is
+// deterministic and identical router rows give identical logits.
 // Following the per-token routing path of "Expert-Parallel MoE Inference:
 // Serving Sparse Models at Scale" (section "Deeper Analysis", first paragraph,
 // Figure 2): scores are softmax over the E logits or the element-wise sigmoid,
@@ -68,13 +70,30 @@ __global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectAr
   const bool live = t < a.T;                 // whole-wave condition
   const int tt = live ? t : a.T - 1;         // dead waves still reach every barrier
   const float* zrow = a.z + (size_t)tt * a.E;
+  const size_t zsplit = (size_t)a.T * a.E;  // stride between split-K partial sums
 
   float z[kMaxV];
   uint64_t key[kMaxV];
 #pragma unroll
   for (int v = 0; v < kMaxV; ++v) {
     const int e = lane + 64 * v;
-    z[v] = (e < a.E) ? zrow[e] : -INFINITY;
+    if (e < a.E) {
+      // sum the partials in split order; loads are issued 8 at a time so
+      // they are in flight together
+      float acc = 0.f;
+      int sp = 0;
+      for (; sp + 8 <= a.ksplit; sp += 8) {
+        float p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = zrow[(size_t)(sp + u) * zsplit + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += p[u];
+      }
+      for (; sp < a.ksplit; ++sp) acc += zrow[(size_t)sp * zsplit + e];
+      z[v] = acc;
+    } else {
+      z[v] = -INFINITY;
+    }
     key[v] = (e < a.E) ? (((uint64_t)ordered_bits(z[v]) << 32) | (uint32_t)(~e)) : 0ull;
   }
 
