@@ -328,6 +328,14 @@ static bool use_big(const GemmArgs& a) {
   return a.rows >= 1024 && a.rows / segs >= 128;
 }
 
+// Decode-shaped grouped bf16 problems (on average at most one 32-row token
+// block per expert) are weight streams: the weight-streaming kernel.
+static bool use_decode(const GemmArgs& a) {
+  if (a.act != GD_BF16 || a.wdt != GD_BF16 || a.epi == EPI_BIAS_F32) return false;
+  if (a.offsets == nullptr || a.E <= 0) return false;
+  return a.rows <= 32 * a.E;
+}
+
 int gemm_block_m(const GemmArgs& a) {
   if (a.act == GD_F32) return 64;
   return use_big(a) ? 256 : 128;
@@ -346,6 +354,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       default: return launch_f32<EPI_BIAS_F32>(a, s);
     }
   }
+  if (use_decode(a)) return launch_gemm_decode(a, s);
   if (use_big(a)) return launch_gemm_big(a, s);
   return a.wdt == GD_FP8 ? launch_mfma_epi<GD_FP8>(a, s) : launch_mfma_epi<GD_BF16>(a, s);
 }

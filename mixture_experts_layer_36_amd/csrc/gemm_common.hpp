@@ -183,7 +183,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
 // Widest output among the segments of a launch.
 inline int gemm_max_cols(const GemmArgs& a) { return (a.sh_rows > 0 && a.shN > a.N) ? a.shN : a.N; }
 
-// Launchers of the individual kernel families (gemm.hip, gemm_big.hip).
+// Launchers of the individual kernel families (gemm.hip, gemm_big.hip,
+// gemm_decode.hip).
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -27,7 +27,12 @@ CASES = {
     # 256-row direct-to-LDS kernel: ragged tails, K = 3 * 128, N not a multiple of 256
     "mixtral_big_tiles": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6),
     "mixtral_big_k128": MIXTRAL_PREFILL.scaled(T=600, d=128, f=128, E=4),
+    # weight-streaming decode kernel (at most 32 rows per expert on average):
+    # shared segment over several 32-row token blocks, K below the pipeline depth,
+    # shared width different from the routed width
     "dsv3_decode_small": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256),
+    "decode_k128": DSV3_DECODE.scaled(T=24, d=128, f=128, E=16, f_shared=128),
+    "decode_shared_wide": DSV3_DECODE.scaled(T=70, d=256, f=128, E=32, f_shared=384),
     "dsv3_skew_small": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128),
     "qwen_fp8_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32),
 }
@@ -117,7 +122,7 @@ def test_stages_chain(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small",
-                                  "mixtral_big_tiles"])
+                                  "mixtral_big_tiles", "dsv3_decode_small"])
 def test_grouped_ffn_from_oracle_inputs(name):
     """The FFN stage fed the oracle's own x_perm and offsets."""
     w, L, dev, ref = _setup(name)
@@ -161,7 +166,8 @@ def test_shared_expert_and_combine_from_oracle_inputs():
     assert np.max(np.abs(got - ref_out)) <= 2.0 ** -7 * np.max(np.abs(ref_out))
 
 
-@pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles"])
+@pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
+                                  "decode_shared_wide"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
