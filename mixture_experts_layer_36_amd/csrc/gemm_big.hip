@@ -17,6 +17,15 @@
 //   * the LDS fragments of the next k16 step are read while the current
 //     step's MFMAs run (two fragment sets, interleaved by
 //     sched_group_barrier), across the stage boundary too;
+//   * an expert's last tile with at most 128 rows runs a half-height layout
+//     (all four wavefronts on the 128 rows, each with half the weight rows),
+//     so a short tail costs half a tile rather than a whole one;
+//   * tiles that remain after the last full wave of tiles (one tile per
+//     compute unit) are split along K into pieces that fill that wave; each
+//     piece stores its raw fp32 accumulators and a fixup kernel adds the
+//     pieces in order and runs the epilogue, so the result is deterministic
+//     (the down projection of a Mixtral-shaped layer has 2.25 waves of
+//     tiles, so without this its last wave would run a quarter full);
 //   * LDS rows of BK elements with 16-byte chunks XOR-swizzled by row
 //     ((r >> 2) & 3 for 64-byte rows, (r ^ (r >> 3)) & 7 for 128-byte rows):
 //     measured on gfx950 (64 banks; a 128-bit read is served 16 lanes at a
@@ -35,22 +44,52 @@ constexpr int BM = 256, BK = 32, STAGES = 4;
 constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
 [[maybe_unused]] constexpr int KK = BK / 16;       // k16 MFMA steps per stage
 
-// WN wavefronts along the weight rows, 2 along the activation rows.
-template <int BN, int WN>
+// Full layout: WN wavefronts along the weight rows, 2 along the 256
+// activation rows, each wave 128 activation rows x RW weight rows.  Half
+// layout (tiles of at most 128 rows): all 2*WN wavefronts on the 128
+// activation rows, each with RW/2 weight rows.  The LDS ring is the same.
+template <int BN, int WN, bool HALF>
 struct BigCfg {
   static constexpr int NTHR = 128 * WN;
-  static constexpr int RA = BM / 2;   // activation rows per wave
-  static constexpr int RW = BN / WN;  // weight rows per wave
-  static constexpr int TA = RA / 32;
-  static constexpr int TW = RW / 32;
+  static constexpr int RW = BN / WN;                 // weight rows per wave column (full layout)
+  static constexpr int TA = 4;                       // 128 activation rows per wave
+  static constexpr int TW = HALF ? RW / 64 : RW / 32;
+  static constexpr int A_ROWS = HALF ? BM / 2 : BM;  // activation rows loaded
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BN * BK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;          // bf16 elements per stage
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;    // bf16 elements per stage
   static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS");
-  static constexpr int A_LOADS = BM * BK / 8 / NTHR;       // 16-byte loads per thread
+  static constexpr int A_LOADS = A_ROWS * BK / 8 / NTHR;  // 16-byte loads per thread
   static constexpr int B_LOADS = BN * BK / 8 / NTHR;
   static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(TW >= 1 && A_LOADS >= 1, "layout");
 };
+
+// LDS weight row of a wave's block i, its first activation row and the first
+// output column of its blocks (relative to the tile's first column).  SwiGLU
+// tiles hold, per wave column of the full layout, RW/2 rows of W1 followed
+// by the same columns of W3, and a wave's blocks i < TW/2 are W1 (u), the
+// blocks i + TW/2 the matching W3 (v).
+template <int BN, int WN, bool HALF, int EPI>
+__device__ __forceinline__ int wave_wrow(int wave, int i) {
+  using C = BigCfg<BN, WN, HALF>;
+  if (!HALF) return (wave % WN) * C::RW + i * 32;
+  if (EPI != EPI_SWIGLU) return wave * (C::RW / 2) + i * 32;
+  const int slab = wave >> 1, sub = wave & 1;
+  return i < C::TW / 2 ? slab * C::RW + sub * (C::RW / 4) + i * 32
+                       : slab * C::RW + C::RW / 2 + sub * (C::RW / 4) + (i - C::TW / 2) * 32;
+}
+template <int BN, int WN, bool HALF>
+__device__ __forceinline__ int wave_arow(int wave) {
+  return HALF ? 0 : (wave / WN) * 128;
+}
+template <int BN, int WN, bool HALF, int EPI>
+__device__ __forceinline__ int wave_col(int wave) {
+  using C = BigCfg<BN, WN, HALF>;
+  if (!HALF) return (wave % WN) * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
+  if (EPI != EPI_SWIGLU) return wave * (C::RW / 2);
+  return (wave >> 1) * (C::RW / 2) + (wave & 1) * (C::RW / 4);
+}
 
 // Chunk swizzle: the rows read by one fragment load (32 consecutive rows, one
 // logical chunk) spread over distinct LDS bank groups.
@@ -68,31 +107,81 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 [[maybe_unused]] __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// Split plan over R real tiles on n_cu compute units: the first `full`
+// tiles run whole; each of the `rem` others is split into `s` K-pieces
+// (s >= 2, each piece >= 8 stages of the kt_plan stages, rem * s <= slots).
+struct SplitPlan {
+  int full, rem, s;
+};
+__device__ __forceinline__ SplitPlan split_plan(int R, int kt_plan, int n_cu, int slots) {
+  SplitPlan p{R, 0, 1};
+  if (slots <= 0 || R <= 0 || n_cu <= 0) return p;
+  const int w = R / n_cu, r = R - w * n_cu;
+  if (r == 0) return p;
+  const int s = min(min(n_cu / r, kt_plan / 8), slots / r);
+  if (s < 2) return p;
+  p.full = w * n_cu;
+  p.rem = r;
+  p.s = s;
+  return p;
+}
+
+// What one block computes: tile (mt, nt), k-stages [k0, k1) of its segment's
+// KT, and the partial slot of a split piece (-1: the whole tile).
+struct Work {
+  int mt, nt, k0num, slot, s;
+};
+// Blocks are dealt round-robin to the 8 XCDs (block b on XCD b % 8).  Whole
+// tiles come first, an equal contiguous share per XCD (grouped order, so the
+// blocks an XCD runs at once share operands in its L2); the split pieces
+// follow, again an equal share per XCD, so they all run in the last wave.
+[[maybe_unused]] __device__ __forceinline__ bool big_work(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu,
+                                         int BMv, Work& w) {
+  const int m_real = real_mtiles(a, BMv);
+  const int R = m_real * n_tiles;
+  const SplitPlan p = split_plan(R, kt_plan, n_cu, a.partial ? a.partial_slots : 0);
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  int L;
+  w.slot = -1;
+  w.k0num = 0;
+  w.s = 1;
+  if (p.rem > 0) {
+    const int f8 = p.full >> 3, Q = p.rem * p.s, q = (Q + 7) >> 3;
+    if (i < f8) {
+      L = x * f8 + i;
+    } else {
+      const int j = i - f8, pi = x * q + j;
+      if (j >= q || pi >= Q) return false;
+      L = p.full + pi / p.s;
+      w.k0num = pi % p.s;
+      w.slot = pi;
+      w.s = p.s;
+    }
+  } else {
+    const int share = (R + 7) >> 3;
+    L = x * share + i;
+    if (i >= share || L >= R) return false;
+  }
+  tile_coords(L, m_real, n_tiles, w.mt, w.nt);
+  return true;
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Buffer descriptor word 3 for raw 32-bit-format buffers on gfx9-family GPUs.
 [[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
 
-template <int BN, int WN, int EPI>
-__global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n_slots,
-                                                                          int n_tiles) {
-  // device pass only: the host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = BigCfg<BN, WN>;
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * C::STAGE];
-
-  int mt, nt;
-  block_coords(real_mtiles(a, BM), n_tiles, mt, nt);
-  if (mt < 0) return;
-  TileInfo ti;
-  Seg sg;
-  if (!tile_info(a, mt, BM, ti, sg)) return;
-  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
-  if (ncol0 >= sg.N) return;
-
+// One tile (or K-piece of a tile) in the full or the half layout.
+template <int BN, int WN, int EPI, bool HALF>
+__device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
+                                         int ncol0, __bf16* lds) {
+  using C = BigCfg<BN, WN, HALF>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
-  const int wm = wave / WN, wn = wave % WN;
   const int K = sg.K;
+  // this block's k-stages of the segment: all, or piece k0num of s
+  const int KT_all = K / BK;
+  const int kt0 = wk.k0num * KT_all / wk.s, kt1 = (wk.k0num + 1) * KT_all / wk.s;
 
   // Direct loads go through buffer resources: a block-uniform descriptor
   // (SGPRs) per operand, a 32-bit per-lane byte offset fixed across stages
@@ -101,7 +190,8 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   // descriptor's size bounds every access to the tile's own rows.  Slot s of
   // a stage's tile is row s / CH, physical chunk s % CH, which holds logical
   // chunk (s % CH) ^ swz(row).
-  const int KT = K / BK;
+  const int KT = kt1 - kt0;
+  const int kbase = kt0 * BK * 2;  // byte offset of the first k-stage
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0, ti.nrows * K * 2, kBufferFlags);
   uint32_t a_off[C::A_LOADS];
@@ -112,10 +202,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
     const int rr = min(r, ti.nrows - 1);
     a_off[j] = (uint32_t)(rr * K + c * 8) * 2u;
   }
-  // B: SwiGLU tiles take each wave's RW rows as RW/2 rows of W1 then the same
-  // columns of W3 (one descriptor each); the 64 slots of one load are 64/CH
-  // consecutive rows inside one half, so the choice is uniform per load.
-  const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  // B: SwiGLU tiles take each wave column's RW rows as RW/2 rows of W1 then
+  // the same columns of W3 (one descriptor each); the 64 slots of one load
+  // are 64/CH consecutive rows inside one half, so the choice is uniform per
+  // load.
+  const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : min(BN, sg.N - ncol0);
   const size_t b_start = (size_t)ncol0 * K * 2;
   const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(sg.B0 + b_start), (short)0, b_rows * K * 2, kBufferFlags);
@@ -144,7 +235,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   // part 0 = the A loads of a stage, part 1 = its B loads
   auto issue_part = [&](int kt, int buf, int part) {
     __bf16* st = lds + buf * C::STAGE;
-    const int kb = min(kt, KT - 1) * BK * 2;  // byte offset of the stage's k-slice
+    const int kb = kbase + min(kt, KT - 1) * BK * 2;  // byte offset of the stage's k-slice
     if (part == 0) {
 #pragma unroll
       for (int j = 0; j < C::A_LOADS; ++j)
@@ -171,6 +262,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   // Fragments of one k16 step: the wave's weight blocks and activation blocks.
+  const int arow = wave_arow<BN, WN, HALF>(wave);
   struct Frags {
     bf16x8 w[C::TW], x[C::TA];
   };
@@ -178,10 +270,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < C::TW; ++i)
-      F.w[i] = *(const bf16x8*)(L + C::A_ELEMS + lds_off(wn * C::RW + i * 32 + (lane & 31), c));
+      F.w[i] = *(const bf16x8*)(L + C::A_ELEMS +
+                                lds_off(wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31), c));
 #pragma unroll
     for (int j = 0; j < C::TA; ++j)
-      F.x[j] = *(const bf16x8*)(L + lds_off(wm * C::RA + j * 32 + (lane & 31), c));
+      F.x[j] = *(const bf16x8*)(L + lds_off(arow + j * 32 + (lane & 31), c));
   };
   auto mfmas = [&](const Frags& F) {
 #pragma unroll
@@ -241,20 +334,134 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
     interleave_refill();
   }
 
-  const int col0 = ncol0 + wn * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
-  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, wm * C::RA, col0, lane);
+  if (wk.slot >= 0) {
+    // a K-piece: raw accumulators to its slot, register-major so that each
+    // 16-byte store of a wave is contiguous
+    float4* P = (float4*)(a.partial + (size_t)wk.slot * (kPartialSlotBytes / 4));
+#pragma unroll
+    for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    return;
+  }
+  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave),
+                                        lane);
+}
+#endif
+
+template <int BN, int WN, int EPI>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n_tiles, int kt_plan,
+                                                                int n_cu) {
+  // device pass only: the host pass needs just the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * BigCfg<BN, WN, false>::STAGE];
+  Work wk;
+  if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
+  TileInfo ti;
+  Seg sg;
+  if (!tile_info(a, wk.mt, BM, ti, sg)) return;
+  const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+  if (ncol0 >= sg.N) return;
+  if (ti.nrows <= BM / 2)
+    big_tile<BN, WN, EPI, true>(a, ti, sg, wk, ncol0, lds);
+  else
+    big_tile<BN, WN, EPI, false>(a, ti, sg, wk, ncol0, lds);
 #endif
 }
 
+
+// Sum of a split tile's K-pieces in piece order, each thread its own
+// accumulator registers (the layout the pieces stored), then the epilogue.
+template <int BN, int WN, int EPI, bool HALF>
+__device__ __forceinline__ void fixup_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
+                                           int first_slot, int s) {
+  using C = BigCfg<BN, WN, HALF>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f32x16 acc[C::TW][C::TA];
+#pragma unroll
+  for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  for (int piece = 0; piece < s; ++piece) {
+    const float4* P = (const float4*)(a.partial + (size_t)(first_slot + piece) * (kPartialSlotBytes / 4));
+#pragma unroll
+    for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = P[((i * C::TA + j) * 4 + q) * C::NTHR + tid];
+          acc[i][j][4 * q] += v.x;
+          acc[i][j][4 * q + 1] += v.y;
+          acc[i][j][4 * q + 2] += v.z;
+          acc[i][j][4 * q + 3] += v.w;
+        }
+  }
+  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, wave_arow<BN, WN, HALF>(wave),
+                                        ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+}
+
+// One block per split tile.
+template <int BN, int WN, int EPI>
+__global__ __launch_bounds__(128 * WN) void gemm_big_fixup_kernel(GemmArgs a, int n_tiles, int kt_plan,
+                                                                  int n_cu) {
+  const int m_real = real_mtiles(a, BM);
+  const SplitPlan p = split_plan(m_real * n_tiles, kt_plan, n_cu, a.partial ? a.partial_slots : 0);
+  if ((int)blockIdx.x >= p.rem) return;
+  int mt, nt;
+  tile_coords(p.full + blockIdx.x, m_real, n_tiles, mt, nt);
+  TileInfo ti;
+  Seg sg;
+  if (!tile_info(a, mt, BM, ti, sg)) return;
+  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+  if (ncol0 >= sg.N) return;
+  if (ti.nrows <= BM / 2)
+    fixup_tile<BN, WN, EPI, true>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+  else
+    fixup_tile<BN, WN, EPI, false>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+}
+
+// Compute units of the current device (the split plan fills one wave of them).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int BN, int EPI, int WN = MOE_BIG_WN>
-hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
+  GemmArgs a = a_in;
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
   const int ncol = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int n_tiles = gemm_max_cols(a) / ncol;
-  int nb = n_slots * n_tiles;
+  const int n_tiles = (gemm_max_cols(a) + ncol - 1) / ncol;
+  const int kt_plan = (a.sh_rows > 0 ? min(a.K, a.shK) : a.K) / BK;
+  int n_cu = device_cus();
+  if (n_cu <= 0 || n_cu % 8 != 0 || a.partial == nullptr) {
+    n_cu = 0;  // no split: every tile runs whole
+    a.partial = nullptr;
+    a.partial_slots = 0;
+  }
+  a.partial_slots = min(a.partial_slots, kPartialSlots);
+  // whole tiles plus at most one wave of pieces, 8 XCD shares rounded up
+  int nb = n_slots * n_tiles + (n_cu > 0 ? n_cu + 8 : 0);
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI>), dim3(nb), dim3(BigCfg<BN, WN>::NTHR), 0, s, a,
-                     n_slots, n_tiles);
+  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI>), dim3(nb), dim3(128 * WN), 0, s, a,
+                     n_tiles, kt_plan, n_cu);
+  if (n_cu > 0)
+    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI>), dim3(n_cu / 2), dim3(128 * WN),
+                       0, s, a, n_tiles, kt_plan, n_cu);
   return hipGetLastError();
 }
 

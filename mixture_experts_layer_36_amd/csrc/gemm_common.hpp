@@ -83,6 +83,13 @@ __device__ __forceinline__ int real_mtiles(const GemmArgs& a, int BM) {
 // L2.  gridDim.x is a multiple of 8 and covers the upper bound of tiles;
 // blocks beyond the real count exit.
 constexpr int kGroupM = 4;
+// Tile L of the grouped order -> (m-tile slot, n-tile).
+__device__ __forceinline__ void tile_coords(int L, int m_real, int n_tiles, int& mt, int& nt) {
+  const int g = L / (kGroupM * n_tiles), within = L % (kGroupM * n_tiles);
+  const int gm = min(kGroupM, m_real - g * kGroupM);
+  mt = g * kGroupM + within % gm;
+  nt = within / gm;
+}
 __device__ __forceinline__ void block_coords(int m_real, int n_tiles, int& mt, int& nt) {
   const int per_xcd = (gridDim.x >> 3);
   const int R = m_real * n_tiles;
@@ -91,10 +98,7 @@ __device__ __forceinline__ void block_coords(int m_real, int n_tiles, int& mt, i
   const int L = (blockIdx.x & 7) * share + i;
   mt = -1;
   if (i >= share || L >= R || i >= per_xcd) return;
-  const int g = L / (kGroupM * n_tiles), within = L % (kGroupM * n_tiles);
-  const int gm = min(kGroupM, m_real - g * kGroupM);
-  mt = g * kGroupM + within % gm;
-  nt = within / gm;
+  tile_coords(L, m_real, n_tiles, mt, nt);
 }
 
 // silu(u) = u * sigmoid(u) with the hardware exp2 and reciprocal: relative

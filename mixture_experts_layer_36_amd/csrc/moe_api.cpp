@@ -113,6 +113,8 @@ struct DispatchWs {
 struct FfnWs {
   int32_t* table;
   int n_slots;
+  float* partial;     // K-split partial sums of the prefill kernel (NULL: not used)
+  int partial_slots;
 };
 struct LayerWs {
   RouteWs route;
@@ -144,6 +146,12 @@ FfnWs carve_ffn(Carve& c, const moe_desc* d, bool with_shared) {
   FfnWs w;
   w.n_slots = gemm_max_slots(int(n_assign(d)), d->E, block_m(d), with_shared ? d->T : 0);
   w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots + 1));
+  w.partial = nullptr;
+  w.partial_slots = 0;
+  if (block_m(d) == 256) {  // the prefill kernel splits its last wave of tiles
+    w.partial = c.take<float>(kPartialSlotBytes * kPartialSlots);
+    w.partial_slots = kPartialSlots;
+  }
   return w;
 }
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
@@ -241,6 +249,8 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* o
   g.tile_table = ws.table;
   g.offsets = offsets;
   g.n_slots = ws.n_slots;
+  g.partial = ws.partial;
+  g.partial_slots = ws.partial_slots;
   g.B0 = w1;
   g.B1 = w3;
   g.s0 = s1;
@@ -273,6 +283,8 @@ moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offset
   g.tile_table = ws.table;
   g.offsets = offsets;
   g.n_slots = ws.n_slots;
+  g.partial = ws.partial;
+  g.partial_slots = ws.partial_slots;
   g.B0 = w2;
   g.s0 = s2;
   g.N = d->d;

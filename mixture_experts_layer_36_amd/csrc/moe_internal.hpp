@@ -118,7 +118,16 @@ struct GemmArgs {
   const void* shB1;
   void* shC;
   int shN, shK;
+  // Prefill kernel only: fp32 slots for the K-split pieces of the tiles left
+  // over after the last full wave of tiles (NULL / 0: never split).
+  float* partial;
+  int partial_slots;
 };
+
+// Bytes of one partial-sum slot (one 256 x 256 tile of fp32 accumulators) and
+// the slots a launch may use (at most one per compute unit).
+constexpr size_t kPartialSlotBytes = 256 * 256 * 4;
+constexpr int kPartialSlots = 256;
 
 // Rows per m-tile the grouped GEMM uses for this problem (the tile table must
 // be built with the same value).

@@ -27,6 +27,9 @@ CASES = {
     # 256-row direct-to-LDS kernel: ragged tails, K = 3 * 128, N not a multiple of 256
     "mixtral_big_tiles": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6),
     "mixtral_big_k128": MIXTRAL_PREFILL.scaled(T=600, d=128, f=128, E=4),
+    # 48 tiles per GEMM on 256 compute units: every tile is split along K (4
+    # pieces in the gate-up GEMM, 2 in the down GEMM) and summed by the fixup
+    "mixtral_big_split": MIXTRAL_PREFILL.scaled(T=1200, d=1024, f=512, E=4),
     # weight-streaming decode kernel (at most 32 rows per expert on average):
     # shared segment over several 32-row token blocks, K below the pipeline depth,
     # shared width different from the routed width
@@ -122,7 +125,7 @@ def test_stages_chain(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small",
-                                  "mixtral_big_tiles", "dsv3_decode_small"])
+                                  "mixtral_big_tiles", "dsv3_decode_small", "mixtral_big_split"])
 def test_grouped_ffn_from_oracle_inputs(name):
     """The FFN stage fed the oracle's own x_perm and offsets."""
     w, L, dev, ref = _setup(name)
@@ -167,7 +170,7 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
-                                  "decode_shared_wide"])
+                                  "decode_shared_wide", "mixtral_big_split"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
