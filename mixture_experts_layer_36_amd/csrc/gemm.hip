@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
     const int q = tid + j * C::NTHR;
     const int r = q >> 3, c = q & 7;
     const int rr = min(r, ti.nrows - 1);
-    a_src[j] = (const uint16_t*)sg.A + (size_t)(ti.row0 + rr) * K + k_begin + c * 8;
+    a_src[j] = (const uint16_t*)sg.A + (size_t)a_row(sg, ti.row0, rr) * K + k_begin + c * 8;
     a_dst[j] = swz(r, c);
   }
   const uint8_t* b_src[C::B_CHUNKS];
@@ -207,6 +207,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
 #pragma unroll
   for (int q = 0; q < 4; ++q) wrow[q] = (EPI == EPI_SWIGLU) ? ((q < 2) ? 2 * tx + q : 32 + 2 * tx + q - 2) : 4 * tx + q;
 
+  size_t arow[4];  // A row (element offset) of each staged row of this thread
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    arow[q] = (size_t)a_row(sg, ti.row0, min((tid + q * 256) >> 4, ti.nrows - 1)) * K;
+
   float acc[4][4] = {};
   for (int k0 = k_begin; k0 < k_begin + kspan; k0 += BK) {
     // stage: 64 rows x 16 k for A and B (4 elements per thread each)
@@ -214,8 +219,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + q * 256;
       const int r = idx >> 4, kk = idx & 15;
-      const int ar = min(r, ti.nrows - 1);
-      As[kk][r] = A[(size_t)(ti.row0 + ar) * K + k0 + kk];
+      As[kk][r] = A[arow[q] + k0 + kk];
       const float* base;
       int n;
       if (EPI == EPI_SWIGLU) {

@@ -192,15 +192,20 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // chunk (s % CH) ^ swz(row).
   const int KT = kt1 - kt0;
   const int kbase = kt0 * BK * 2;  // byte offset of the first k-stage
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0, ti.nrows * K * 2, kBufferFlags);
+  // With a row map (fused dispatch gather) the descriptor spans all of A and
+  // each lane's offset starts at its row's A row.
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K * 2, kBufferFlags)
+              : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0,
+                                                  ti.nrows * K * 2, kBufferFlags);
   uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int s = (wave * C::A_LOADS + j) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
-    a_off[j] = (uint32_t)(rr * K + c * 8) * 2u;
+    const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
+    a_off[j] = (uint32_t)(ar * K + c * 8) * 2u;
   }
   // B: SwiGLU tiles take each wave column's RW rows as RW/2 rows of W1 then
   // the same columns of W3 (one descriptor each); the 64 slots of one load

@@ -22,7 +22,13 @@ struct Seg {
   const float* s1;
   char* C;
   int N, K;
+  const int32_t* amap;      // routed rows through the row map (NULL: rows in order)
 };
+
+// A row of segment row `r` (tile-relative row r of a tile starting at row0).
+__device__ __forceinline__ int a_row(const Seg& sg, int row0, int r) {
+  return sg.amap ? sg.amap[row0 + r] : row0 + r;
+}
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == GD_F32 ? 4 : dt == GD_BF16 ? 2 : 1; }
 
@@ -49,6 +55,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.C = (char*)a.shC;
     sg.N = a.shN;
     sg.K = a.shK;
+    sg.amap = nullptr;
     return ti.nrows > 0;
   }
   if (a.tile_table == nullptr) {
@@ -68,6 +75,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.C = (char*)a.C;
   sg.N = a.N;
   sg.K = a.K;
+  sg.amap = a.a_map;
   return ti.nrows > 0;
 }
 

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
   // segment operands
   const bool shared = seg == a.E;
   int row0, nrows;
+  const int32_t* amap = nullptr;  // routed rows through the row map (fused dispatch gather)
   const char *A, *B0, *B1;
   char* Cp;
   int N, K;
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
     nrows = a.offsets[seg + 1] - row0;
     const size_t woff = (size_t)seg * a.N * a.K * 2;
     A = (const char*)a.A;
+    amap = a.a_map;
     B0 = (const char*)a.B0 + woff;
     B1 = a.B1 ? (const char*)a.B1 + woff : nullptr;
     Cp = (char*)a.C;
@@ -118,13 +120,16 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
   f32x16 acc;
   for (int tb0 = 0; tb0 < nrows; tb0 += TB) {
     const int tb_rows = min(TB, nrows - tb0);
+    // rows past the block's end read as zero: offset beyond the descriptor
+    const uint32_t t_bytes = (uint32_t)(amap ? a.a_map_rows : tb_rows) * K * 2;
     const __amdgpu_buffer_rsrc_t tok = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + (size_t)(row0 + tb0) * K * 2), (short)0, tb_rows * K * 2, kBufferFlags);
+        (void*)(amap ? A : A + (size_t)(row0 + tb0) * K * 2), (short)0, t_bytes, kBufferFlags);
     uint32_t t_off[T_LOADS];
 #pragma unroll
     for (int j = 0; j < T_LOADS; ++j) {
       const int r = tr + 8 * j, c = tc ^ dswz(r);
-      t_off[j] = (uint32_t)(r * K + c * 8) * 2u;
+      const int ar = amap ? (r < tb_rows ? amap[row0 + tb0 + r] : -1) : r;
+      t_off[j] = ar < 0 ? t_bytes : (uint32_t)(ar * K + c * 8) * 2u;
     }
     auto issue = [&](int kt, int buf) {
       __bf16* st = lds + buf * STAGE;

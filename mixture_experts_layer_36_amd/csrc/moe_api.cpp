@@ -154,6 +154,13 @@ FfnWs carve_ffn(Carve& c, const moe_desc* d, bool with_shared) {
   }
   return w;
 }
+
+// The layer reads GEMM1's activation rows straight from x through perm_token
+// (x_perm is never written) when every row offset of x fits the kernels'
+// 32-bit buffer offsets.
+bool fuse_gather(const moe_desc* d) {
+  return size_t(d->T) * size_t(d->d) * act_bytes(d) < (size_t(1) << 31);
+}
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
   LayerWs w;
   const size_t A = n_assign(d), ab = act_bytes(d);
@@ -163,7 +170,7 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   w.perm_token = c.take<int32_t>(sizeof(int32_t) * A);
   w.inv_pos = c.take<int32_t>(sizeof(int32_t) * A);
   w.offsets = c.take<int32_t>(sizeof(int32_t) * (d->E + 1));
-  w.x_perm = c.take<char>(A * d->d * ab);
+  w.x_perm = fuse_gather(d) ? nullptr : c.take<char>(A * d->d * ab);
   w.h = c.take<char>(A * d->f * ab);
   w.y_perm = c.take<char>(A * d->d * ab);
   w.sh = d->f_shared ? c.take<char>(size_t(d->T) * d->f_shared * ab) : nullptr;
@@ -216,6 +223,7 @@ moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, in
                         const DispatchWs& ws, hipStream_t s) {
   DispatchArgs a{idx, int(n_assign(d)), d->E, d->k, ws.chunk_cnt, counts, offsets, perm_token, inv_pos};
   MOE_TRY(dev(launch_dispatch_index(a, s)));
+  if (x_perm == nullptr) return MOE_OK;  // fused gather: GEMM1 reads x through perm_token
   return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), int(d->d * act_bytes(d)), x_perm, s));
 }
 
@@ -229,7 +237,8 @@ struct SharedSeg {
   void* y = nullptr;        // GEMM2 output
 };
 
-moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* offsets,
+// a_map: NULL (A = x_perm) or perm_token (A = x, the fused dispatch gather).
+moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map, const int32_t* offsets,
                          const void* w1, const void* w3, const float* s1, const float* s3, void* h,
                          const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr) {
   GemmArgs g{};
@@ -243,7 +252,9 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* x_perm, const int32_t* o
     g.shN = d->f_shared;
     g.shK = d->d;
   }
-  g.A = x_perm;
+  g.A = A;
+  g.a_map = a_map;
+  g.a_map_rows = a_map ? d->T : 0;
   g.rows = int(n_assign(d));
   g.E = d->E;
   g.tile_table = ws.table;
@@ -411,7 +422,7 @@ moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t*
   const FfnWs w = carve_ffn(c, d, false);
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(run_tables(d, offsets, w, s));
-  MOE_TRY(run_ffn_gemm1(d, x_perm, offsets, w1, w3, s1, s3, h, w, s));
+  MOE_TRY(run_ffn_gemm1(d, x_perm, nullptr, offsets, w1, w3, s1, s3, h, w, s));
   return run_ffn_gemm2(d, h, offsets, w2, s2, y_perm, w, s);
 }
 
@@ -470,7 +481,9 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   }
   MOE_TRY(run_tables(d, w.offsets, w.ffn, s, fused));
   MOE_TRY(record(trace, 2, s));
-  MOE_TRY(run_ffn_gemm1(d, w.x_perm, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s, fused ? &sh : nullptr));
+  const bool fg = w.x_perm == nullptr;  // fused gather
+  MOE_TRY(run_ffn_gemm1(d, fg ? x : w.x_perm, fg ? w.perm_token : nullptr, w.offsets, w1, w3, s1, s3, w.h,
+                        w.ffn, s, fused ? &sh : nullptr));
   MOE_TRY(record(trace, 3, s));
   MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr));
   MOE_TRY(record(trace, 4, s));

@@ -91,8 +91,12 @@ enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_BIAS_F32 = 2 };
 enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };
 
 struct GemmArgs {
-  const void* A;               // [rows][K] activations
-  int rows;                    // rows of A (all routed segments)
+  const void* A;               // [rows][K] activations (a_map: [a_map_rows][K])
+  int rows;                    // rows of the routed segments
+  // Optional row map of the routed segments: buffer row p reads A row
+  // a_map[p] (the fused dispatch gather: A = x, a_map = perm_token).
+  const int32_t* a_map;
+  int a_map_rows;              // rows of A when a_map is set
   int E;                       // routed segments (experts); 0 or 1: one segment
   const int32_t* tile_table;   // [n_slots + 1]: (segment << 21 | m-tile in segment) or -1, then
                                // the number of real m-tiles; NULL: one segment of `rows`
