@@ -55,15 +55,44 @@ struct BigCfg {
   static constexpr int TA = 4;                       // 128 activation rows per wave
   static constexpr int TW = HALF ? RW / 64 : RW / 32;
   static constexpr int A_ROWS = HALF ? BM / 2 : BM;  // activation rows loaded
-  static constexpr int A_ELEMS = BM * BK;
-  static constexpr int B_ELEMS = BN * BK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;    // bf16 elements per stage
-  static_assert(STAGES * STAGE * 2 <= 160 * 1024, "LDS");
-  static constexpr int A_LOADS = A_ROWS * BK / 8 / NTHR;  // 16-byte loads per thread
-  static constexpr int B_LOADS = BN * BK / 8 / NTHR;
-  static constexpr int LOADS = A_LOADS + B_LOADS;
-  static_assert(TW >= 1 && A_LOADS >= 1, "layout");
+  static_assert(TW >= 1, "layout");
 };
+
+// Stage bytes and 16-byte loads per thread.  bf16 weight rows are BK * 2 = 64
+// bytes (4 chunks); fp8 (E4M3) rows are 32 bytes (2 chunks), half the traffic.
+template <int BN, int WN, bool HALF, int WDT>
+struct BigMem {
+  static constexpr int NTHR = 128 * WN;
+  static constexpr int WB = (WDT == GD_FP8) ? 1 : 2;  // weight bytes per element
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * WB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
+  static constexpr int A_LOADS = BigCfg<BN, WN, HALF>::A_ROWS * BK * 2 / 16 / NTHR;
+  static constexpr int B_LOADS = B_BYTES / 16 / NTHR;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "layout");
+};
+
+// fp8 weight rows in LDS: 32 bytes = two 16-byte chunks, chunk c of row r at
+// c ^ ((r >> 3) & 1), so the 16 rows one 128-bit read pass serves cover all
+// 64 banks once.
+[[maybe_unused]] __device__ __forceinline__ int f8_off(int r, int c) { return r * 32 + ((c ^ ((r >> 3) & 1)) << 4); }
+
+// Eight OCP E4M3 codes -> eight bf16, exactly (every E4M3 value is a bf16
+// value): the hardware conversion to f32, then the upper halves.
+[[maybe_unused]] __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  u32x4 o;
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  o[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  o[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+  o[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+  return __builtin_bit_cast(bf16x8, o);
+}
 
 // LDS weight row of a wave's block i, its first activation row and the first
 // output column of its blocks (relative to the tile's first column).  SwiGLU
@@ -172,10 +201,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // One tile (or K-piece of a tile) in the full or the half layout.
-template <int BN, int WN, int EPI, bool HALF>
+template <int BN, int WN, int EPI, bool HALF, int WDT>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
-                                         int ncol0, __bf16* lds) {
+                                         int ncol0, char* lds) {
   using C = BigCfg<BN, WN, HALF>;
+  using M = BigMem<BN, WN, HALF, WDT>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int K = sg.K;
@@ -191,17 +221,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // a stage's tile is row s / CH, physical chunk s % CH, which holds logical
   // chunk (s % CH) ^ swz(row).
   const int KT = kt1 - kt0;
-  const int kbase = kt0 * BK * 2;  // byte offset of the first k-stage
   // With a row map (fused dispatch gather) the descriptor spans all of A and
   // each lane's offset starts at its row's A row.
   const __amdgpu_buffer_rsrc_t a_rsrc =
       sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K * 2, kBufferFlags)
               : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0,
                                                   ti.nrows * K * 2, kBufferFlags);
-  uint32_t a_off[C::A_LOADS];
+  uint32_t a_off[M::A_LOADS];
 #pragma unroll
-  for (int j = 0; j < C::A_LOADS; ++j) {
-    const int s = (wave * C::A_LOADS + j) * 64 + lane;
+  for (int j = 0; j < M::A_LOADS; ++j) {
+    const int s = (wave * M::A_LOADS + j) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
     const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
@@ -212,26 +241,28 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // are 64/CH consecutive rows inside one half, so the choice is uniform per
   // load.
   const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : min(BN, sg.N - ncol0);
-  const size_t b_start = (size_t)ncol0 * K * 2;
+  const size_t b_start = (size_t)ncol0 * K * M::WB;
   const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sg.B0 + b_start), (short)0, b_rows * K * 2, kBufferFlags);
+      (void*)(sg.B0 + b_start), (short)0, b_rows * K * M::WB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K * 2, kBufferFlags);
-  uint32_t b_off[C::B_LOADS];
-  bool b_w3[C::B_LOADS];
+      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K * M::WB, kBufferFlags);
+  constexpr int BCH = BK * M::WB / 16;  // 16-byte chunks per weight row
+  uint32_t b_off[M::B_LOADS];
+  bool b_w3[M::B_LOADS];
 #pragma unroll
-  for (int j = 0; j < C::B_LOADS; ++j) {
-    const int s = (wave * C::B_LOADS + j) * 64 + lane;
-    const int r = s / CH, c = (s % CH) ^ swz(r);
+  for (int j = 0; j < M::B_LOADS; ++j) {
+    const int s = (wave * M::B_LOADS + j) * 64 + lane;
+    const int r = s / BCH;
+    const int c = (WDT == GD_FP8) ? ((s % BCH) ^ ((r >> 3) & 1)) : ((s % BCH) ^ swz(r));
     int n = r;  // row offset from ncol0
     b_w3[j] = false;
     if (EPI == EPI_SWIGLU) {
       const int half = C::RW / 2;
-      const int r0 = (wave * C::B_LOADS + j) * 64 / CH;
+      const int r0 = (wave * M::B_LOADS + j) * 64 / BCH;
       b_w3[j] = (r0 % C::RW) >= half;
       n = (r / C::RW) * half + (r % C::RW) % half;
     }
-    b_off[j] = (uint32_t)(n * K + c * 8) * 2u;
+    b_off[j] = (uint32_t)(n * K * M::WB + c * 16);
   }
 
   // Stages past the end re-load the last stage into a buffer that is never
@@ -239,21 +270,21 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // are constants and the refill can be scheduled between the MFMAs.
   // part 0 = the A loads of a stage, part 1 = its B loads
   auto issue_part = [&](int kt, int buf, int part) {
-    __bf16* st = lds + buf * C::STAGE;
-    const int kb = kbase + min(kt, KT - 1) * BK * 2;  // byte offset of the stage's k-slice
+    char* st = lds + buf * M::STAGE_BYTES;
+    const int ks = kt0 + min(kt, KT - 1);  // the stage's k-slice
     if (part == 0) {
 #pragma unroll
-      for (int j = 0; j < C::A_LOADS; ++j)
+      for (int j = 0; j < M::A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            a_rsrc, (lds_ptr_t)(st + (wave * C::A_LOADS + j) * 512), 16, a_off[j], kb, 0, 0);
+            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * BK * 2, 0, 0);
     } else {
 #pragma unroll
-      for (int j = 0; j < C::B_LOADS; ++j) {
-        const lds_ptr_t dst = (lds_ptr_t)(st + C::A_ELEMS + (wave * C::B_LOADS + j) * 512);
+      for (int j = 0; j < M::B_LOADS; ++j) {
+        const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
         if (b_w3[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], kb, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * BK * M::WB, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], kb, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * BK * M::WB, 0, 0);
       }
     }
   };
@@ -271,15 +302,28 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   struct Frags {
     bf16x8 w[C::TW], x[C::TA];
   };
-  auto read_frags = [&](Frags& F, const __bf16* L, int kk) {
-    const int c = kk * 2 + (lane >> 5);
+  // A k16 step's k values for lane half h = lane / 32: bf16 weights use the
+  // MFMA's own order (chunk 2 kk + h); fp8 weights use chunk 2 h + kk for both
+  // operands -- the same permutation of k on both sides leaves the dot
+  // products unchanged -- so one 16-byte read of a fp8 weight row holds the
+  // lane's values for both k16 steps of the stage.
+  u32x4 w8[C::TW];  // fp8: the stage's raw weight bytes (both steps)
+  auto read_frags = [&](Frags& F, const char* L, int kk) {
+    const int h = lane >> 5;
+    const int c = (WDT == GD_FP8) ? 2 * h + kk : kk * 2 + h;
 #pragma unroll
-    for (int i = 0; i < C::TW; ++i)
-      F.w[i] = *(const bf16x8*)(L + C::A_ELEMS +
-                                lds_off(wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31), c));
+    for (int i = 0; i < C::TW; ++i) {
+      const int wr = wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31);
+      if (WDT == GD_FP8) {
+        if (kk == 0) w8[i] = *(const u32x4*)(L + M::A_BYTES + f8_off(wr, h));
+        F.w[i] = kk == 0 ? e4m3x8_to_bf16(w8[i][0], w8[i][1]) : e4m3x8_to_bf16(w8[i][2], w8[i][3]);
+      } else {
+        F.w[i] = *(const bf16x8*)(L + M::A_BYTES + 2 * lds_off(wr, c));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < C::TA; ++j)
-      F.x[j] = *(const bf16x8*)(L + lds_off(arow + j * 32 + (lane & 31), c));
+      F.x[j] = *(const bf16x8*)(L + 2 * lds_off(arow + j * 32 + (lane & 31), c));
   };
   auto mfmas = [&](const Frags& F) {
 #pragma unroll
@@ -316,13 +360,13 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   issue_part(1, 1, 0); issue_part(1, 1, 1);
   issue_part(2, 2, 0); issue_part(2, 2, 1);
   issue_part(3, 3, 0);
-  wait_vmcnt<2 * C::LOADS + C::A_LOADS>();  // stage 0 done
+  wait_vmcnt<2 * M::LOADS + M::A_LOADS>();  // stage 0 done
   barrier_only();
 
   Frags F[2];
   read_frags(F[0], lds, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const __bf16* L = lds + (kt % STAGES) * C::STAGE;
+    const char* L = lds + (kt % STAGES) * M::STAGE_BYTES;
     // step 0: next fragments of this stage, B half of stage kt+3
     read_frags(F[1], L, 1);
     issue_part(kt + 3, (kt + 3) % STAGES, 1);
@@ -331,10 +375,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     // step 1: stage kt+1 resident and stage kt retired everywhere, then the
     // A half of stage kt+4 into buffer kt % 4 and stage kt+1's first fragments
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    wait_vmcnt<2 * C::LOADS>();
+    wait_vmcnt<2 * M::LOADS>();
     barrier_only();
     issue_part(kt + 4, kt % STAGES, 0);
-    read_frags(F[0], lds + ((kt + 1) % STAGES) * C::STAGE, 0);
+    read_frags(F[0], lds + ((kt + 1) % STAGES) * M::STAGE_BYTES, 0);
     mfmas(F[1]);
     interleave_refill();
   }
@@ -353,17 +397,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     return;
   }
-  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave),
-                                        lane);
+  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
 }
 #endif
 
-template <int BN, int WN, int EPI>
+template <int BN, int WN, int EPI, int WDT>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n_tiles, int kt_plan,
                                                                 int n_cu) {
   // device pass only: the host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * BigCfg<BN, WN, false>::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, false, WDT>::STAGE_BYTES];
   Work wk;
   if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
@@ -372,16 +415,16 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
   if (ti.nrows <= BM / 2)
-    big_tile<BN, WN, EPI, true>(a, ti, sg, wk, ncol0, lds);
+    big_tile<BN, WN, EPI, true, WDT>(a, ti, sg, wk, ncol0, lds);
   else
-    big_tile<BN, WN, EPI, false>(a, ti, sg, wk, ncol0, lds);
+    big_tile<BN, WN, EPI, false, WDT>(a, ti, sg, wk, ncol0, lds);
 #endif
 }
 
 
 // Sum of a split tile's K-pieces in piece order, each thread its own
 // accumulator registers (the layout the pieces stored), then the epilogue.
-template <int BN, int WN, int EPI, bool HALF>
+template <int BN, int WN, int EPI, bool HALF, int WDT>
 __device__ __forceinline__ void fixup_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
                                            int first_slot, int s) {
   using C = BigCfg<BN, WN, HALF>;
@@ -408,12 +451,12 @@ __device__ __forceinline__ void fixup_tile(const GemmArgs& a, const TileInfo& ti
           acc[i][j][4 * q + 3] += v.w;
         }
   }
-  store_tile<C::TW, C::TA, GD_BF16, EPI>(a, ti, sg, acc, wave_arow<BN, WN, HALF>(wave),
+  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, wave_arow<BN, WN, HALF>(wave),
                                         ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
 }
 
 // One block per split tile.
-template <int BN, int WN, int EPI>
+template <int BN, int WN, int EPI, int WDT>
 __global__ __launch_bounds__(128 * WN) void gemm_big_fixup_kernel(GemmArgs a, int n_tiles, int kt_plan,
                                                                   int n_cu) {
   const int m_real = real_mtiles(a, BM);
@@ -427,9 +470,9 @@ __global__ __launch_bounds__(128 * WN) void gemm_big_fixup_kernel(GemmArgs a, in
   const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
   if (ti.nrows <= BM / 2)
-    fixup_tile<BN, WN, EPI, true>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+    fixup_tile<BN, WN, EPI, true, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
   else
-    fixup_tile<BN, WN, EPI, false>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+    fixup_tile<BN, WN, EPI, false, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
 }
 
 // Compute units of the current device (the split plan fills one wave of them).
@@ -445,7 +488,7 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int BN, int EPI, int WN = MOE_BIG_WN>
+template <int BN, int EPI, int WDT, int WN = MOE_BIG_WN>
 hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   GemmArgs a = a_in;
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
@@ -462,10 +505,10 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   // whole tiles plus at most one wave of pieces, 8 XCD shares rounded up
   int nb = n_slots * n_tiles + (n_cu > 0 ? n_cu + 8 : 0);
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI>), dim3(nb), dim3(128 * WN), 0, s, a,
+  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb), dim3(128 * WN), 0, s, a,
                      n_tiles, kt_plan, n_cu);
   if (n_cu > 0)
-    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI>), dim3(n_cu / 2), dim3(128 * WN),
+    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT>), dim3(n_cu / 2), dim3(128 * WN),
                        0, s, a, n_tiles, kt_plan, n_cu);
   return hipGetLastError();
 }
@@ -473,8 +516,12 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
-  if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU>(a, s);
-  return (a.N % 256 == 0) ? launch_big<256, EPI_STORE>(a, s) : launch_big<128, EPI_STORE>(a, s);
+  if (a.wdt == GD_FP8) {
+    if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU, GD_FP8>(a, s);
+    return (a.N % 256 == 0) ? launch_big<256, EPI_STORE, GD_FP8>(a, s) : launch_big<128, EPI_STORE, GD_FP8>(a, s);
+  }
+  if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU, GD_BF16>(a, s);
+  return (a.N % 256 == 0) ? launch_big<256, EPI_STORE, GD_BF16>(a, s) : launch_big<128, EPI_STORE, GD_BF16>(a, s);
 }
 
 }  // namespace moe

@@ -126,14 +126,26 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
                                            f32x16 (&acc)[TW][TA], int row_base, int col0,
                                            int lane) {
   const int r_in = lane & 31;
+  const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr;
+  if (EPI == EPI_SWIGLU) {
 #pragma unroll
-  for (int j = 0; j < TA; ++j) {
-    const int lrow = row_base + j * 32 + r_in;
-    if (lrow >= ti.nrows) continue;
-    const size_t row = (size_t)(ti.row0 + lrow);
-    if (EPI == EPI_SWIGLU) {
+    for (int i = 0; i < TW / 2; ++i) {
+      // fp8 per-output-channel scales of this block's columns: one 16-byte
+      // load per run of 4 columns, shared by all activation blocks
+      float4 su[4], sv[4];
 #pragma unroll
-      for (int i = 0; i < TW / 2; ++i) {
+      for (int g = 0; g < 4; ++g) {
+        const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+        if (scaled) {
+          su[g] = *(const float4*)(sg.s0 + n);
+          sv[g] = *(const float4*)(sg.s1 + n);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TA; ++j) {
+        const int lrow = row_base + j * 32 + r_in;
+        if (lrow >= ti.nrows) continue;
+        const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
@@ -142,9 +154,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
           for (int q = 0; q < 4; ++q) {
             float u = acc[i][j][g * 4 + q];
             float v = acc[i + TW / 2][j][g * 4 + q];
-            if (WDT == GD_FP8 && sg.s0) {
-              u *= sg.s0[n + q];
-              v *= sg.s1[n + q];
+            if (scaled) {
+              u *= su[g][q];
+              v *= sv[g][q];
             }
             hv[q] = silu(u) * v;
           }
@@ -154,9 +166,19 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
           *(u32x2*)((uint16_t*)sg.C + row * sg.N + n) = o;
         }
       }
-    } else if (EPI == EPI_STORE) {
+    }
+  } else if (EPI == EPI_STORE) {
 #pragma unroll
-      for (int i = 0; i < TW; ++i) {
+    for (int i = 0; i < TW; ++i) {
+      float4 sc[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (scaled) sc[g] = *(const float4*)(sg.s0 + col0 + i * 32 + g * 8 + (lane >> 5) * 4);
+#pragma unroll
+      for (int j = 0; j < TA; ++j) {
+        const int lrow = row_base + j * 32 + r_in;
+        if (lrow >= ti.nrows) continue;
+        const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
@@ -164,7 +186,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             yv[q] = acc[i][j][g * 4 + q];
-            if (WDT == GD_FP8 && sg.s0) yv[q] *= sg.s0[n + q];
+            if (scaled) yv[q] *= sc[g][q];
           }
           u32x2 o;
           o[0] = pack_bf16x2(yv[0], yv[1]);
@@ -172,7 +194,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
           *(u32x2*)((uint16_t*)sg.C + row * sg.N + n) = o;
         }
       }
-    } else {  // EPI_BIAS_F32: router logits (partial sums of one K range)
+    }
+  } else {  // EPI_BIAS_F32: router logits (partial sums of one K range)
+#pragma unroll
+    for (int j = 0; j < TA; ++j) {
+      const int lrow = row_base + j * 32 + r_in;
+      if (lrow >= ti.nrows) continue;
+      const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
 #pragma unroll

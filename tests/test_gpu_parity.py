@@ -38,6 +38,10 @@ CASES = {
     "decode_shared_wide": DSV3_DECODE.scaled(T=70, d=256, f=128, E=32, f_shared=384),
     "dsv3_skew_small": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128),
     "qwen_fp8_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32),
+    # fp8 weights in the 256-row kernel: skewed tails (half tiles), K-split
+    # gate-up tiles, and a 128-wide down-projection tile (d = 384)
+    "qwen_fp8_big": QWEN_FP8_SKEW.scaled(T=800, d=512, f=384, E=16, k=4),
+    "qwen_fp8_big_n128": QWEN_FP8_SKEW.scaled(T=600, d=384, f=256, E=8, k=4),
 }
 
 _CACHE = {}
@@ -125,7 +129,8 @@ def test_stages_chain(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "qwen_fp8_small", "tiny_f32_ragged", "dsv3_skew_small",
-                                  "mixtral_big_tiles", "dsv3_decode_small", "mixtral_big_split"])
+                                  "mixtral_big_tiles", "dsv3_decode_small", "mixtral_big_split",
+                                  "qwen_fp8_big"])
 def test_grouped_ffn_from_oracle_inputs(name):
     """The FFN stage fed the oracle's own x_perm and offsets."""
     w, L, dev, ref = _setup(name)
@@ -170,7 +175,7 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
-                                  "decode_shared_wide", "mixtral_big_split"])
+                                  "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
