@@ -42,10 +42,24 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunk
   const int e = threadIdx.x;
   int run = 0;
   if (e < a.E) {
-    for (int c = 0; c < n_chunks; ++c) {
+    // rows of e before chunk c (relative to offsets[e]); the chunk counts are
+    // read 16 at a time so their loads are in flight together
+    constexpr int kBatch = 16;
+    int c0 = 0;
+    for (; c0 + kBatch <= n_chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = a.chunk_cnt[(size_t)(c0 + u) * a.E + e];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        a.chunk_cnt[(size_t)(c0 + u) * a.E + e] = run;
+        run += v[u];
+      }
+    }
+    for (int c = c0; c < n_chunks; ++c) {
       int* p = a.chunk_cnt + (size_t)c * a.E + e;
       const int v = *p;
-      *p = run;  // rows of e before chunk c (relative to offsets[e])
+      *p = run;
       run += v;
     }
     a.counts[e] = run;
@@ -60,17 +74,14 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunk
     __syncthreads();
   }
   const int excl = tot[e] - ((e < a.E) ? run : 0);
-  if (e < a.E) {
-    a.offsets[e] = excl;
-    for (int c = 0; c < n_chunks; ++c) a.chunk_cnt[(size_t)c * a.E + e] += excl;
-  }
+  if (e < a.E) a.offsets[e] = excl;  // the scatter adds it to the relative chunk bases
   if (e == a.E - 1) a.offsets[a.E] = tot[e];
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
   __shared__ int next_row[kMaxE];
   const int lane = threadIdx.x;
-  for (int e = lane; e < a.E; e += 64) next_row[e] = a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
+  for (int e = lane; e < a.E; e += 64) next_row[e] = a.offsets[e] + a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
   __syncthreads();
   const int base = blockIdx.x * kDispatchChunk;
   const int end = min(base + kDispatchChunk, a.n_assign);

@@ -325,10 +325,12 @@ hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 // Prefill-shaped problems with bf16 activations and bf16 or fp8 weights
-// (enough rows per expert to fill 256-row tiles) go to the direct-to-LDS
-// 256-row kernel; the rest use 128-row tiles.
+// (enough rows per expert to fill 256-row tiles), and router logits of at
+// least 1024 tokens, go to the direct-to-LDS 256-row kernel; the rest use
+// 128-row tiles.
 static bool use_big(const GemmArgs& a) {
-  if (a.act != GD_BF16 || a.wdt == GD_F32 || a.epi == EPI_BIAS_F32) return false;
+  if (a.act != GD_BF16 || a.wdt == GD_F32) return false;
+  if (a.epi == EPI_BIAS_F32) return a.wdt == GD_BF16 && a.tile_table == nullptr && a.rows >= 1024;
   const int segs = a.E > 0 ? a.E : 1;
   return a.rows >= 1024 && a.rows / segs >= 128;
 }

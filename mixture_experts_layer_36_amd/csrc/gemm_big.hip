@@ -23,7 +23,8 @@
 //   * tiles that remain after the last full wave of tiles (one tile per
 //     compute unit) are split along K into pieces that fill that wave; each
 //     piece stores its raw fp32 accumulators and a fixup kernel adds the
-//     pieces in order and runs the epilogue, so the result is deterministic
+//     pieces in order and applies the epilogue (many blocks per split tile,
+//     one 4-column run per work unit), so the result is deterministic
 //     (the down projection of a Mixtral-shaped layer has 2.25 waves of
 //     tiles, so without this its last wave would run a quarter full);
 //   * LDS rows of BK elements with 16-byte chunks XOR-swizzled by row
@@ -209,9 +210,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int K = sg.K;
-  // this block's k-stages of the segment: all, or piece k0num of s
+  // this block's k-stages of the segment: all, piece k0num of s, or (router
+  // logits) the blockIdx.y-th of ksplit ranges
   const int KT_all = K / BK;
-  const int kt0 = wk.k0num * KT_all / wk.s, kt1 = (wk.k0num + 1) * KT_all / wk.s;
+  const int np = wk.s * a.ksplit, pi = wk.k0num * a.ksplit + (int)blockIdx.y;
+  const int kt0 = pi * KT_all / np, kt1 = (pi + 1) * KT_all / np;
 
   // Direct loads go through buffer resources: a block-uniform descriptor
   // (SGPRs) per operand, a 32-bit per-lane byte offset fixed across stages
@@ -422,57 +425,88 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
 }
 
 
-// Sum of a split tile's K-pieces in piece order, each thread its own
-// accumulator registers (the layout the pieces stored), then the epilogue.
+// Fixup of the split tiles, one float4 of the pieces' register layout per
+// work unit: unit ((i * TA + j) * 4 + g) * NTHR + t holds accumulator floats
+// 4g..4g+3 of block (i, j) of GEMM thread t, i.e. four consecutive output
+// columns of one row.  The unit's pieces are added in piece order (the same
+// sum whichever block ran which piece), then the tile's epilogue is applied
+// to those four columns.  SwiGLU units pair block i (u) with block i + TW/2
+// (v).  Spreading units over many blocks keeps the reads in flight.
+constexpr int kFixupChunks = 16;  // blocks per split tile
 template <int BN, int WN, int EPI, bool HALF, int WDT>
-__device__ __forceinline__ void fixup_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
-                                           int first_slot, int s) {
+__device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
+                                            int first_slot, int s) {
   using C = BigCfg<BN, WN, HALF>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  f32x16 acc[C::TW][C::TA];
-#pragma unroll
-  for (int i = 0; i < C::TW; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TA; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  for (int piece = 0; piece < s; ++piece) {
-    const float4* P = (const float4*)(a.partial + (size_t)(first_slot + piece) * (kPartialSlotBytes / 4));
-#pragma unroll
-    for (int i = 0; i < C::TW; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TA; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v = P[((i * C::TA + j) * 4 + q) * C::NTHR + tid];
-          acc[i][j][4 * q] += v.x;
-          acc[i][j][4 * q + 1] += v.y;
-          acc[i][j][4 * q + 2] += v.z;
-          acc[i][j][4 * q + 3] += v.w;
-        }
+  constexpr int NT = 128 * WN;  // threads of the GEMM block
+  constexpr int TWO = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
+  constexpr int UNITS = NT * TWO * C::TA * 4;
+  constexpr size_t SLOT4 = kPartialSlotBytes / 16;
+  const float4* P = (const float4*)a.partial + (size_t)first_slot * SLOT4;
+  auto sum = [&](int e) {
+    float4 x = P[e];
+    for (int p = 1; p < s; ++p) {
+      const float4 y = P[(size_t)p * SLOT4 + e];
+      x.x += y.x;
+      x.y += y.y;
+      x.z += y.z;
+      x.w += y.w;
+    }
+    return x;
+  };
+  for (int u = blockIdx.y * blockDim.x + threadIdx.x; u < UNITS; u += gridDim.y * blockDim.x) {
+    const int t = u % NT, r = u / NT;
+    const int g = r & 3, j = (r >> 2) % C::TA, i = (r >> 2) / C::TA;
+    const int wave = t >> 6, lane = t & 63;
+    const int row = wave_arow<BN, WN, HALF>(wave) + j * 32 + (lane & 31);
+    if (row >= ti.nrows) continue;
+    const int n = ncol0 + wave_col<BN, WN, HALF, EPI>(wave) + i * 32 + g * 8 + (lane >> 5) * 4;
+    float o[4];
+    const float4 x = sum(((i * C::TA + j) * 4 + g) * NT + t);
+    if (EPI == EPI_SWIGLU) {
+      const float4 y = sum((((i + C::TW / 2) * C::TA + j) * 4 + g) * NT + t);
+      float4 su = make_float4(1.f, 1.f, 1.f, 1.f), sv = su;
+      if (WDT == GD_FP8 && sg.s0) {
+        su = *(const float4*)(sg.s0 + n);
+        sv = *(const float4*)(sg.s1 + n);
+      }
+      o[0] = silu(x.x * su.x) * (y.x * sv.x);
+      o[1] = silu(x.y * su.y) * (y.y * sv.y);
+      o[2] = silu(x.z * su.z) * (y.z * sv.z);
+      o[3] = silu(x.w * su.w) * (y.w * sv.w);
+    } else {
+      float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (WDT == GD_FP8 && sg.s0) sc = *(const float4*)(sg.s0 + n);
+      o[0] = x.x * sc.x;
+      o[1] = x.y * sc.y;
+      o[2] = x.z * sc.z;
+      o[3] = x.w * sc.w;
+    }
+    u32x2 v;
+    v[0] = pack_bf16x2(o[0], o[1]);
+    v[1] = pack_bf16x2(o[2], o[3]);
+    *(u32x2*)((uint16_t*)sg.C + (size_t)(ti.row0 + row) * sg.N + n) = v;
   }
-  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, wave_arow<BN, WN, HALF>(wave),
-                                        ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
 }
 
-// One block per split tile.
+// Blocks (split tile, chunk).
 template <int BN, int WN, int EPI, int WDT>
-__global__ __launch_bounds__(128 * WN) void gemm_big_fixup_kernel(GemmArgs a, int n_tiles, int kt_plan,
-                                                                  int n_cu) {
-  const int m_real = real_mtiles(a, BM);
-  const SplitPlan p = split_plan(m_real * n_tiles, kt_plan, n_cu, a.partial ? a.partial_slots : 0);
-  if ((int)blockIdx.x >= p.rem) return;
-  int mt, nt;
-  tile_coords(p.full + blockIdx.x, m_real, n_tiles, mt, nt);
-  TileInfo ti;
-  Seg sg;
-  if (!tile_info(a, mt, BM, ti, sg)) return;
-  const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
-  if (ncol0 >= sg.N) return;
-  if (ti.nrows <= BM / 2)
-    fixup_tile<BN, WN, EPI, true, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
-  else
-    fixup_tile<BN, WN, EPI, false, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+__global__ __launch_bounds__(256) void gemm_big_fixup_kernel(GemmArgs a, int n_tiles, int kt_plan, int n_cu) {
+  if constexpr (EPI != EPI_BIAS_F32) {  // router logits never split this way
+    const int m_real = real_mtiles(a, BM);
+    const SplitPlan p = split_plan(m_real * n_tiles, kt_plan, n_cu, a.partial ? a.partial_slots : 0);
+    if ((int)blockIdx.x >= p.rem) return;
+    int mt, nt;
+    tile_coords(p.full + blockIdx.x, m_real, n_tiles, mt, nt);
+    TileInfo ti;
+    Seg sg;
+    if (!tile_info(a, mt, BM, ti, sg)) return;
+    const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+    if (ncol0 >= sg.N) return;
+    if (ti.nrows <= BM / 2)
+      fixup_units<BN, WN, EPI, true, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+    else
+      fixup_units<BN, WN, EPI, false, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+  }
 }
 
 // Compute units of the current device (the split plan fills one wave of them).
@@ -496,7 +530,8 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   const int n_tiles = (gemm_max_cols(a) + ncol - 1) / ncol;
   const int kt_plan = (a.sh_rows > 0 ? min(a.K, a.shK) : a.K) / BK;
   int n_cu = device_cus();
-  if (n_cu <= 0 || n_cu % 8 != 0 || a.partial == nullptr) {
+  if (a.ksplit < 1) a.ksplit = 1;
+  if (n_cu <= 0 || n_cu % 8 != 0 || a.partial == nullptr || a.ksplit > 1) {
     n_cu = 0;  // no split: every tile runs whole
     a.partial = nullptr;
     a.partial_slots = 0;
@@ -505,10 +540,10 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   // whole tiles plus at most one wave of pieces, 8 XCD shares rounded up
   int nb = n_slots * n_tiles + (n_cu > 0 ? n_cu + 8 : 0);
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb), dim3(128 * WN), 0, s, a,
+  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb, a.ksplit), dim3(128 * WN), 0, s, a,
                      n_tiles, kt_plan, n_cu);
   if (n_cu > 0)
-    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT>), dim3(n_cu / 2), dim3(128 * WN),
+    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT>), dim3(n_cu / 2, kFixupChunks), dim3(256),
                        0, s, a, n_tiles, kt_plan, n_cu);
   return hipGetLastError();
 }
@@ -516,6 +551,7 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
+  if (a.epi == EPI_BIAS_F32) return launch_big<256, EPI_BIAS_F32, GD_BF16>(a, s);
   if (a.wdt == GD_FP8) {
     if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU, GD_FP8>(a, s);
     return (a.N % 256 == 0) ? launch_big<256, EPI_STORE, GD_FP8>(a, s) : launch_big<128, EPI_STORE, GD_FP8>(a, s);

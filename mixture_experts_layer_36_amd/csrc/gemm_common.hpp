@@ -206,12 +206,25 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+          float* zr = (float*)sg.C + ((size_t)blockIdx.y * a.rows + row) * sg.N + n;
+          if ((sg.N & 3) == 0 && n + 3 < sg.N) {  // whole run, 16-byte aligned
+            float4 z = make_float4(acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                   acc[i][j][g * 4 + 3]);
+            if (a.bias && blockIdx.y == 0) {
+              z.x += a.bias[n];
+              z.y += a.bias[n + 1];
+              z.z += a.bias[n + 2];
+              z.w += a.bias[n + 3];
+            }
+            *(float4*)zr = z;
+          } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (n + q < sg.N) {
-              float z = acc[i][j][g * 4 + q];
-              if (a.bias && blockIdx.y == 0) z += a.bias[n + q];
-              ((float*)sg.C)[((size_t)blockIdx.y * a.rows + row) * sg.N + n + q] = z;
+            for (int q = 0; q < 4; ++q) {
+              if (n + q < sg.N) {
+                float z = acc[i][j][g * 4 + q];
+                if (a.bias && blockIdx.y == 0) z += a.bias[n + q];
+                zr[q] = z;
+              }
             }
           }
         }

@@ -96,10 +96,25 @@ struct RouteWs {
 // next to the inputs.  K / ksplit stays a multiple of the 64-wide k step.
 int route_splits(const moe_desc* d) {
   if (d->act == MOE_F32) return 1;
-  const int64_t tiles = int64_t((d->T + 127) / 128) * ((d->E + 127) / 128);
-  const int64_t kmax = d->d / 64;
+  GemmArgs g{};  // the launch the router GEMM will use
+  g.act = gemm_dtype(d->act);
+  g.wdt = gemm_dtype(d->act);
+  g.rows = d->T;
+  g.epi = EPI_BIAS_F32;
+  const int bm = gemm_block_m(g);
   const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
   const int64_t part_bytes = int64_t(d->T) * d->E * 4;
+  if (bm == 256) {
+    // 256 x 256 tiles: split K until one wave of the GPU is filled, each
+    // range at least 8 stages of 32, the partial sums at most twice the input
+    const int64_t tiles = int64_t((d->T + 255) / 256) * ((d->E + 255) / 256);
+    int64_t want = (256 + tiles - 1) / tiles;
+    want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, d->d / 256));
+    return int(std::max<int64_t>(1, std::min<int64_t>(want, 16)));
+  }
+  const int64_t tiles = int64_t((d->T + 127) / 128) * ((d->E + 127) / 128);
+  const int64_t kmax = d->d / 64;
   int64_t want = (1024 + tiles - 1) / tiles;
   want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
   int s = 1;

@@ -14,8 +14,8 @@
 // logit << 32 | ~expert id), so the largest key is the largest score with ties
 // going to the lower id.  Softmax and sigmoid are strictly increasing in the
 // logit, so ranking logits ranks scores.  Each lane holds experts
-// lane, lane+64, ... (up to 8 for E <= 512); the wave-wide maximum is a
-// butterfly of DPP/ds_swizzle shuffles.  With a group limit (the single-GPU
+// lane, lane+64, ... (up to 8 for E <= 512); the wave-wide maximum uses DPP
+// moves within rows of 16 lanes and one read lane per row.  With a group limit (the single-GPU
 // form of node-limited routing, same page, section "Load imbalance and how to
 // fight it"), group scores (sum of each contiguous group's two largest scores)
 // go through LDS and groups outside the best topk_group are masked out.
@@ -38,15 +38,29 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// 64-bit lane move through DPP (VALU data-parallel primitives, no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Wave-wide maximum, the same in every lane: within each row of 16 lanes by
+// DPP swaps (quad_perm [1,0,3,2], [2,3,0,1]) and rotations (row_ror 4, 8),
+// then across the four rows from one lane of each.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x124>(v));  // row_ror 4
+  v = max_u64(v, dpp_u64<0x128>(v));  // row_ror 8
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
