@@ -12,6 +12,8 @@ inputs already resident in HBM.  Prints one JSON line:
               HIP events the library records around each stage inside the
               timed steps, on the stream the kernels run on
   cpu_baseline the float64 oracle on a bounded token sample, host cores
+  stages_gbps achieved GB/s of the route, dispatch and combine stages
+              (algorithmic bytes over the stage's event time)
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -71,6 +73,28 @@ def layer_bytes(w, counts) -> float:
     b = w.T * w.d * ab * 2 + w.E * w.d * ab + w.E * 4 + touched * per_expert
     b += 3 * w.d * w.f_shared * ab + 8 * w.T * w.k
     return float(b)
+
+
+def stage_bytes(w, has_bias: bool) -> dict:
+    """Algorithmic bytes of the memory-bound stages of the layer path:
+    route = x + router weight (+ bias) + the top-k indices and gates written;
+    dispatch = the index work (top-k ids read, per-expert counts and offsets,
+    perm_token and inv_pos written) -- the row gather itself is fused into the
+    gate-up GEMM's activation loads; combine = the T*k routed rows read, the
+    indices and gates, out written (+ the shared expert's rows read)."""
+    ab = 4 if w.act == "f32" else 2
+    tk = w.T * w.k
+    route = w.T * w.d * ab + w.E * w.d * ab + (w.E * 4 if has_bias else 0) + 8 * tk
+    dispatch = 4 * tk + 8 * tk + 8 * w.E
+    combine = tk * w.d * ab + 8 * tk + w.T * w.d * ab + (w.T * w.d * ab if w.f_shared else 0)
+    return {"route": float(route), "dispatch": float(dispatch), "combine": float(combine)}
+
+
+# Ceilings measured on MI355X by separate probes (not in this run): a
+# register-only loop of 32x32x16 bf16 MFMAs on every SIMD, and a streaming
+# read of 8 GiB with 16-byte loads.
+MFMA_LOOP_TFLOPS = 1785.0
+STREAM_READ_GBS = 6300.0
 
 
 def calibrate_copy():
@@ -193,13 +217,15 @@ def main():
         achieved = layer_bytes(w, c) / layer_s / 1e9
         roof = {"bound": "hbm", "kernel": "whole layer (all kernels)", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "algorithmic_bytes": layer_bytes(w, c)}
+                "algorithmic_bytes": layer_bytes(w, c),
+                "frac_of_measured_read_ceiling": round(achieved / STREAM_READ_GBS, 4)}
     else:
         achieved = flops_gemm1 / gemm1_s / 1e12
         roof = {"bound": "mfma", "kernel": "routed gate-up GEMM + SwiGLU (gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU)",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops_gemm1,
-                "avg_launch_us": round(gemm1_s * 1e6, 2)}
+                "avg_launch_us": round(gemm1_s * 1e6, 2),
+                "frac_of_measured_mfma_ceiling": round(achieved / MFMA_LOOP_TFLOPS, 4)}
     # HBM bytes per launch of that kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE passes, valid only while the kernels are unchanged
     roof["traffic"] = None
@@ -221,13 +247,15 @@ def main():
         "roofline": roof,
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
         "stages_us": stage_us,
+        "stages_gbps": {k: round(v / (stage_us[k] * 1e-6) / 1e9, 1)
+                        for k, v in stage_bytes(w, dev.bias is not None).items()},
         "step_event_ms": round(step_event_ms, 4),
         "load": {"max_over_mean": round(float(c.max() / c.mean()), 3),
                  "experts_touched": int((c > 0).sum()), "experts": w.E},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral8x7b_prefill_bf16": 48, "tiny_f32": 64}.get(w.name, 16)
+        sample = args.cpu_sample or {"mixtral8x7b_prefill_bf16": 4096, "tiny_f32": 64}.get(w.name, 16)
         rec["cpu_baseline"] = cpu_baseline(w, L, host_experts, min(sample, w.T))
     print(json.dumps(rec))
 

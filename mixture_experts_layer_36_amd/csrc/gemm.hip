@@ -330,7 +330,8 @@ hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
 // 128-row tiles.
 static bool use_big(const GemmArgs& a) {
   if (a.act != GD_BF16 || a.wdt == GD_F32) return false;
-  if (a.epi == EPI_BIAS_F32) return a.wdt == GD_BF16 && a.tile_table == nullptr && a.rows >= 1024;
+  // router logits: worth a 256-wide tile only with at least 128 experts
+  if (a.epi == EPI_BIAS_F32) return a.wdt == GD_BF16 && a.tile_table == nullptr && a.rows >= 1024 && a.N >= 128;
   const int segs = a.E > 0 ? a.E : 1;
   return a.rows >= 1024 && a.rows / segs >= 128;
 }

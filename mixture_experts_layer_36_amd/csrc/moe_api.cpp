@@ -100,6 +100,7 @@ int route_splits(const moe_desc* d) {
   g.act = gemm_dtype(d->act);
   g.wdt = gemm_dtype(d->act);
   g.rows = d->T;
+  g.N = d->E;
   g.epi = EPI_BIAS_F32;
   const int bm = gemm_block_m(g);
   const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
