@@ -44,7 +44,9 @@ float32 scale per output channel.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
+from fractions import Fraction
 from typing import Callable, Optional, Sequence
 
 import numpy as np
@@ -223,28 +225,51 @@ def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3
 # --------------------------------------------------------------------------
 
 
-def dispatch(topk_idx: np.ndarray, E: int):
+def expert_capacity(capacity_factor, T: int, k: int, E: int) -> int:
+    """Slots per expert, capacity = capacity_factor * (T * k / E) ("Expert-
+    Parallel MoE Inference", §Capacity factor and token dropping), rounded up
+    to whole slots (so a factor of 1.0 provisions at least the average load).
+    Exact: the factor is taken as the decimal it is written as (1.1 is 11/10).
+    0 means no limit (the dropless path) and is returned for factors <= 0."""
+    cf = capacity_factor if isinstance(capacity_factor, Fraction) else Fraction(str(capacity_factor))
+    if cf <= 0:
+        return 0
+    return int(math.ceil(cf * T * k / E))
+
+
+def dispatch(topk_idx: np.ndarray, E: int, capacity: int = 0):
     """Expert-contiguous layout of the T*k assignments a = t*k + j.
 
-    counts[e] = number of assignments to e; offsets = exclusive prefix sum;
-    assignments are placed in increasing a, each at its expert's next free row.
-    Returns counts[E], offsets[E+1], perm_token[T*k] (row -> token),
-    inv_pos[T*k] (assignment -> row).  This buffer is what the dispatch
-    exchange ships to the expert owners ("Expert-Parallel MoE Inference",
-    §The all-to-all dispatch and combine, step by step, Figure 3).
+    counts[e] = number of assignments to e (the demand); assignments claim
+    their expert's rows in increasing a.  With capacity > 0 each expert has
+    that many slots ("each routed token checks whether the target expert
+    still has a free capacity slot", "Expert-Parallel MoE Inference",
+    §Deeper Analysis, Figure 2): an assignment finding its expert full is
+    dropped (inv_pos = -1, no row).  offsets = exclusive prefix sum of the
+    kept counts.
+    Returns counts[E], offsets[E+1], perm_token[offsets[E]] (row -> token),
+    inv_pos[T*k] (assignment -> row, or -1).  This buffer is what the dispatch
+    exchange ships to the expert owners (same page, §The all-to-all dispatch
+    and combine, step by step, Figure 3).
     """
     T, k = topk_idx.shape
     a_exp = topk_idx.reshape(-1).astype(np.int64)
     counts = np.zeros(E, dtype=np.int64)
     for e in a_exp:
         counts[e] += 1
+    kept = counts if capacity <= 0 else np.minimum(counts, capacity)
     offsets = np.zeros(E + 1, dtype=np.int64)
     for e in range(E):
-        offsets[e + 1] = offsets[e] + counts[e]
+        offsets[e + 1] = offsets[e] + kept[e]
     nxt = offsets[:-1].copy()
-    perm_token = np.empty(T * k, dtype=np.int64)
+    used = np.zeros(E, dtype=np.int64)
+    perm_token = np.empty(offsets[E], dtype=np.int64)
     inv_pos = np.empty(T * k, dtype=np.int64)
     for a, e in enumerate(a_exp):
+        if capacity > 0 and used[e] == capacity:
+            inv_pos[a] = -1  # overflow: dropped
+            continue
+        used[e] += 1
         p = nxt[e]
         nxt[e] += 1
         inv_pos[a] = p
@@ -317,7 +342,9 @@ def combine(y_perm: np.ndarray, inv_pos: np.ndarray, topk_w: np.ndarray, act: st
     out = np.zeros((T, y_perm.shape[1]))
     pos = np.asarray(inv_pos, dtype=np.int64).reshape(T, k)
     for j in range(k):
-        out += topk_w[:, j: j + 1] * y_perm[pos[:, j]]
+        # a dropped assignment (inv_pos -1) skips the expert: no contribution
+        kept = pos[:, j] >= 0
+        out[kept] += topk_w[kept, j: j + 1] * y_perm[pos[kept, j]]
     if shared_y is not None:
         out += shared_y
     return round_act(out, act)
@@ -345,13 +372,15 @@ class LayerResult:
 
 
 def layer_forward(x, w_router, bias, spec: RouteSpec, E: int, expert_weights: ExpertFn, act: str,
-                  shared: Optional[Sequence[np.ndarray]] = None) -> LayerResult:
+                  shared: Optional[Sequence[np.ndarray]] = None, capacity: int = 0) -> LayerResult:
     """The whole layer: route, dispatch, grouped SwiGLU FFN, shared expert,
     combine.  x, w_router and the weights are float64 values of the stored
-    inputs.  The layer is token-wise: running it on a subset of the tokens
-    gives exactly those tokens' results."""
+    inputs.  Without a capacity the layer is token-wise: running it on a
+    subset of the tokens gives exactly those tokens' results.  With a
+    capacity (slots per expert) overflow assignments are dropped and the
+    kept ones keep their gates."""
     idx, gw, _ = route(x, w_router, bias, spec)
-    counts, offsets, perm_token, inv_pos = dispatch(idx, E)
+    counts, offsets, perm_token, inv_pos = dispatch(idx, E, capacity)
     x_perm = gather_rows(x, perm_token)
     h, y_perm = grouped_ffn(x_perm, offsets, expert_weights, act)
     sh = sy = None

@@ -66,7 +66,18 @@ QWEN_FP8_SKEW = Workload("qwen_moe_fp8_skew", T=8192, d=4096, f=1536, E=128,
                          topk_group=0, f_shared=0, act="bf16", wdt="e4m3",
                          bias_scale=1.5)
 
-ALL = (TINY_F32, MIXTRAL_PREFILL, DSV3_DECODE, DSV3_PREFILL_SKEW, QWEN_FP8_SKEW)
+# One GPU's share of the DeepSeek-V3-shaped prefill layer under 8-way expert
+# parallelism ("Expert-Parallel MoE Inference: Serving Sparse Models at
+# Scale", section "Deeper Analysis", the worked sizing of rows per expert and
+# GPU): 32 local experts and T*k/8 = 16384 routed rows; each GPU runs the
+# replicated shared expert on its own 2048 tokens.  The cross-GPU exchange
+# is not modelled -- only the per-GPU kernel shape.
+DSV3_EP8_SHARD = Workload("dsv3_ep8_shard_bf16", T=2048, d=7168, f=2048, E=32,
+                          k=8, score="sigmoid", renorm=True, n_group=0,
+                          topk_group=0, f_shared=2048, act="bf16", wdt="bf16",
+                          bias_scale=0.0)
+
+ALL = (TINY_F32, MIXTRAL_PREFILL, DSV3_DECODE, DSV3_PREFILL_SKEW, QWEN_FP8_SKEW, DSV3_EP8_SHARD)
 BY_NAME = {w.name: w for w in ALL}
 # Default seed of each workload: its position in ALL, counting from 1.
 DEFAULT_SEED = {w.name: i + 1 for i, w in enumerate(ALL)}

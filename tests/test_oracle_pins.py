@@ -389,11 +389,71 @@ def check_margin_rule():
     del x
 
 
+def check_capacity():
+    # slot formula: the page's worked numbers (4096 assignments over 256
+    # experts = 16 per expert) at a few factors, rounded up to whole slots
+    assert O.expert_capacity(1.0, 512, 8, 256) == 16
+    assert O.expert_capacity(1.25, 512, 8, 256) == 20
+    assert O.expert_capacity(2.0, 512, 8, 256) == 32
+    assert O.expert_capacity(1.1, 512, 8, 256) == 18      # 17.6 -> 18
+    assert O.expert_capacity(0.1, 10, 1, 1) == 1          # exact decimal, not 1.0000000000000000555
+    assert O.expert_capacity(0, 512, 8, 256) == 0 and O.expert_capacity(-1, 512, 8, 256) == 0
+    rng = np.random.default_rng(21)
+    for T, k, E, cap in ((40, 2, 4, 7), (100, 3, 8, 20), (64, 8, 16, 25), (30, 1, 3, 1)):
+        # skewed scores so some experts overflow
+        s = rng.random((T, E)) * np.linspace(1.0, 3.0, E)
+        idx = O.select_topk(s, O.RouteSpec(k=k))
+        a_exp = idx.reshape(-1)
+        counts, offsets, perm_token, inv_pos = O.dispatch(idx, E, cap)
+        full = O.dispatch(idx, E)
+        # special case: a capacity no expert reaches is the dropless layout
+        big = O.dispatch(idx, E, int(full[0].max()))
+        for u, v in zip(big, full):
+            assert np.array_equal(u, v)
+        assert np.array_equal(counts, full[0])             # counts stay the demand
+        # brute force: per expert, the first `cap` assignments in increasing a
+        kept = np.zeros(T * k, dtype=bool)
+        for e in range(E):
+            mine = [a for a in range(T * k) if a_exp[a] == e]
+            kept[mine[:cap]] = True
+        assert np.array_equal(inv_pos >= 0, kept)
+        assert np.array_equal(np.diff(offsets), np.minimum(full[0], cap))
+        assert offsets[-1] == kept.sum() == len(perm_token)
+        for e in range(E):
+            rows = [a for a in range(T * k) if a_exp[a] == e and kept[a]]
+            assert np.array_equal(inv_pos[rows], offsets[e] + np.arange(len(rows)))
+            assert np.array_equal(perm_token[offsets[e]:offsets[e + 1]], np.array(rows, dtype=np.int64) // k)
+    # drops only fall as the factor grows, and vanish once every expert fits
+    s = rng.random((200, 16)) * np.linspace(1.0, 4.0, 16)
+    idx = O.select_topk(s, O.RouteSpec(k=2))
+    drops = [int((O.dispatch(idx, 16, O.expert_capacity(cf, 200, 2, 16))[3] < 0).sum())
+             for cf in (0.5, 1.0, 1.25, 2.0, 8.0)]
+    assert all(a >= b for a, b in zip(drops, drops[1:])) and drops[0] > 0 and drops[-1] == 0
+    # layer closed form: the capacity layer's output is the dropless layer's
+    # per-assignment terms with the dropped ones removed (gates unchanged)
+    T, d, f, E, k = 24, 8, 16, 4, 2
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    W = _weights(rng, E, d, f)
+    spec = O.RouteSpec(k=k)
+    ref = O.layer_forward(x, wr, None, spec, E, lambda e: W[e], "f32")
+    cap = 5
+    got = O.layer_forward(x, wr, None, spec, E, lambda e: W[e], "f32", capacity=cap)
+    kept = got.inv_pos >= 0
+    assert (~kept).any() and kept.any()
+    want = np.zeros((T, d))
+    for a in range(T * k):
+        if kept[a]:
+            want[a // k] += ref.topk_w[a // k, a % k] * ref.y_perm[ref.inv_pos[a]]
+    assert np.array_equal(got.out, O.round_act(want, "f32"))  # same j order, same rounding
+
+
 CHECKS = [check_bf16_round, check_decoders, check_router_logits, check_scores,
           check_topk_bruteforce, check_k1_argmax, check_constructed_ties, check_group_limit,
           check_gates, check_worked_example_counts, check_ep_sizing_and_batch, check_dispatch,
           check_gather, check_dense_special_case, check_identical_experts_closed_form,
-          check_uniform_gates_mean, check_combine, check_locality, check_margin_rule]
+          check_uniform_gates_mean, check_combine, check_locality, check_margin_rule,
+          check_capacity]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -445,7 +505,9 @@ def _m_group_top1(s, n_group):
     return np.sort(s.reshape(T, n_group, E // n_group), axis=2)[:, :, -1]
 
 
-def _m_dispatch_unstable(topk_idx, E):
+def _m_dispatch_unstable(topk_idx, E, capacity=0):
+    if capacity > 0:
+        return _DISPATCH(topk_idx, E, capacity)
     c, o, p, i = _DISPATCH(topk_idx, E)
     p = p.copy()
     i = i.copy()
@@ -455,6 +517,23 @@ def _m_dispatch_unstable(topk_idx, E):
     for a in range(len(i)):
         e = topk_idx.reshape(-1)[a]
         i[a] = o[e] + o[e + 1] - 1 - i[a]
+    return c, o, p, i
+
+
+def _m_capacity_off_by_one(topk_idx, E, capacity=0):
+    return _DISPATCH(topk_idx, E, capacity + 1 if capacity > 0 else 0)
+
+
+def _m_capacity_keeps_last(topk_idx, E, capacity=0):
+    """Fills an expert's slots with its last assignments instead of its first."""
+    if capacity <= 0:
+        return _DISPATCH(topk_idx, E)
+    T, k = topk_idx.shape
+    rev = topk_idx.reshape(-1)[::-1].reshape(T, k)
+    c, o, p, i = _DISPATCH(rev, E, capacity)
+    n = T * k
+    i = i[::-1].copy()
+    p = np.array([n - 1 - 0 for _ in p])  # rows no longer name the right tokens
     return c, o, p, i
 
 
@@ -485,11 +564,13 @@ MUTATIONS = [
     ("group_scores", _m_group_top1),
     ("dispatch", _m_dispatch_unstable),
     ("combine", _m_combine_wrong_index),
+    ("dispatch", _m_capacity_off_by_one),
+    ("dispatch", _m_capacity_keeps_last),
     ("round_bf16", _m_round_truncate),
 ]
 
 
-@pytest.mark.parametrize("name,bad", MUTATIONS, ids=[m[0] + "_mutant" for m in MUTATIONS])
+@pytest.mark.parametrize("name,bad", MUTATIONS, ids=[m[0] + "_" + m[1].__name__.lstrip("_") for m in MUTATIONS])
 def test_planted_mistakes(monkeypatch, name, bad):
     monkeypatch.setattr(M, name, bad)
     # O.* re-exports bind the original objects: patch those names too
