@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens for the oracle timing")
+    p.add_argument("--capacity-factor", type=float, default=0.0,
+                   help="expert capacity = factor * T * k / E slots (0: dropless); overflow is dropped")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -75,18 +77,19 @@ def layer_bytes(w, counts) -> float:
     return float(b)
 
 
-def stage_bytes(w, has_bias: bool) -> dict:
+def stage_bytes(w, has_bias: bool, kept: int) -> dict:
     """Algorithmic bytes of the memory-bound stages of the layer path:
     route = x + router weight (+ bias) + the top-k indices and gates written;
     dispatch = the index work (top-k ids read, per-expert counts and offsets,
     perm_token and inv_pos written) -- the row gather itself is fused into the
-    gate-up GEMM's activation loads; combine = the T*k routed rows read, the
+    gate-up GEMM's activation loads; combine = the routed rows read (T*k, or
+    those kept under a capacity), the
     indices and gates, out written (+ the shared expert's rows read)."""
     ab = 4 if w.act == "f32" else 2
     tk = w.T * w.k
     route = w.T * w.d * ab + w.E * w.d * ab + (w.E * 4 if has_bias else 0) + 8 * tk
     dispatch = 4 * tk + 8 * tk + 8 * w.E
-    combine = tk * w.d * ab + 8 * tk + w.T * w.d * ab + (w.T * w.d * ab if w.f_shared else 0)
+    combine = kept * w.d * ab + 8 * tk + w.T * w.d * ab + (w.T * w.d * ab if w.f_shared else 0)
     return {"route": float(route), "dispatch": float(dispatch), "combine": float(combine)}
 
 
@@ -127,8 +130,10 @@ def cpu_baseline(w, L, host_experts, sample):
         return w1, w3, w2
 
     shared = O.adapters.decoded_shared(L)
+    # with a capacity factor the sample gets its own slots (factor * sample * k / E)
+    cap = O.expert_capacity(getattr(w, "capacity_factor", 0), sample, w.k, w.E)
     t0 = time.perf_counter()
-    O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared)
+    O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
@@ -154,6 +159,8 @@ def main():
         return
     w = BY_NAME[args.workload]
     seed = DEFAULT_SEED[w.name] if args.seed is None else args.seed
+    if args.capacity_factor > 0:
+        w = w.scaled(capacity_factor=args.capacity_factor)
     L = LayerInputs(w, seed)
     host_experts = {}
 
@@ -204,8 +211,10 @@ def main():
                 for j, name in enumerate(moe.TRACE_STAGES)}
     step_event_ms = float(np.mean([tr[0].elapsed_time(tr[-1]) for tr in traces]))
     c = counts.cpu().numpy()
-    n_assign = int(c.sum())
-    assert n_assign == w.T * w.k, "routing lost assignments"
+    assert int(c.sum()) == w.T * w.k, "routing lost assignments"
+    cap = desc.capacity
+    kept = np.minimum(c, cap) if cap > 0 else c
+    n_assign = int(kept.sum())  # rows the experts process
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = w.T * args.steps / elapsed
@@ -243,15 +252,18 @@ def main():
         "dtype": "bf16" if w.act == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
-                   "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed},
+                   "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
+                   "capacity_factor": w.capacity_factor},
         "roofline": roof,
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
         "stages_us": stage_us,
         "stages_gbps": {k: round(v / (stage_us[k] * 1e-6) / 1e9, 1)
-                        for k, v in stage_bytes(w, dev.bias is not None).items()},
+                        for k, v in stage_bytes(w, dev.bias is not None, n_assign).items()},
         "step_event_ms": round(step_event_ms, 4),
         "load": {"max_over_mean": round(float(c.max() / c.mean()), 3),
                  "experts_touched": int((c > 0).sum()), "experts": w.E},
+        "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,
+                     "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -86,6 +86,10 @@ typedef struct {
   int32_t act;        /* moe_dtype of activations: MOE_F32 or MOE_BF16            */
   int32_t wdtype;     /* moe_dtype of routed weights: act, or MOE_FP8_E4M3 when
                          act is MOE_BF16 (per-output-channel fp32 scales)         */
+  int32_t capacity;   /* 0 = dropless; else slots per expert (>= 1): the page's
+                         capacity_factor * T * k / E, rounded up by the caller.
+                         Assignments claim slots in increasing a = t*k + j; one
+                         that finds its expert full is dropped (contributes 0) */
 } moe_desc;
 
 /* Number of hipEvents moe_layer_forward records when given a trace array. */
@@ -122,13 +126,20 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
 
 /* Dispatch.  For the T*k assignments a = t*k + j (expert topk_idx[t][j]):
  *   counts[e]      = number of assignments to expert e          int32 [E]
- *   offsets[e]     = sum of counts[e'] for e' < e; offsets[E] = T*k   [E+1]
+ *   kept[e]        = counts[e], or min(counts[e], capacity) with a capacity
+ *   offsets[e]     = sum of kept[e'] for e' < e; offsets[E] = sum of kept
+ *                    (T*k when dropless)                          int32 [E+1]
  *   inv_pos[a]     = row of assignment a: offsets[e] + number of earlier
- *                    assignments (smaller a) to the same expert  int32 [T*k]
- *   perm_token[p]  = token of row p (so perm_token[inv_pos[a]] = a / k) [T*k]
- *   x_perm[p][:]   = x[perm_token[p]][:]                  act dtype [T*k][d]
+ *                    assignments (smaller a) to the same expert, or -1 when
+ *                    that number reaches the capacity (dropped)   int32 [T*k]
+ *   perm_token[p]  = token of row p (so perm_token[inv_pos[a]] = a / k),
+ *                    for p < offsets[E]                            [T*k]
+ *   x_perm[p][:]   = x[perm_token[p]][:], p < offsets[E]  act dtype [T*k][d]
  * Rows of one expert are contiguous and in increasing token order; the result
- * is deterministic.  topk_idx entries must lie in [0, E).
+ * is deterministic.  topk_idx entries must lie in [0, E).  The capacity slots
+ * are those of "Expert-Parallel MoE Inference", section "Capacity factor and
+ * token dropping": each routed token takes a free slot of its expert or is
+ * dropped.
  * ws: device workspace of moe_workspace_size(MOE_STAGE_DISPATCH) bytes. */
 moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const void* x,
                         int32_t* counts, int32_t* offsets, int32_t* perm_token,
@@ -142,7 +153,7 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const voi
  *   y = h W2_e^T      (times s2 for fp8) stored in the act dtype [T*k][d]
  * SwiGLU, silu(u) = u / (1 + exp(-u)).
  *   offsets  [E+1] int32 (device), as produced by moe_dispatch; offsets[E]
- *            must equal T*k
+ *            <= T*k (rows past it are not touched)
  *   w1, w3   [E][f][d], w2 [E][d][f] in wdtype
  *   s1, s3   [E][f], s2 [E][d] fp32 per-output-channel scales when wdtype is
  *            MOE_FP8_E4M3, else NULL
@@ -154,7 +165,8 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32
 
 /* Combine.  out[t][:] = sum_{j<k} topk_w[t][j] * y_perm[inv_pos[t*k+j]][:]
  *                       (+ shared_y[t][:]), fp32 accumulation in that order,
- * stored in the act dtype.  No atomics: each token reads its own k rows.
+ * stored in the act dtype; terms with inv_pos = -1 (dropped) are skipped.
+ * No atomics: each token reads its own k rows.
  *   shared_y [T][d] act dtype, nullable. */
 moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* inv_pos,
                        const float* topk_w, const void* shared_y, void* out, void* stream);

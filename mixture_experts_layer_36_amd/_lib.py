@@ -8,6 +8,7 @@ raises.
 from __future__ import annotations
 
 import ctypes
+from fractions import Fraction
 import os
 from typing import Optional, Sequence
 
@@ -37,23 +38,37 @@ class MoeError(RuntimeError):
         super().__init__(f"{where}: {msg}")
 
 
+def capacity_slots(capacity_factor, T: int, k: int, E: int) -> int:
+    """Slots per expert for moe_desc.capacity: capacity_factor * T * k / E
+    rounded up, computed exactly from the decimal factor (1.1 is 11/10); 0
+    (dropless) for factors <= 0."""
+    cf = Fraction(str(capacity_factor))
+    if cf <= 0:
+        return 0
+    num = cf.numerator * T * k
+    den = cf.denominator * E
+    return -(-num // den)
+
+
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "f", "E", "k", "score", "renorm", "n_group", "topk_group",
-                 "f_shared", "act", "wdtype")]
+                 "f_shared", "act", "wdtype", "capacity")]
 
     @classmethod
     def make(cls, T, d, f, E, k, score="softmax", renorm=True, n_group=0, topk_group=0,
-             f_shared=0, act="bf16", wdtype="bf16") -> "Desc":
+             f_shared=0, act="bf16", wdtype="bf16", capacity=0) -> "Desc":
         return cls(T, d, f, E, k, SOFTMAX if score == "softmax" else SIGMOID, int(bool(renorm)),
-                   n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype])
+                   n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype], capacity)
 
     @classmethod
     def from_attrs(cls, w) -> "Desc":
         """From any object with T, d, f, E, k, score, renorm, n_group,
-        topk_group, f_shared, act and wdt attributes."""
+        topk_group, f_shared, act and wdt attributes (and optionally
+        capacity_factor)."""
+        cap = capacity_slots(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
         return cls.make(w.T, w.d, w.f, w.E, w.k, w.score, w.renorm, w.n_group, w.topk_group,
-                        w.f_shared, w.act, w.wdt)
+                        w.f_shared, w.act, w.wdt, cap)
 
 
 _LIB: Optional[ctypes.CDLL] = None

@@ -7,7 +7,8 @@
 // Communication, Overlap and Load Balance", Figure 2) and of "Expert-Parallel
 // MoE Inference: Serving Sparse Models at Scale" (section "Deeper Analysis",
 // Figure 2).  No atomics: a token gathers its own k rows through inv_pos, so
-// the result is deterministic.  The sum runs j = 0..k-1, then the shared row.
+// the result is deterministic.  The sum runs j = 0..k-1, then the shared row;
+// an assignment dropped for capacity (inv_pos = -1) contributes nothing.
 // One block per token row; 16-byte loads and stores, HBM-bound.
 #include "moe_internal.hpp"
 
@@ -32,6 +33,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   for (int v = threadIdx.x; v < nvec; v += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < a.k; ++j) {
+      if (s_row[j] < 0) continue;  // dropped for capacity: no contribution
       const u32x4 r = y[(size_t)s_row[j] * nvec + v];
       const float g = s_g[j];
 #pragma unroll
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineArgs a) {
   for (int v = threadIdx.x; v < nvec; v += 256) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < a.k; ++j) {
+      if (s_row[j] < 0) continue;  // dropped for capacity: no contribution
       const f32x4 r = y[(size_t)s_row[j] * nvec + v];
       const float g = s_g[j];
 #pragma unroll

@@ -62,9 +62,10 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunk
       *p = run;
       run += v;
     }
-    a.counts[e] = run;
+    a.counts[e] = run;  // the demand; the rows kept are min(run, cap)
   }
-  tot[e] = (e < a.E) ? run : 0;
+  const int kept = (e < a.E) ? min(run, a.cap) : 0;
+  tot[e] = kept;
   __syncthreads();
   // inclusive Hillis-Steele scan over kMaxE entries
   for (int off = 1; off < kMaxE; off <<= 1) {
@@ -73,15 +74,15 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunk
     tot[e] += v;
     __syncthreads();
   }
-  const int excl = tot[e] - ((e < a.E) ? run : 0);
+  const int excl = tot[e] - kept;
   if (e < a.E) a.offsets[e] = excl;  // the scatter adds it to the relative chunk bases
   if (e == a.E - 1) a.offsets[a.E] = tot[e];
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
-  __shared__ int next_row[kMaxE];
+  __shared__ int next_row[kMaxE];  // rank within the expert of the chunk's next assignment
   const int lane = threadIdx.x;
-  for (int e = lane; e < a.E; e += 64) next_row[e] = a.offsets[e] + a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
+  for (int e = lane; e < a.E; e += 64) next_row[e] = a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
   __syncthreads();
   const int base = blockIdx.x * kDispatchChunk;
   const int end = min(base + kDispatchChunk, a.n_assign);
@@ -98,25 +99,33 @@ __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
       same &= bit ? m : ~m;
     }
     const int rank = __popcll(same & below);
-    const int row = valid ? next_row[e] + rank : 0;
+    const int rel = valid ? next_row[e] + rank : 0;  // earlier assignments to e
     __syncthreads();  // every lane has read next_row before any update
     const bool last = (same >> lane) == 1ull;  // highest lane of its group
-    if (valid && last) next_row[e] = row + 1;
+    if (valid && last) next_row[e] = rel + 1;
     __syncthreads();
     if (valid) {
-      a.inv_pos[i] = row;
-      a.perm_token[row] = i / a.k;
+      if (rel < a.cap) {  // a free slot of its expert
+        const int row = a.offsets[e] + rel;
+        a.inv_pos[i] = row;
+        a.perm_token[row] = i / a.k;
+      } else {
+        a.inv_pos[i] = -1;  // the expert is full: dropped
+      }
     }
   }
 }
 
 // x_perm[p][:] = x[perm_token[p]][:], 16-byte vectors; one block per 8 rows.
+// rows_dev (device, nullable): the number of rows actually laid out
+// (offsets[E]), at most `rows`; rows past it are left untouched.
 __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x,
                                                      const int32_t* __restrict__ perm,
-                                                     int rows, int vec_per_row,
-                                                     u32x4* __restrict__ out) {
+                                                     int rows, const int32_t* __restrict__ rows_dev,
+                                                     int vec_per_row, u32x4* __restrict__ out) {
   const int r0 = blockIdx.x * 8;
-  for (int r = r0; r < min(r0 + 8, rows); ++r) {
+  const int n = rows_dev ? min(*rows_dev, rows) : rows;
+  for (int r = r0; r < min(r0 + 8, n); ++r) {
     const size_t src = (size_t)perm[r] * vec_per_row;
     const size_t dst = (size_t)r * vec_per_row;
     for (int v = threadIdx.x; v < vec_per_row; v += 256) out[dst + v] = x[src + v];
@@ -143,11 +152,11 @@ hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, int row_bytes,
-                              void* x_perm, hipStream_t s) {
+hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
+                              int row_bytes, void* x_perm, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_kernel, dim3((rows + 7) / 8), dim3(256), 0, s,
-                     (const u32x4*)x, perm_token, rows, row_bytes / 16, (u32x4*)x_perm);
+                     (const u32x4*)x, perm_token, rows, rows_dev, row_bytes / 16, (u32x4*)x_perm);
   return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ moe_status check_desc(const moe_desc* d) {
   if (d->E > kMaxE || d->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (d->d % 128 != 0 || d->f % 128 != 0 || d->f_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (int64_t(d->T) * d->k >= kMaxAssign) return MOE_ERR_UNSUPPORTED;
+  if (d->capacity < 0) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -237,10 +238,13 @@ moe_status run_route(const moe_desc* d, const void* x, const void* wr, const flo
 moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, int32_t* counts,
                         int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
                         const DispatchWs& ws, hipStream_t s) {
-  DispatchArgs a{idx, int(n_assign(d)), d->E, d->k, ws.chunk_cnt, counts, offsets, perm_token, inv_pos};
+  DispatchArgs a{idx, int(n_assign(d)), d->E, d->k, ws.chunk_cnt, counts, offsets, perm_token, inv_pos,
+                 d->capacity > 0 ? d->capacity : INT32_MAX};
   MOE_TRY(dev(launch_dispatch_index(a, s)));
   if (x_perm == nullptr) return MOE_OK;  // fused gather: GEMM1 reads x through perm_token
-  return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), int(d->d * act_bytes(d)), x_perm, s));
+  // the gather stops at offsets[E] (the rows kept), read on the device
+  return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), offsets + d->E, int(d->d * act_bytes(d)),
+                                x_perm, s));
 }
 
 // Optional shared-expert segment of the routed launches (see fuse_shared).
@@ -476,7 +480,7 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d->T == 0) {  // nothing routed: counts are all zero
-    DispatchArgs a{nullptr, 0, d->E, d->k, nullptr, counts, nullptr, nullptr, nullptr};
+    DispatchArgs a{nullptr, 0, d->E, d->k, nullptr, counts, nullptr, nullptr, nullptr, INT32_MAX};
     return dev(launch_dispatch_index(a, s));
   }
   Carve c(ws);

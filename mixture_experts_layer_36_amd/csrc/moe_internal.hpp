@@ -65,12 +65,14 @@ struct DispatchArgs {
   int32_t* offsets;         // [E+1]
   int32_t* perm_token;      // [n_assign]
   int32_t* inv_pos;         // [n_assign]
+  int cap;                  // slots per expert (INT32_MAX: dropless)
 };
 hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
 
-// x_perm[p] = x[perm_token[p]], rows of row_bytes (multiple of 16).
-hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, int row_bytes,
-                              void* x_perm, hipStream_t s);
+// x_perm[p] = x[perm_token[p]] for p < min(rows, *rows_dev) (rows_dev: device
+// row count, nullable), rows of row_bytes (multiple of 16).
+hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
+                              int row_bytes, void* x_perm, hipStream_t s);
 
 // Combine.
 struct CombineArgs {

@@ -31,6 +31,7 @@ class Workload:
     act: str          # activation storage: "f32" | "bf16"
     wdt: str          # expert-weight storage: "f32" | "bf16" | "e4m3"
     bias_scale: float  # router bias b_e = -bias_scale * ln(rank_e); 0 = no bias
+    capacity_factor: float = 0.0  # 0 = dropless; else slots = ceil(cf * T * k / E)
 
     @property
     def assignments(self) -> int:

@@ -40,8 +40,11 @@ def oracle_layer(L: LayerInputs, tokens=None) -> O.LayerResult:
             cache[e] = O.adapters.decoded_expert(L, e)
         return cache[e]
 
-    return O.layer_forward(x, wr, b, O.workload_spec(L.w), L.w.E, ew, L.w.act,
-                           O.adapters.decoded_shared(L))
+    w = L.w
+    cap = O.expert_capacity(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
+    assert tokens is None or cap == 0, "a capacity couples the tokens: no subsets"
+    return O.layer_forward(x, wr, b, O.workload_spec(w), w.E, ew, w.act,
+                           O.adapters.decoded_shared(L), capacity=cap)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
@@ -92,7 +95,8 @@ def assert_dispatch(idx, counts, offsets, perm_token, inv_pos, ref: O.LayerResul
     tolerated order swap within a token's k experts maps consistently."""
     assert np.array_equal(counts, ref.counts), "counts"
     assert np.array_equal(offsets, ref.offsets), "offsets"
-    assert np.array_equal(perm_token, ref.perm_token), "perm_token"
+    n = len(ref.perm_token)  # rows kept (all T*k when dropless)
+    assert np.array_equal(perm_token[:n], ref.perm_token), "perm_token"
     T, k = ref.topk_idx.shape
     got = inv_pos.reshape(T, k)
     want = ref.inv_pos.reshape(T, k)

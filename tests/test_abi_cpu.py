@@ -56,6 +56,8 @@ def test_status_strings():
     (dict(n_group=8, topk_group=1), moe.MOE_ERR_INVALID),   # groups of 1
     (dict(n_group=4, topk_group=1, k=3), moe.MOE_ERR_INVALID),  # 1 group of 2 < k
     (dict(n_group=4, topk_group=2, k=3), moe.MOE_OK),
+    (dict(capacity=5), moe.MOE_OK),
+    (dict(capacity=-1), moe.MOE_ERR_INVALID),
 ])
 def test_validate(kw, code):
     assert moe.validate(_good(**kw)) == code
@@ -120,3 +122,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(ImportError):
         moe.validate(_good())
+
+
+def test_capacity_slots_match_the_oracle():
+    """The binding's slot count (host logic of the product) against the
+    oracle's own rounding of capacity_factor * T * k / E."""
+    import oracle as O
+    for cf, T, k, E in ((1.0, 512, 8, 256), (1.25, 512, 8, 256), (1.1, 512, 8, 256), (0.1, 10, 1, 1),
+                        (1.3, 4096, 2, 8), (0, 100, 2, 4), (-2, 100, 2, 4), (2, 7, 3, 5)):
+        assert moe.capacity_slots(cf, T, k, E) == O.expert_capacity(cf, T, k, E), (cf, T, k, E)

@@ -42,6 +42,14 @@ CASES = {
     # gate-up tiles, and a 128-wide down-projection tile (d = 384)
     "qwen_fp8_big": QWEN_FP8_SKEW.scaled(T=800, d=512, f=384, E=16, k=4),
     "qwen_fp8_big_n128": QWEN_FP8_SKEW.scaled(T=600, d=384, f=256, E=8, k=4),
+    # expert capacity (overflow dropped): every GEMM path and the shared expert
+    "mixtral_cap": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384, capacity_factor=1.0),
+    "mixtral_big_cap": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6, capacity_factor=1.0),
+    "dsv3_skew_cap": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128,
+                                             capacity_factor=1.0),
+    "decode_cap": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, capacity_factor=1.0),
+    "qwen_fp8_cap": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32, capacity_factor=1.25),
+    "tiny_f32_cap": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3, capacity_factor=0.75),
 }
 
 _CACHE = {}
@@ -108,15 +116,16 @@ def test_stages_chain(name):
     torch.cuda.synchronize()
     assert_dispatch(idx.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(),
                     perm.cpu().numpy(), inv.cpu().numpy(), ref)
-    assert torch.equal(x_perm, dev.x[perm.long()])  # bitwise row copies
+    n = int(offsets[-1])  # rows laid out: T*k, or fewer with a capacity
+    assert torch.equal(x_perm[:n], dev.x[perm[:n].long()])  # bitwise row copies
 
     h = torch.empty((A, w.f), dtype=dev.x.dtype, device="cuda")
     y = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
     moe.grouped_ffn(desc, x_perm, offsets, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3, dev.s2, h, y,
                     moe.workspace(desc, moe.STAGE_FFN))
     torch.cuda.synchronize()
-    eh = assert_values(from_torch(h, w.act), ref.h, w, "h")
-    ey = assert_values(from_torch(y, w.act), ref.y_perm, w, "y_perm")
+    eh = assert_values(from_torch(h[:n], w.act), ref.h, w, "h")
+    ey = assert_values(from_torch(y[:n], w.act), ref.y_perm, w, "y_perm")
 
     out = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
     moe.combine(desc, y, inv, gw, None, out)
@@ -175,7 +184,7 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
-                                  "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big"])
+                                  "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big", "dsv3_skew_cap"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
