@@ -88,6 +88,74 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
+# --------------------------------------------------------------------------
+# fp8 dispatch payload (block-scaled E4M3)
+# --------------------------------------------------------------------------
+
+FP8_BLOCK = 32      # elements of a row sharing one scale
+E4M3_MAX = 448.0
+
+
+def _rne_e4m3_magnitude(v: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3 magnitude code (ties to even) of 0 <= v <= 448: normal
+    codes hold (1 + m/8) * 2^(e-7) for exponent field e = 1..15, subnormal
+    codes m * 2^-9.  Written from the format, step by step."""
+    v = np.asarray(v, dtype=np.float64)
+    code = np.zeros(v.shape, dtype=np.int64)
+    nz = v > 0
+    _, ex = np.frexp(np.where(nz, v, 1.0))          # v = f * 2^ex, f in [0.5, 1)
+    e_unb = ex - 1                                   # v in [2^e_unb, 2^(e_unb+1))
+    normal = nz & (e_unb >= -6)
+    # normal: v / 2^(e_unb - 3) in [8, 16) -> round to an integer in [8, 16]
+    q = np.rint(np.where(normal, np.ldexp(v, -(e_unb - 3)), 0.0)).astype(np.int64)
+    carry = q == 16                                  # rounded up into the next binade
+    e_field = np.where(carry, e_unb + 8, e_unb + 7)
+    mant = np.where(carry, 0, q - 8)
+    code = np.where(normal, (e_field << 3) | mant, code)
+    # subnormal: v / 2^-9 in [0, 8) -> integer 0..8 (8 is the smallest normal, code 8)
+    sub = nz & (e_unb < -6)
+    qs = np.rint(np.where(sub, np.ldexp(v, 9), 0.0)).astype(np.int64)
+    code = np.where(sub, qs, code)
+    return code
+
+
+def quantize_fp8_blocks(x: np.ndarray, block: int = FP8_BLOCK):
+    """The fp8 dispatch payload: each row cut into blocks of `block` elements;
+    a block with largest magnitude amax gets the power-of-two scale 2^s with s
+    the smallest integer such that amax <= 448 * 2^s (no element saturates),
+    stored as an E8M0 byte (s + 127, s clamped to [-127, 127]; an all-zero
+    block gets s = 0); its elements become E4M3 codes of x / 2^s rounded to
+    nearest, ties to even.  ("Tensor vs Expert vs Data Parallelism for MoE
+    Serving", section "Deeper Analysis", Figure 2: dispatch sends FP8 token
+    copies, combine returns BF16.)  Returns codes uint8 [rows][d] and scales
+    uint8 [rows][d / block]."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, d = x.shape
+    xb = x.reshape(rows, d // block, block)
+    amax = np.abs(xb).max(axis=2)
+    s = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    # smallest s with amax <= 448 * 2^s: start from 2^s ~ amax / 448 and step
+    s0 = np.floor(np.log2(np.where(nz, amax, 1.0) / E4M3_MAX)).astype(np.int64) - 1
+    for _ in range(4):
+        up = nz & (np.ldexp(E4M3_MAX, s0) < amax)
+        s0 = np.where(up, s0 + 1, s0)
+    s = np.where(nz, np.clip(s0, -127, 127), 0)
+    v = np.abs(xb) * np.ldexp(1.0, -s)[:, :, None]
+    mag = _rne_e4m3_magnitude(v)
+    sign = (xb < 0).astype(np.int64) << 7
+    codes = np.where(mag == 0, 0, mag | sign).reshape(rows, d).astype(np.uint8)
+    return codes, (s + 127).astype(np.uint8)
+
+
+def dequantize_fp8_blocks(codes: np.ndarray, scales: np.ndarray, block: int = FP8_BLOCK) -> np.ndarray:
+    """Values of a block-scaled E4M3 payload: code value * 2^(scale - 127)."""
+    v = e4m3_to_f64(codes)
+    rows, d = v.shape
+    e = np.asarray(scales, dtype=np.int64) - 127
+    return (v.reshape(rows, d // block, block) * np.ldexp(1.0, e)[:, :, None]).reshape(rows, d)
+
+
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
@@ -372,16 +440,20 @@ class LayerResult:
 
 
 def layer_forward(x, w_router, bias, spec: RouteSpec, E: int, expert_weights: ExpertFn, act: str,
-                  shared: Optional[Sequence[np.ndarray]] = None, capacity: int = 0) -> LayerResult:
+                  shared: Optional[Sequence[np.ndarray]] = None, capacity: int = 0,
+                  fp8_dispatch: bool = False) -> LayerResult:
     """The whole layer: route, dispatch, grouped SwiGLU FFN, shared expert,
     combine.  x, w_router and the weights are float64 values of the stored
     inputs.  Without a capacity the layer is token-wise: running it on a
     subset of the tokens gives exactly those tokens' results.  With a
     capacity (slots per expert) overflow assignments are dropped and the
-    kept ones keep their gates."""
+    kept ones keep their gates.  With fp8_dispatch the dispatched rows are the
+    block-scaled E4M3 payload of x (quantize_fp8_blocks) as the routed
+    experts' input; the router and the shared expert read x itself."""
     idx, gw, _ = route(x, w_router, bias, spec)
     counts, offsets, perm_token, inv_pos = dispatch(idx, E, capacity)
-    x_perm = gather_rows(x, perm_token)
+    payload = dequantize_fp8_blocks(*quantize_fp8_blocks(x)) if fp8_dispatch else x
+    x_perm = gather_rows(payload, perm_token)
     h, y_perm = grouped_ffn(x_perm, offsets, expert_weights, act)
     sh = sy = None
     if shared is not None:

@@ -448,12 +448,64 @@ def check_capacity():
     assert np.array_equal(got.out, O.round_act(want, "f32"))  # same j order, same rounding
 
 
+def _nearest_code_bruteforce(v):
+    """Exhaustive nearest E4M3 code of one magnitude, ties to the even mantissa."""
+    best = None
+    for c in range(0x7F):  # non-negative finite codes
+        val = O.E4M3_VALUES[c]
+        dist = abs(val - v)
+        if best is None or dist < best[0] or (dist == best[0] and (c & 1) == 0):
+            best = (dist, c)
+    return best[1]
+
+
+def check_fp8_payload():
+    rng = np.random.default_rng(31)
+    # magnitudes over the whole range, exact codes, ties and subnormals
+    vals = np.concatenate([rng.uniform(0, 448, 300), O.E4M3_VALUES[:0x7F],
+                           (O.E4M3_VALUES[1:0x7F] + O.E4M3_VALUES[:0x7E]) / 2,
+                           rng.uniform(0, 2.0 ** -6, 60)])
+    got = M._rne_e4m3_magnitude(vals)
+    for v, c in zip(vals, got):
+        assert c == _nearest_code_bruteforce(v), (v, c)
+    # rows of blocks at very different scales, with a zero block
+    x = O.round_bf16(rng.standard_normal((6, 128)) * np.repeat([1e-4, 3.0, 700.0, 0.0], 32))
+    codes, scales = O.quantize_fp8_blocks(x)
+    assert codes.shape == x.shape and scales.shape == (6, 4)
+    s = scales.astype(np.int64) - 127
+    amax = np.abs(x.reshape(6, 4, 32)).max(axis=2)
+    nz = amax > 0
+    assert (np.ldexp(448.0, s)[nz] >= amax[nz]).all()            # nothing saturates
+    assert (np.ldexp(448.0, s - 1)[nz] < amax[nz]).all()         # and s is the smallest such
+    assert (scales[~nz] == 127).all() and (codes.reshape(6, 4, 32)[~nz] == 0).all()
+    deq = O.dequantize_fp8_blocks(codes, scales)
+    # each element is its nearest representable (per-block scale), i.e. within half a step
+    v = np.abs(x.reshape(6, 4, 32)) * np.ldexp(1.0, -s)[:, :, None]
+    for (r, b, i), vv in np.ndenumerate(v):
+        assert codes.reshape(6, 4, 32)[r, b, i] & 0x7F == _nearest_code_bruteforce(vv)
+    assert np.array_equal(np.sign(deq), np.sign(x))
+    # sign symmetry and exact round trip of representable payloads
+    c2, s2 = O.quantize_fp8_blocks(-x)
+    assert np.array_equal(s2, scales) and np.array_equal(c2[codes != 0], codes[codes != 0] ^ 0x80)
+    # a payload's values are representable, so requantising returns them exactly
+    # (the scale may step down when a block's largest element rounded down to
+    # 224 * 2^s, so codes need not repeat; values do)
+    assert np.array_equal(O.dequantize_fp8_blocks(*O.quantize_fp8_blocks(deq)), deq)
+    # layer special case: on a representable payload the fp8 dispatch changes nothing
+    T, d, f, E, k = 6, 128, 32, 4, 2
+    W = _weights(rng, E, d, f)
+    wr = rng.standard_normal((E, d))
+    ref = O.layer_forward(deq, wr, None, O.RouteSpec(k=k), E, lambda e: W[e], "f32")
+    got = O.layer_forward(deq, wr, None, O.RouteSpec(k=k), E, lambda e: W[e], "f32", fp8_dispatch=True)
+    assert np.array_equal(got.out, ref.out)
+
+
 CHECKS = [check_bf16_round, check_decoders, check_router_logits, check_scores,
           check_topk_bruteforce, check_k1_argmax, check_constructed_ties, check_group_limit,
           check_gates, check_worked_example_counts, check_ep_sizing_and_batch, check_dispatch,
           check_gather, check_dense_special_case, check_identical_experts_closed_form,
           check_uniform_gates_mean, check_combine, check_locality, check_margin_rule,
-          check_capacity]
+          check_capacity, check_fp8_payload]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -537,6 +589,27 @@ def _m_capacity_keeps_last(topk_idx, E, capacity=0):
     return c, o, p, i
 
 
+_RNE_E4M3 = M._rne_e4m3_magnitude
+_QUANT_FP8 = M.quantize_fp8_blocks
+
+
+def _m_e4m3_truncate(v):
+    """Rounds toward zero instead of to nearest."""
+    c = _RNE_E4M3(v)
+    back = M.E4M3_VALUES[c]
+    return np.where(back > np.asarray(v, dtype=np.float64), c - 1, c)
+
+
+def _m_fp8_scale_low(x, block=32):
+    """Takes a scale one power of two too small (the largest elements saturate)."""
+    codes, scales = _QUANT_FP8(x, block)
+    scales = scales - 1
+    v = np.asarray(x, dtype=np.float64).reshape(x.shape[0], -1, block) * np.ldexp(1.0, -(scales.astype(np.int64) - 127))[:, :, None]
+    mag = np.minimum(_RNE_E4M3(np.minimum(np.abs(v), 448.0)), 0x7E)
+    codes = (mag | ((v < 0).astype(np.int64) << 7)).reshape(x.shape).astype(np.uint8)
+    return codes, scales
+
+
 def _m_combine_wrong_index(y_perm, inv_pos, topk_w, act, shared_y=None):
     T, k = topk_w.shape
     out = np.zeros((T, y_perm.shape[1]))
@@ -566,6 +639,8 @@ MUTATIONS = [
     ("combine", _m_combine_wrong_index),
     ("dispatch", _m_capacity_off_by_one),
     ("dispatch", _m_capacity_keeps_last),
+    ("_rne_e4m3_magnitude", _m_e4m3_truncate),
+    ("quantize_fp8_blocks", _m_fp8_scale_low),
     ("round_bf16", _m_round_truncate),
 ]
 
