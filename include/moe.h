@@ -90,7 +90,30 @@ typedef struct {
                          capacity_factor * T * k / E, rounded up by the caller.
                          Assignments claim slots in increasing a = t*k + j; one
                          that finds its expert full is dropped (contributes 0) */
+  int32_t dispatch_fp8; /* 0: the dispatched rows are x itself (act dtype);
+                         1: they are the block-scaled E4M3 payload of x (act
+                         must be MOE_BF16; see "fp8 dispatch payload" below).
+                         The router and the shared expert always read x.    */
 } moe_desc;
+
+/* fp8 dispatch payload (dispatch_fp8 = 1).  Each row of x is cut into blocks
+ * of 32 elements; a block with largest magnitude amax gets the scale 2^s, s
+ * the smallest integer with amax <= 448 * 2^s (so nothing saturates), clamped
+ * to [-127, 127], and s = 0 for an all-zero block; its elements become OCP
+ * E4M3 codes of x / 2^s rounded to nearest, ties to even (a value that rounds
+ * to zero is +0).  The experts see code value * 2^s.  DeepSeek's serving
+ * system dispatches FP8 token copies and combines in BF16 ("Tensor vs Expert
+ * vs Data Parallelism for MoE Serving", section "Deeper Analysis", Figure 2);
+ * the 32-element power-of-two scale is the block the gfx950 block-scaled MFMA
+ * consumes.  A payload of R rows is one buffer of
+ *   MOE_FP8_PAYLOAD_BYTES(R, d) bytes:
+ *   codes  uint8 [R][d]                at byte 0
+ *   scales uint8 [R][MOE_FP8_SCALE_STRIDE(d)], E8M0 (byte = s + 127), at
+ *          byte MOE_FP8_SCALES_OFFSET(R, d); block b of row r at r*stride + b. */
+#define MOE_FP8_SCALE_STRIDE(d) ((((size_t)(d) / 32) + 15) / 16 * 16)
+#define MOE_FP8_SCALES_OFFSET(R, d) (((size_t)(R) * (size_t)(d) + 255) / 256 * 256)
+#define MOE_FP8_PAYLOAD_BYTES(R, d) \
+  (MOE_FP8_SCALES_OFFSET(R, d) + (size_t)(R) * MOE_FP8_SCALE_STRIDE(d))
 
 /* Number of hipEvents moe_layer_forward records when given a trace array. */
 #define MOE_TRACE_EVENTS 7
@@ -134,7 +157,9 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
  *                    that number reaches the capacity (dropped)   int32 [T*k]
  *   perm_token[p]  = token of row p (so perm_token[inv_pos[a]] = a / k),
  *                    for p < offsets[E]                            [T*k]
- *   x_perm[p][:]   = x[perm_token[p]][:], p < offsets[E]  act dtype [T*k][d]
+ *   x_perm[p][:]   = x[perm_token[p]][:], p < offsets[E]  act dtype [T*k][d];
+ *                    with dispatch_fp8 the payload of those rows, R = T*k
+ *                    (MOE_FP8_PAYLOAD_BYTES(T*k, d) bytes)
  * Rows of one expert are contiguous and in increasing token order; the result
  * is deterministic.  topk_idx entries must lie in [0, E).  The capacity slots
  * are those of "Expert-Parallel MoE Inference", section "Capacity factor and
@@ -147,7 +172,8 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const voi
                         void* stream);
 
 /* Grouped expert FFN over the expert-contiguous rows.  Expert e transforms
- * rows [offsets[e], offsets[e+1]) of x_perm:
+ * rows [offsets[e], offsets[e+1]) of x_perm (act dtype [T*k][d], or with
+ * dispatch_fp8 the payload of T*k rows as moe_dispatch writes it):
  *   u = x W1_e^T, v = x W3_e^T (fp32 accumulate, times s1/s3 for fp8),
  *   h = silu(u) * v   stored in the act dtype                    [T*k][f]
  *   y = h W2_e^T      (times s2 for fp8) stored in the act dtype [T*k][d]

@@ -6,6 +6,7 @@ arguments; see _lib.py.
 from ._lib import (  # noqa: F401
     BF16, EXPORTS, F32, FP8_E4M3, LIB_PATH, MOE_ERR_DEVICE, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_OK, SIGMOID, SOFTMAX, STAGE_DISPATCH, STAGE_FFN, STAGE_LAYER,
-    STAGE_ROUTE, TRACE_EVENTS, TRACE_STAGES, Desc, MoeError, capacity_slots, combine, dispatch, grouped_ffn,
-    layer_forward, loaded_path, route, validate, workspace, workspace_size,
+    STAGE_ROUTE, TRACE_EVENTS, TRACE_STAGES, Desc, MoeError, capacity_slots, combine, dispatch,
+    fp8_payload_bytes, fp8_payload_views, fp8_scale_stride, fp8_scales_offset, grouped_ffn, layer_forward,
+    loaded_path, route, validate, workspace, workspace_size,
 )

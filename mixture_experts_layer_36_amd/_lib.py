@@ -53,22 +53,46 @@ def capacity_slots(capacity_factor, T: int, k: int, E: int) -> int:
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "f", "E", "k", "score", "renorm", "n_group", "topk_group",
-                 "f_shared", "act", "wdtype", "capacity")]
+                 "f_shared", "act", "wdtype", "capacity", "dispatch_fp8")]
 
     @classmethod
     def make(cls, T, d, f, E, k, score="softmax", renorm=True, n_group=0, topk_group=0,
-             f_shared=0, act="bf16", wdtype="bf16", capacity=0) -> "Desc":
+             f_shared=0, act="bf16", wdtype="bf16", capacity=0, dispatch_fp8=False) -> "Desc":
         return cls(T, d, f, E, k, SOFTMAX if score == "softmax" else SIGMOID, int(bool(renorm)),
-                   n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype], capacity)
+                   n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype], capacity,
+                   int(bool(dispatch_fp8)))
 
     @classmethod
     def from_attrs(cls, w) -> "Desc":
         """From any object with T, d, f, E, k, score, renorm, n_group,
         topk_group, f_shared, act and wdt attributes (and optionally
-        capacity_factor)."""
+        capacity_factor and dispatch_fp8)."""
         cap = capacity_slots(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
         return cls.make(w.T, w.d, w.f, w.E, w.k, w.score, w.renorm, w.n_group, w.topk_group,
-                        w.f_shared, w.act, w.wdt, cap)
+                        w.f_shared, w.act, w.wdt, cap, getattr(w, "dispatch_fp8", False))
+
+
+# The fp8 dispatch payload of R rows of width d (moe.h): E4M3 codes [R][d] at
+# byte 0, E8M0 scales [R][scale_stride(d)] at byte scales_offset(R, d).
+def fp8_scale_stride(d: int) -> int:
+    return (d // 32 + 15) // 16 * 16
+
+
+def fp8_scales_offset(R: int, d: int) -> int:
+    return (R * d + 255) // 256 * 256
+
+
+def fp8_payload_bytes(R: int, d: int) -> int:
+    return fp8_scales_offset(R, d) + R * fp8_scale_stride(d)
+
+
+def fp8_payload_views(buf: torch.Tensor, R: int, d: int):
+    """(codes [R][d], scales [R][d/32]) views of a uint8 payload buffer."""
+    st = fp8_scale_stride(d)
+    off = fp8_scales_offset(R, d)
+    codes = buf[:R * d].view(R, d)
+    scales = buf[off:off + R * st].view(R, st)[:, :d // 32]
+    return codes, scales
 
 
 _LIB: Optional[ctypes.CDLL] = None

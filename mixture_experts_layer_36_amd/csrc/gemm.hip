@@ -329,6 +329,7 @@ hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
 // least 1024 tokens, go to the direct-to-LDS 256-row kernel; the rest use
 // 128-row tiles.
 static bool use_big(const GemmArgs& a) {
+  if (a.act == GD_FP8) return gemm_fp8_act_ok(a);
   if (a.act != GD_BF16 || a.wdt == GD_F32) return false;
   // router logits: worth a 256-wide tile only with at least 128 experts
   if (a.epi == EPI_BIAS_F32) return a.wdt == GD_BF16 && a.tile_table == nullptr && a.rows >= 1024 && a.N >= 128;
@@ -342,6 +343,16 @@ static bool use_decode(const GemmArgs& a) {
   if (a.act != GD_BF16 || a.wdt != GD_BF16 || a.epi == EPI_BIAS_F32) return false;
   if (a.offsets == nullptr || a.E <= 0) return false;
   return a.rows <= 32 * a.E;
+}
+
+// fp8 activations (the block-scaled dispatch payload) run only on the 256-row
+// kernel's fp8 x fp8 gate-up path: the same shapes it takes with bf16
+// activations, so the tile height matches the down projection's.
+bool gemm_fp8_act_ok(const GemmArgs& a) {
+  if (a.wdt != GD_FP8 || a.epi != EPI_SWIGLU || a.sh_rows > 0) return false;
+  if (a.K % 64 != 0 || a.a_sstride % 16 != 0 || a.a_sstride * 32 < a.K) return false;
+  const int segs = a.E > 0 ? a.E : 1;
+  return a.rows >= 1024 && a.rows / segs >= 128;
 }
 
 int gemm_block_m(const GemmArgs& a) {
@@ -362,6 +373,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       default: return launch_f32<EPI_BIAS_F32>(a, s);
     }
   }
+  if (a.act == GD_FP8 && (!gemm_fp8_act_ok(a) || a.a_scales == nullptr)) return hipErrorInvalidValue;
   if (use_decode(a)) return launch_gemm_decode(a, s);
   if (use_big(a)) return launch_gemm_big(a, s);
   return a.wdt == GD_FP8 ? launch_mfma_epi<GD_FP8>(a, s) : launch_mfma_epi<GD_BF16>(a, s);

@@ -27,6 +27,9 @@
 //     one 4-column run per work unit), so the result is deterministic
 //     (the down projection of a Mixtral-shaped layer has 2.25 waves of
 //     tiles, so without this its last wave would run a quarter full);
+//   * with the fp8 dispatch payload as activations and E4M3 weights, the
+//     gate-up GEMM runs both operands in fp8 on the block-scaled MFMA
+//     (big_tile_fp8 below);
 //   * LDS rows of BK elements with 16-byte chunks XOR-swizzled by row
 //     ((r >> 2) & 3 for 64-byte rows, (r ^ (r >> 3)) & 7 for 128-byte rows):
 //     measured on gfx950 (64 banks; a 128-bit read is served 16 lanes at a
@@ -385,6 +388,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     mfmas(F[1]);
     interleave_refill();
   }
+  wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
 
   if (wk.slot >= 0) {
     // a K-piece: raw accumulators to its slot, register-major so that each
@@ -424,6 +428,299 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
 #endif
 }
 
+
+// ---------------------------------------------------------------------------
+// fp8 x fp8 gate-up tiles: activations are the block-scaled E4M3 dispatch
+// payload (codes, and one E8M0 scale per 32 k values of a row), weights are
+// E4M3 with per-output-channel fp32 scales.  v_mfma_scale_f32_32x32x64_f8f6f4
+// takes, per lane, 32 k values of one row of each operand (two 16-value
+// halves, one from each 32-value block, measured on gfx950) and one E8M0
+// scale per lane: lane half h's scale multiplies k-block h.  The activation
+// scale is that block's payload scale, the weight scale 2^0 (the channel
+// scales are applied in the epilogue as on the bf16 path).
+// Per k, an fp8 MFMA takes half the cycles and each operand half the bytes
+// of bf16, so a stage holds BK8 = 64 k values in the same 64-byte LDS rows
+// and the same ring of four 32 KB stages.  The activation scales come in
+// 16-byte chunks per row (16 blocks, 8 stages) through a two-slot LDS ring
+// refilled once per 8 stages; K-pieces of split tiles start on chunk
+// boundaries.
+//
+// A stage's 4 x 4 grid of 32x32 blocks runs in four quarters (weight half,
+// activation half): (lo, lo), (lo, hi), (hi, hi), (hi, lo).  The fragments
+// of the first quarter are in registers when the stage starts; the other
+// halves of this stage are read during the first two quarters, then every
+// wave passes the barrier (all of this stage read, the next stage landed)
+// and the next stage's lo halves are read during the last two, so LDS reads
+// stay spread over the MFMAs.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int BK8 = 64;            // k per stage of the fp8 x fp8 path
+[[maybe_unused]] constexpr int SC_STAGES = 8;       // stages per 16-byte chunk of scales
+[[maybe_unused]] constexpr int SC_BYTES = BM * 16;  // one chunk for every row of a tile
+
+// f(IC<I>{}) for I = B .. E-1, each with I a constant expression.
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Spread ND LDS reads and NV direct loads over the NM MFMAs of a quarter.
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void sched_quarter() {
+  constexpr int dpm = (ND + NM - 1) / NM, vpm = (NV + NM - 1) / NM;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (dpm > 0) __builtin_amdgcn_sched_group_barrier(0x100, dpm, 0);
+    if (vpm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vpm, 0);
+  }
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+template <int BN, int WN, int EPI, bool HALF>
+__device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
+                                             int ncol0, char* lds) {
+  using C = BigCfg<BN, WN, HALF>;
+  using M = BigMem<BN, WN, HALF, GD_BF16>;  // 64-byte rows on both operands: the bf16 stage geometry
+  static_assert(C::NTHR == BM, "one scale row per thread");
+  constexpr int TW2 = C::TW / 2, TA2 = C::TA / 2;
+  static_assert(TW2 >= 1 && TA2 >= 1, "quarters");
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = sg.K;  // bytes per row of either operand
+  // this block's chunks of 8 stages: all, or piece k0num of s
+  const int KT_all = K / BK8, NCK = (KT_all + SC_STAGES - 1) / SC_STAGES;
+  const int ck0 = wk.k0num * NCK / wk.s, ck1 = (wk.k0num + 1) * NCK / wk.s;
+  const int kt0 = ck0 * SC_STAGES, KT = min(ck1 * SC_STAGES, KT_all) - kt0, NC = ck1 - ck0;
+
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K, kBufferFlags)
+              : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K), (short)0, ti.nrows * K,
+                                                  kBufferFlags);
+  uint32_t a_off[M::A_LOADS];
+#pragma unroll
+  for (int j = 0; j < M::A_LOADS; ++j) {
+    const int s = (wave * M::A_LOADS + j) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ swz(r);
+    const int rr = min(r, ti.nrows - 1);
+    const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
+    a_off[j] = (uint32_t)(ar * K + c * 16);
+  }
+  const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : min(BN, sg.N - ncol0);
+  const size_t b_start = (size_t)ncol0 * K;
+  const __amdgpu_buffer_rsrc_t b0_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(sg.B0 + b_start), (short)0, b_rows * K, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K, kBufferFlags);
+  uint32_t b_off[M::B_LOADS];
+  bool b_w3[M::B_LOADS];
+#pragma unroll
+  for (int j = 0; j < M::B_LOADS; ++j) {
+    const int s = (wave * M::B_LOADS + j) * 64 + lane;
+    const int r = s / CH, c = (s % CH) ^ swz(r);
+    int n = r;
+    b_w3[j] = false;
+    if (EPI == EPI_SWIGLU) {
+      const int half = C::RW / 2;
+      const int r0 = (wave * M::B_LOADS + j) * 64 / CH;
+      b_w3[j] = (r0 % C::RW) >= half;
+      n = (r / C::RW) * half + (r % C::RW) % half;
+    }
+    b_off[j] = (uint32_t)(n * K + c * 16);
+  }
+  // scales: thread t loads the chunk of tile row t (rows past the tile's
+  // end repeat its last row); waves past the loaded rows load nothing
+  const uint8_t* s_base = sg.amap ? a.a_scales : a.a_scales + (size_t)ti.row0 * a.a_sstride;
+  const int s_rows = sg.amap ? a.a_map_rows : ti.nrows;
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)s_base, (short)0, s_rows * a.a_sstride, kBufferFlags);
+  uint32_t s_off;
+  {
+    const int rr = min(tid, ti.nrows - 1);
+    const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
+    s_off = (uint32_t)(ar * a.a_sstride + ck0 * 16);
+  }
+  char* sring = lds + STAGES * M::STAGE_BYTES;
+
+  auto issue_part = [&](int kt, int buf, int part) {
+    char* st = lds + buf * M::STAGE_BYTES;
+    const int ks = kt0 + min(kt, KT - 1);
+    if (part == 0) {
+#pragma unroll
+      for (int j = 0; j < M::A_LOADS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * BK8, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < M::B_LOADS; ++j) {
+        const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
+        if (b_w3[j])
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * BK8, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * BK8, 0, 0);
+      }
+    }
+  };
+  auto issue_scales = [&](int c) {  // piece chunk c (clamped) into ring slot c & 1
+    if (wave * 64 < C::A_ROWS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(sring + (c & 1) * SC_BYTES + wave * 1024), 16,
+                                               s_off, min(c, NC - 1) * 16, 0, 0);
+  };
+
+  f32x16 acc[C::TW][C::TA];
+#pragma unroll
+  for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  const int arow = wave_arow<BN, WN, HALF>(wave);
+  // The lane's 32 bytes of an LDS row: the MFMA takes k values 16h..16h+15
+  // from bytes 0-15 and 32+16h..32+16h+15 from bytes 16-31 of lane half h
+  // (16-byte chunks h and h + 2 of the 64-k row), and lane half h's scale
+  // covers k-block h (k 32h..32h+31).
+  auto frag = [&](const char* base, int r) -> i32x8 {
+    const i32x4 p = *(const i32x4*)(base + 2 * lds_off(r, h));
+    const i32x4 q = *(const i32x4*)(base + 2 * lds_off(r, h + 2));
+    return __builtin_shufflevector(p, q, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto wfrag = [&](const char* L, int i) {
+    return frag(L + M::A_BYTES, wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31));
+  };
+  auto xfrag = [&](const char* L, int j) { return frag(L, arow + j * 32 + (lane & 31)); };
+  u32x4 SC[C::TA];  // this chunk's 16 scale bytes of each activation block's row
+  auto read_scales = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j)
+      SC[j] = *(const u32x4*)(sring + (c & 1) * SC_BYTES + (arow + j * 32 + (lane & 31)) * 16);
+  };
+  auto mf = [&](int i, int j, const i32x8& w, const i32x8& x, int sb) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, acc[i][j], 0, 0, 0, 127, 0, sb);
+  };
+
+  i32x8 WL[2][TW2], XL[2][TA2], WH[TW2], XH[TA2];
+  // prologue: scale chunk 0, stages 0..2 and the A part of stage 3
+  issue_scales(0);
+  issue_part(0, 0, 0); issue_part(0, 0, 1);
+  issue_part(1, 1, 0); issue_part(1, 1, 1);
+  issue_part(2, 2, 0); issue_part(2, 2, 1);
+  issue_part(3, 3, 0);
+  wait_vmcnt<2 * M::LOADS + M::A_LOADS>();  // scale chunk 0 and stage 0 done
+  barrier_only();
+  read_scales(0);
+#pragma unroll
+  for (int i = 0; i < TW2; ++i) WL[0][i] = wfrag(lds, i);
+#pragma unroll
+  for (int j = 0; j < TA2; ++j) XL[0][j] = xfrag(lds, j);
+
+  // Stage kt is in ring buffer kt % 4 = st % 4 (chunks are 8 stages), so
+  // every LDS address below is a constant offset.  Waits and refills are
+  // those of the bf16 pipeline; a scale chunk load adds one more load to
+  // some waits' windows, which only makes them wait a little longer.
+  for (int c = 0; c < NC; ++c) {
+    static_for<0, SC_STAGES>([&](auto ST) {
+      constexpr int st = decltype(ST)::value, p = st & 1;
+      const int kt = c * SC_STAGES + st;
+      if (kt >= KT) return;
+      const char* L = lds + (st % STAGES) * M::STAGE_BYTES;
+      const char* Ln = lds + ((st + 1) % STAGES) * M::STAGE_BYTES;
+      int sb[C::TA];
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j) sb[j] = (int)((SC[j][st >> 1] >> (16 * (st & 1) + 8 * h)) & 0xffu);
+      if (st == 0) issue_scales(c + 1);
+      // (lo, lo): read this stage's activation hi half; B part of stage kt+3
+      issue_part(kt + 3, (st + 3) % STAGES, 1);
+#pragma unroll
+      for (int j = 0; j < TA2; ++j) XH[j] = xfrag(L, TA2 + j);
+#pragma unroll
+      for (int i = 0; i < TW2; ++i)
+#pragma unroll
+        for (int j = 0; j < TA2; ++j) mf(i, j, WL[p][i], XL[p][j], sb[j]);
+      sched_quarter<TW2 * TA2, 2 * TA2, M::B_LOADS>();
+      __builtin_amdgcn_sched_barrier(0);
+      // (lo, hi): read this stage's weight hi half
+#pragma unroll
+      for (int i = 0; i < TW2; ++i) WH[i] = wfrag(L, TW2 + i);
+#pragma unroll
+      for (int i = 0; i < TW2; ++i)
+#pragma unroll
+        for (int j = 0; j < TA2; ++j) mf(i, TA2 + j, WL[p][i], XH[j], sb[TA2 + j]);
+      sched_quarter<TW2 * TA2, 2 * TW2, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      // this stage read everywhere, stage kt+1 resident: A part of stage
+      // kt+4 into this buffer
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      wait_vmcnt<2 * M::LOADS>();
+      barrier_only();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(kt + 4, st % STAGES, 0);
+      // (hi, hi): next stage's weight lo half
+#pragma unroll
+      for (int i = 0; i < TW2; ++i) WL[p ^ 1][i] = wfrag(Ln, i);
+#pragma unroll
+      for (int i = 0; i < TW2; ++i)
+#pragma unroll
+        for (int j = 0; j < TA2; ++j) mf(TW2 + i, TA2 + j, WH[i], XH[j], sb[TA2 + j]);
+      sched_quarter<TW2 * TA2, 2 * TW2, M::A_LOADS>();
+      __builtin_amdgcn_sched_barrier(0);
+      // (hi, lo): next stage's activation lo half (and, at a chunk's end,
+      // the next chunk's scales)
+#pragma unroll
+      for (int j = 0; j < TA2; ++j) XL[p ^ 1][j] = xfrag(Ln, j);
+      if (st == SC_STAGES - 1) read_scales(c + 1);
+#pragma unroll
+      for (int i = 0; i < TW2; ++i)
+#pragma unroll
+        for (int j = 0; j < TA2; ++j) mf(TW2 + i, j, WH[i], XL[p][j], sb[j]);
+      sched_quarter<TW2 * TA2, 2 * TA2 + (st == SC_STAGES - 1 ? C::TA : 0), 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
+
+  if (wk.slot >= 0) {
+    float4* P = (float4*)(a.partial + (size_t)wk.slot * (kPartialSlotBytes / 4));
+#pragma unroll
+    for (int i = 0; i < C::TW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TA; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    return;
+  }
+  store_tile<C::TW, C::TA, GD_FP8, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+}
+#endif
+
+template <int BN, int WN, int EPI>
+__global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_tiles, int kt_plan,
+                                                                    int n_cu) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, false, GD_BF16>::STAGE_BYTES +
+                                                     2 * SC_BYTES];
+  Work wk;
+  if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
+  TileInfo ti;
+  Seg sg;
+  if (!tile_info(a, wk.mt, BM, ti, sg)) return;
+  const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
+  if (ncol0 >= sg.N) return;
+  if (ti.nrows <= BM / 2)
+    big_tile_fp8<BN, WN, EPI, true>(a, ti, sg, wk, ncol0, lds);
+  else
+    big_tile_fp8<BN, WN, EPI, false>(a, ti, sg, wk, ncol0, lds);
+#endif
+}
 
 // Fixup of the split tiles, one float4 of the pieces' register layout per
 // work unit: unit ((i * TA + j) * 4 + g) * NTHR + t holds accumulator floats
@@ -522,13 +819,13 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int BN, int EPI, int WDT, int WN = MOE_BIG_WN>
+template <int BN, int EPI, int WDT, bool FP8ACT = false, int WN = MOE_BIG_WN>
 hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   GemmArgs a = a_in;
   const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
   const int ncol = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = (gemm_max_cols(a) + ncol - 1) / ncol;
-  const int kt_plan = (a.sh_rows > 0 ? min(a.K, a.shK) : a.K) / BK;
+  const int kt_plan = (a.sh_rows > 0 ? min(a.K, a.shK) : a.K) / (FP8ACT ? BK8 : BK);
   int n_cu = device_cus();
   if (a.ksplit < 1) a.ksplit = 1;
   if (n_cu <= 0 || n_cu % 8 != 0 || a.partial == nullptr || a.ksplit > 1) {
@@ -540,8 +837,12 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   // whole tiles plus at most one wave of pieces, 8 XCD shares rounded up
   int nb = n_slots * n_tiles + (n_cu > 0 ? n_cu + 8 : 0);
   nb = (nb + 7) & ~7;
-  hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb, a.ksplit), dim3(128 * WN), 0, s, a,
-                     n_tiles, kt_plan, n_cu);
+  if constexpr (FP8ACT)
+    hipLaunchKernelGGL((gemm_big_fp8_kernel<BN, WN, EPI>), dim3(nb), dim3(128 * WN), 0, s, a, n_tiles, kt_plan,
+                       n_cu);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb, a.ksplit), dim3(128 * WN), 0, s, a,
+                       n_tiles, kt_plan, n_cu);
   if (n_cu > 0)
     hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT>), dim3(n_cu / 2, kFixupChunks), dim3(256),
                        0, s, a, n_tiles, kt_plan, n_cu);
@@ -551,6 +852,7 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
+  if (a.act == GD_FP8) return launch_big<256, EPI_SWIGLU, GD_FP8, true>(a, s);  // checked by the caller
   if (a.epi == EPI_BIAS_F32) return launch_big<256, EPI_BIAS_F32, GD_BF16>(a, s);
   if (a.wdt == GD_FP8) {
     if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU, GD_FP8>(a, s);

@@ -54,6 +54,8 @@ moe_status check_desc(const moe_desc* d) {
   if (d->d % 128 != 0 || d->f % 128 != 0 || d->f_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (int64_t(d->T) * d->k >= kMaxAssign) return MOE_ERR_UNSUPPORTED;
   if (d->capacity < 0) return MOE_ERR_INVALID;
+  if (d->dispatch_fp8 != 0 && d->dispatch_fp8 != 1) return MOE_ERR_INVALID;
+  if (d->dispatch_fp8 && d->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -61,6 +63,28 @@ int64_t n_assign(const moe_desc* d) { return int64_t(d->T) * d->k; }
 
 int gemm_dtype(int moe_dt) {
   return moe_dt == MOE_F32 ? GD_F32 : moe_dt == MOE_BF16 ? GD_BF16 : GD_FP8;
+}
+
+// The fp8 dispatch payload of R rows: codes, then scales (moe.h).
+size_t payload_sstride(const moe_desc* d) { return MOE_FP8_SCALE_STRIDE(d->d); }
+size_t payload_bytes(const moe_desc* d, size_t R) { return MOE_FP8_PAYLOAD_BYTES(R, d->d); }
+uint8_t* payload_scales(void* p, const moe_desc* d, size_t R) {
+  return static_cast<uint8_t*>(p) + MOE_FP8_SCALES_OFFSET(R, d->d);
+}
+
+// The gate-up GEMM runs fp8 x fp8 on the payload itself (E4M3 weights on a
+// prefill-shaped problem); otherwise it reads the payload's values as bf16.
+bool fp8_act(const moe_desc* d) {
+  if (!d->dispatch_fp8 || d->wdtype != MOE_FP8_E4M3) return false;
+  GemmArgs g{};
+  g.act = GD_FP8;
+  g.wdt = GD_FP8;
+  g.epi = EPI_SWIGLU;
+  g.rows = int(int64_t(d->T) * d->k);
+  g.E = d->E;
+  g.K = d->d;
+  g.a_sstride = int(payload_sstride(d));
+  return gemm_fp8_act_ok(g);
 }
 
 // m-tile height of the routed grouped GEMMs (must match the launch)
@@ -141,6 +165,7 @@ struct LayerWs {
   int32_t* inv_pos;
   int32_t* offsets;
   void* x_perm;
+  void* xq;       // dispatch_fp8 with the fused gather: x's payload (or its bf16 values) in token order
   void* h;
   void* y_perm;
   void* sh;
@@ -187,7 +212,11 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   w.perm_token = c.take<int32_t>(sizeof(int32_t) * A);
   w.inv_pos = c.take<int32_t>(sizeof(int32_t) * A);
   w.offsets = c.take<int32_t>(sizeof(int32_t) * (d->E + 1));
-  w.x_perm = fuse_gather(d) ? nullptr : c.take<char>(A * d->d * ab);
+  const size_t T = size_t(d->T);
+  w.x_perm = fuse_gather(d) ? nullptr
+                            : c.take<char>(d->dispatch_fp8 ? std::max(A * d->d * 2, payload_bytes(d, A))
+                                                           : A * d->d * ab);
+  w.xq = fuse_gather(d) && d->dispatch_fp8 ? c.take<char>(std::max(T * d->d * 2, payload_bytes(d, T))) : nullptr;
   w.h = c.take<char>(A * d->f * ab);
   w.y_perm = c.take<char>(A * d->d * ab);
   w.sh = d->f_shared ? c.take<char>(size_t(d->T) * d->f_shared * ab) : nullptr;
@@ -195,12 +224,21 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   return w;
 }
 
+// moe_grouped_ffn given a payload that the gate-up GEMM cannot take as fp8:
+// its values as bf16 rows.
+void* carve_ffn_xdq(Carve& c, const moe_desc* d) {
+  return d->dispatch_fp8 && !fp8_act(d) ? c.take<char>(size_t(n_assign(d)) * d->d * 2) : nullptr;
+}
+
 size_t stage_bytes(const moe_desc* d, moe_stage stage) {
   Carve c(nullptr);
   switch (stage) {
     case MOE_STAGE_ROUTE: carve_route(c, d); break;
     case MOE_STAGE_DISPATCH: carve_dispatch(c, d); break;
-    case MOE_STAGE_FFN: carve_ffn(c, d, false); break;
+    case MOE_STAGE_FFN:
+      carve_ffn(c, d, false);
+      carve_ffn_xdq(c, d);
+      break;
     default: carve_layer(c, d); break;
   }
   return c.used;
@@ -247,6 +285,26 @@ moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, in
                                 x_perm, s));
 }
 
+// The fp8 payload of R rows of x into out: rows x[perm[p]] (perm NULL: in
+// order) for p < min(R, *rows_dev); as codes + scales, or (values) as bf16.
+moe_status run_payload(const moe_desc* d, const void* x, const int32_t* perm, int R, const int32_t* rows_dev,
+                       bool values, void* out, hipStream_t s) {
+  Fp8PayloadArgs p{};
+  p.x = x;
+  p.perm = perm;
+  p.rows = R;
+  p.rows_dev = rows_dev;
+  p.d = d->d;
+  p.sstride = int(payload_sstride(d));
+  if (values) {
+    p.deq = out;
+  } else {
+    p.codes = static_cast<uint8_t*>(out);
+    p.scales = payload_scales(out, d, size_t(R));
+  }
+  return dev(launch_fp8_payload(p, s));
+}
+
 // Optional shared-expert segment of the routed launches (see fuse_shared).
 struct SharedSeg {
   const void* x = nullptr;  // GEMM1 input: the tokens in order
@@ -258,10 +316,14 @@ struct SharedSeg {
 };
 
 // a_map: NULL (A = x_perm) or perm_token (A = x, the fused dispatch gather).
+// a_scales: NULL (A in the act dtype) or the scales of a payload A (codes).
 moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map, const int32_t* offsets,
                          const void* w1, const void* w3, const float* s1, const float* s3, void* h,
-                         const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr) {
+                         const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr,
+                         const uint8_t* a_scales = nullptr) {
   GemmArgs g{};
+  g.a_scales = a_scales;
+  g.a_sstride = a_scales ? int(payload_sstride(d)) : 0;
   g.ksplit = 1;
   if (sh) {
     g.sh_rows = d->T;
@@ -289,7 +351,7 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map,
   g.N = d->f;
   g.K = d->d;
   g.C = h;
-  g.act = gemm_dtype(d->act);
+  g.act = a_scales ? GD_FP8 : gemm_dtype(d->act);
   g.wdt = gemm_dtype(d->wdtype);
   g.epi = EPI_SWIGLU;
   return dev(launch_gemm(g, s));
@@ -424,8 +486,12 @@ moe_status moe_dispatch(const moe_desc* d, const int32_t* topk_idx, const void* 
   if (d->T > 0 && ws_bytes < stage_bytes(d, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
   Carve c(ws);
   const DispatchWs w = carve_dispatch(c, d);
-  return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w,
-                      static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!d->dispatch_fp8)
+    return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w, s);
+  MOE_TRY(run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, nullptr, w, s));
+  if (d->T == 0) return MOE_OK;
+  return run_payload(d, x, perm_token, int(n_assign(d)), offsets + d->E, false, x_perm, s);
 }
 
 moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets,
@@ -440,9 +506,21 @@ moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t*
   if (ws_bytes < stage_bytes(d, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
   Carve c(ws);
   const FfnWs w = carve_ffn(c, d, false);
+  void* xdq = carve_ffn_xdq(c, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(run_tables(d, offsets, w, s));
-  MOE_TRY(run_ffn_gemm1(d, x_perm, nullptr, offsets, w1, w3, s1, s3, h, w, s));
+  const size_t A = size_t(n_assign(d));
+  if (d->dispatch_fp8 && fp8_act(d)) {
+    MOE_TRY(run_ffn_gemm1(d, x_perm, nullptr, offsets, w1, w3, s1, s3, h, w, s, nullptr,
+                          payload_scales(const_cast<void*>(x_perm), d, A)));
+  } else if (d->dispatch_fp8) {
+    const uint8_t* codes = static_cast<const uint8_t*>(x_perm);
+    MOE_TRY(dev(launch_fp8_dequant(codes, payload_scales(const_cast<void*>(x_perm), d, A), int(payload_sstride(d)),
+                                   int(A), offsets + d->E, d->d, xdq, s)));
+    MOE_TRY(run_ffn_gemm1(d, xdq, nullptr, offsets, w1, w3, s1, s3, h, w, s));
+  } else {
+    MOE_TRY(run_ffn_gemm1(d, x_perm, nullptr, offsets, w1, w3, s1, s3, h, w, s));
+  }
   return run_ffn_gemm2(d, h, offsets, w2, s2, y_perm, w, s);
 }
 
@@ -488,7 +566,22 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(record(trace, 0, s));
   MOE_TRY(run_route(d, x, w_router, bias, topk_idx, topk_w, w.route, s));
   MOE_TRY(record(trace, 1, s));
-  MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos, w.x_perm, w.disp, s));
+  const bool fg = fuse_gather(d);  // GEMM1 reads its rows through perm_token
+  MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos,
+                       d->dispatch_fp8 ? nullptr : w.x_perm, w.disp, s));
+  // GEMM1's activation rows: x, the gathered x_perm, or the fp8 payload (in
+  // token order when the gather is fused, else gathered), as codes when the
+  // GEMM takes fp8 activations, else as bf16 values
+  const void* a_rows = fg ? x : w.x_perm;
+  const uint8_t* a_scales = nullptr;
+  if (d->dispatch_fp8) {
+    const bool f8 = fp8_act(d);
+    const int R = fg ? d->T : int(n_assign(d));
+    void* dst = fg ? w.xq : w.x_perm;
+    MOE_TRY(run_payload(d, x, fg ? nullptr : w.perm_token, R, fg ? nullptr : w.offsets + d->E, !f8, dst, s));
+    a_rows = dst;
+    if (f8) a_scales = payload_scales(dst, d, size_t(R));
+  }
   const bool fused = fuse_shared(d);
   SharedSeg sh;
   if (fused) {
@@ -501,9 +594,8 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   }
   MOE_TRY(run_tables(d, w.offsets, w.ffn, s, fused));
   MOE_TRY(record(trace, 2, s));
-  const bool fg = w.x_perm == nullptr;  // fused gather
-  MOE_TRY(run_ffn_gemm1(d, fg ? x : w.x_perm, fg ? w.perm_token : nullptr, w.offsets, w1, w3, s1, s3, w.h,
-                        w.ffn, s, fused ? &sh : nullptr));
+  MOE_TRY(run_ffn_gemm1(d, a_rows, fg ? w.perm_token : nullptr, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s,
+                        fused ? &sh : nullptr, a_scales));
   MOE_TRY(record(trace, 3, s));
   MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr));
   MOE_TRY(record(trace, 4, s));

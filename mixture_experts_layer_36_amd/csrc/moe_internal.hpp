@@ -74,6 +74,31 @@ hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
                               int row_bytes, void* x_perm, hipStream_t s);
 
+// The block-scaled E4M3 dispatch payload (fp8_payload.hip): bf16 rows cut
+// into blocks of 32 elements, each block one E8M0 scale 2^s (s smallest with
+// amax <= 448 * 2^s, 0 for an all-zero block) and E4M3 codes of x / 2^s
+// rounded to nearest even.  Row p of the output reads source row perm[p]
+// (perm NULL: row p) for p < min(rows, *rows_dev) (rows_dev nullable).
+// deq == NULL: codes [rows][d] and scales [rows][sstride] are written;
+// otherwise the dequantised values as bf16 rows [rows][d] go to deq.
+constexpr int kFp8Block = 32;
+struct Fp8PayloadArgs {
+  const void* x;            // bf16 source rows [.][d]
+  const int32_t* perm;
+  int rows;
+  const int32_t* rows_dev;
+  int d;
+  uint8_t* codes;
+  uint8_t* scales;
+  int sstride;              // bytes between scale rows (>= d / 32)
+  void* deq;
+};
+hipError_t launch_fp8_payload(const Fp8PayloadArgs& a, hipStream_t s);
+// Payload codes [rows][d] + scales [rows][sstride] -> bf16 rows [rows][d]
+// (exact), rows p < min(rows, *rows_dev).
+hipError_t launch_fp8_dequant(const uint8_t* codes, const uint8_t* scales, int sstride, int rows,
+                              const int32_t* rows_dev, int d, void* out, hipStream_t s);
+
 // Combine.
 struct CombineArgs {
   const void* y_perm;
@@ -90,7 +115,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // A rows are activations (row-major, K contiguous); B_e is the weight matrix
 // of the segment's expert (out x in, K contiguous).
 enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_BIAS_F32 = 2 };
-enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };
+enum GemmDtype { GD_F32 = 0, GD_BF16 = 1, GD_FP8 = 2 };  // act GD_FP8: the block-scaled payload
 
 struct GemmArgs {
   const void* A;               // [rows][K] activations (a_map: [a_map_rows][K])
@@ -112,7 +137,8 @@ struct GemmArgs {
   int N;                       // output columns (h columns for SwiGLU)
   int K;
   void* C;                     // [rows][N] output; EPI_BIAS_F32: [ksplit][rows][N] partial sums
-  int act;                     // GemmDtype of A and C (F32 or BF16); EPI_BIAS_F32 stores f32
+  int act;                     // GemmDtype of A (F32, BF16, or FP8: E4M3 codes with a_scales) and
+                               // of C (F32 for F32, else BF16); EPI_BIAS_F32 stores f32
   int wdt;                     // GemmDtype of B
   int epi;                     // GemmEpilogue
   int ksplit;                  // EPI_BIAS_F32: K is split into ksplit equal ranges (>= 1)
@@ -128,6 +154,10 @@ struct GemmArgs {
   // over after the last full wave of tiles (NULL / 0: never split).
   float* partial;
   int partial_slots;
+  // act == GD_FP8: E8M0 scales of A, one byte per 32 k values, rows of
+  // a_sstride bytes (a multiple of 16), indexed like A's rows.
+  const uint8_t* a_scales;
+  int a_sstride;
 };
 
 // Bytes of one partial-sum slot (one 256 x 256 tile of fp32 accumulators) and
@@ -142,6 +172,9 @@ int gemm_block_m(const GemmArgs& a);
 // segment of sh_rows rows.
 int gemm_max_slots(int rows, int E, int block_m, int sh_rows);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Whether launch_gemm takes act == GD_FP8 for this problem (E4M3 weights,
+// the SwiGLU epilogue, no extra segment, a prefill-sized grouped GEMM).
+bool gemm_fp8_act_ok(const GemmArgs& a);
 
 // Tile tables for up to two tile heights from segment offsets.
 struct TileTableArgs {

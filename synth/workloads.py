@@ -32,6 +32,7 @@ class Workload:
     wdt: str          # expert-weight storage: "f32" | "bf16" | "e4m3"
     bias_scale: float  # router bias b_e = -bias_scale * ln(rank_e); 0 = no bias
     capacity_factor: float = 0.0  # 0 = dropless; else slots = ceil(cf * T * k / E)
+    dispatch_fp8: bool = False    # dispatched rows as the block-scaled E4M3 payload
 
     @property
     def assignments(self) -> int:

@@ -44,7 +44,8 @@ def oracle_layer(L: LayerInputs, tokens=None) -> O.LayerResult:
     cap = O.expert_capacity(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
     assert tokens is None or cap == 0, "a capacity couples the tokens: no subsets"
     return O.layer_forward(x, wr, b, O.workload_spec(w), w.E, ew, w.act,
-                           O.adapters.decoded_shared(L), capacity=cap)
+                           O.adapters.decoded_shared(L), capacity=cap,
+                           fp8_dispatch=getattr(w, "dispatch_fp8", False))
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import mixture_experts_layer_36_amd as moe
 from mixture_experts_layer_36_amd import _lib
@@ -58,9 +59,33 @@ def test_status_strings():
     (dict(n_group=4, topk_group=2, k=3), moe.MOE_OK),
     (dict(capacity=5), moe.MOE_OK),
     (dict(capacity=-1), moe.MOE_ERR_INVALID),
+    (dict(dispatch_fp8=True, act="bf16", wdtype="e4m3"), moe.MOE_OK),
+    (dict(dispatch_fp8=True, act="bf16", wdtype="bf16"), moe.MOE_OK),
+    (dict(dispatch_fp8=True, act="f32", wdtype="f32"), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_validate(kw, code):
     assert moe.validate(_good(**kw)) == code
+
+
+def test_dispatch_fp8_flag_is_0_or_1():
+    d = _good()
+    d.dispatch_fp8 = 2
+    assert moe.validate(d) == moe.MOE_ERR_INVALID
+
+
+def test_fp8_payload_layout():
+    """Payload sizes as moe.h defines them: codes, then scale rows padded to
+    16 bytes, starting on a 256-byte boundary."""
+    assert moe.fp8_scale_stride(128) == 16 and moe.fp8_scale_stride(384) == 16
+    assert moe.fp8_scale_stride(1024) == 32 and moe.fp8_scale_stride(7168) == 224
+    assert moe.fp8_scales_offset(3, 128) == 512
+    assert moe.fp8_payload_bytes(3, 128) == 512 + 3 * 16
+    buf = torch.arange(moe.fp8_payload_bytes(5, 384), dtype=torch.int64).to(torch.uint8)
+    codes, scales = moe.fp8_payload_views(buf, 5, 384)
+    assert codes.shape == (5, 384) and scales.shape == (5, 12)
+    assert int(codes[1, 0]) == 384 % 256
+    off = moe.fp8_scales_offset(5, 384)
+    assert int(scales[2, 3]) == (off + 2 * 16 + 3) % 256
 
 
 def test_workspace_sizes_grow_with_tokens():

@@ -50,6 +50,20 @@ CASES = {
     "decode_cap": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, capacity_factor=1.0),
     "qwen_fp8_cap": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32, capacity_factor=1.25),
     "tiny_f32_cap": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3, capacity_factor=0.75),
+    # block-scaled E4M3 dispatch payload.  fp8 x fp8 gate-up GEMM: skewed
+    # tails (half tiles), K-split tiles (pieces of 8-stage scale chunks), K
+    # not a multiple of 512 (padded scale rows), a capacity
+    "qwen_f8d_big": QWEN_FP8_SKEW.scaled(T=800, d=512, f=384, E=16, k=4, dispatch_fp8=True),
+    "qwen_f8d_split": QWEN_FP8_SKEW.scaled(T=1200, d=1024, f=512, E=4, k=2, dispatch_fp8=True),
+    "qwen_f8d_n128": QWEN_FP8_SKEW.scaled(T=600, d=384, f=256, E=8, k=4, dispatch_fp8=True),
+    "qwen_f8d_cap": QWEN_FP8_SKEW.scaled(T=800, d=512, f=384, E=16, k=4, capacity_factor=1.25,
+                                         dispatch_fp8=True),
+    # payload values as bf16 rows: fp8 weights below the fp8 x fp8 shapes, bf16
+    # weights on the 128-row, 256-row and decode kernels (with the shared expert)
+    "qwen_f8d_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32, dispatch_fp8=True),
+    "mixtral_f8d": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384, dispatch_fp8=True),
+    "mixtral_big_f8d": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6, dispatch_fp8=True),
+    "decode_f8d": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, dispatch_fp8=True),
 }
 
 _CACHE = {}
@@ -110,14 +124,23 @@ def test_stages_chain(name):
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(A, dtype=torch.int32, device="cuda")
     inv = torch.empty(A, dtype=torch.int32, device="cuda")
-    x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    if w.dispatch_fp8:
+        x_perm = torch.empty(moe.fp8_payload_bytes(A, w.d), dtype=torch.uint8, device="cuda")
+    else:
+        x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
     moe.dispatch(desc, idx, dev.x, counts, offsets, perm, inv, x_perm,
                  moe.workspace(desc, moe.STAGE_DISPATCH))
     torch.cuda.synchronize()
     assert_dispatch(idx.cpu().numpy(), counts.cpu().numpy(), offsets.cpu().numpy(),
                     perm.cpu().numpy(), inv.cpu().numpy(), ref)
     n = int(offsets[-1])  # rows laid out: T*k, or fewer with a capacity
-    assert torch.equal(x_perm[:n], dev.x[perm[:n].long()])  # bitwise row copies
+    if w.dispatch_fp8:  # the payload of the gathered rows, byte for byte
+        codes, scales = moe.fp8_payload_views(x_perm, A, w.d)
+        rc, rs = O.quantize_fp8_blocks(O.decoded_inputs(L)[0][perm[:n].cpu().numpy()])
+        assert np.array_equal(codes[:n].cpu().numpy(), rc)
+        assert np.array_equal(scales[:n].cpu().numpy(), rs)
+    else:
+        assert torch.equal(x_perm[:n], dev.x[perm[:n].long()])  # bitwise row copies
 
     h = torch.empty((A, w.f), dtype=dev.x.dtype, device="cuda")
     y = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
@@ -184,7 +207,8 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
-                                  "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big", "dsv3_skew_cap"])
+                                  "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big", "dsv3_skew_cap",
+                                  "qwen_f8d_split", "decode_f8d"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
@@ -194,6 +218,83 @@ def test_deterministic(name):
 
 
 # ----------------------------------------------------------------- edge cases
+
+def _bf16_edge_rows(d=256, seed=11):
+    """bf16 rows that reach every branch of the payload quantiser: an all-zero
+    row; random bit patterns over the whole finite range (subnormal inputs,
+    blocks whose scale clamps at 2^-127, huge blocks); blocks spanning 2^-20
+    of their amax (subnormal E4M3 codes and values that round to zero, of both
+    signs); amax exactly 448 * 2^s and one bf16 step above it (the two scale
+    choices); every E4M3 tie point at several scales; -0.0 entries."""
+    rng = np.random.default_rng(seed)
+    rows = [np.zeros(d, np.uint16)]
+    for _ in range(6):  # random finite bf16 bit patterns
+        r = rng.integers(0, 1 << 16, d, dtype=np.uint32).astype(np.uint16)
+        r[(r & 0x7f80) == 0x7f80] &= 0xbfff  # no Inf / NaN: clear an exponent bit
+        rows.append(r)
+    for lo, hi in ((-20, 0), (-130, 0), (-140, -118)):  # wide ranges, bf16 subnormals, clamped scales
+        e = rng.integers(lo, hi, d)
+        m = rng.integers(0, 128, d)
+        sign = rng.integers(0, 2, d)
+        v = np.ldexp(1.0 + m / 128.0, e) * np.where(sign, -1.0, 1.0)
+        rows.append(O_round_to_bf16_bits(v))
+    f = np.zeros(d)
+    for b in range(d // 32):  # amax = 448 * 2^s exactly / one bf16 step above
+        s = b - 4
+        blk = rng.standard_normal(32) * 2.0 ** s
+        blk[b % 32] = (448.0 if b % 2 == 0 else 456.0) * 2.0 ** s
+        f[b * 32:(b + 1) * 32] = blk
+    rows.append(O_round_to_bf16_bits(f))
+    ties = []  # midpoints between neighbouring E4M3 magnitudes, scale 2^0
+    codes = np.arange(0, 127)
+    vals = O.e4m3_to_f64(codes.astype(np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids = mids[mids == O.round_bf16(mids)]  # exactly representable in bf16
+    for k in range(2):
+        t = np.resize(mids, d) * np.where(np.arange(d) % 2, -1.0, 1.0) * 2.0 ** (3 * k)
+        t[::32] = 448.0 * 2.0 ** (3 * k)  # pins each block's scale
+        rows.append(O_round_to_bf16_bits(t))
+    negz = rng.standard_normal(d)
+    negz[::3] = -0.0
+    rows.append(O_round_to_bf16_bits(negz))
+    return np.stack(rows)
+
+
+def O_round_to_bf16_bits(v):
+    """float64 -> nearest bf16 bit patterns (via the oracle's rounding)."""
+    r = O.round_bf16(np.asarray(v, dtype=np.float64)).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_fp8_payload_bytes_edge_values():
+    """The dispatch payload of crafted rows, byte for byte against the
+    oracle's quantiser (one expert, k = 1: rows in order)."""
+    xb = _bf16_edge_rows()
+    T, d = xb.shape
+    w = MIXTRAL_PREFILL.scaled(T=T, d=d, f=128, E=1, k=1, dispatch_fp8=True)
+    desc = moe.Desc.from_attrs(w)
+    x = to_torch(xb, "bf16")
+    idx = torch.zeros((T, 1), dtype=torch.int32, device="cuda")
+    counts = torch.empty(1, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(2, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, dtype=torch.int32, device="cuda")
+    buf = torch.empty(moe.fp8_payload_bytes(T, d), dtype=torch.uint8, device="cuda")
+    moe.dispatch(desc, idx, x, counts, offsets, perm, inv, buf, moe.workspace(desc, moe.STAGE_DISPATCH))
+    torch.cuda.synchronize()
+    assert np.array_equal(perm.cpu().numpy(), np.arange(T))
+    codes, scales = moe.fp8_payload_views(buf, T, d)
+    rc, rs = O.quantize_fp8_blocks(O.bf16_to_f64(xb))
+    sc = scales.cpu().numpy()
+    assert np.array_equal(sc, rs), np.argwhere(sc != rs)[:5]
+    cc = codes.cpu().numpy()
+    bad = np.argwhere(cc != rc)
+    assert bad.size == 0, [(tuple(i), hex(xb[tuple(i)]), cc[tuple(i)], rc[tuple(i)]) for i in bad[:5]]
+    # the scale choices the rows were built to reach
+    assert (rs == 0).any() and (rs == 127).any()
+    assert (((rc & 0x78) == 0) & ((rc & 7) != 0)).any() and (rc == 0).any()  # subnormal codes, zeros
+
+
 
 def _custom(w, seed=3, bias=None, wr=None, accept=True):
     L = LayerInputs(w, seed)
