@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s per MI355X; grouped-GEMM % MFMA peak; decode % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 DEFAULT_WORKLOAD = "mixtral8x7b_prefill_bf16"
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens for the oracle timing")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="expert capacity = factor * T * k / E slots (0: dropless); overflow is dropped")
+    p.add_argument("--dispatch-fp8", action="store_true",
+                   help="dispatch the block-scaled E4M3 payload of x (fp8 x fp8 gate-up GEMM with E4M3 weights)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -77,6 +80,15 @@ def layer_bytes(w, counts) -> float:
     return float(b)
 
 
+def fp8_gate_up(w) -> bool:
+    """Whether the library runs the gate-up GEMM fp8 x fp8 for w: the fp8
+    payload with E4M3 weights on the prefill kernel's shapes (at least 1024
+    routed rows and 128 per expert on average, K a multiple of 64)."""
+    rows = w.T * w.k
+    return (w.dispatch_fp8 and w.wdt == "e4m3" and rows >= 1024 and rows // w.E >= 128
+            and w.d % 64 == 0)
+
+
 def stage_bytes(w, has_bias: bool, kept: int) -> dict:
     """Algorithmic bytes of the memory-bound stages of the layer path:
     route = x + router weight (+ bias) + the top-k indices and gates written;
@@ -89,6 +101,8 @@ def stage_bytes(w, has_bias: bool, kept: int) -> dict:
     tk = w.T * w.k
     route = w.T * w.d * ab + w.E * w.d * ab + (w.E * 4 if has_bias else 0) + 8 * tk
     dispatch = 4 * tk + 8 * tk + 8 * w.E
+    if w.dispatch_fp8:  # x read once, its payload (codes + scale rows) written in token order
+        dispatch += w.T * w.d * ab + w.T * (w.d + (w.d // 32 + 15) // 16 * 16)
     combine = kept * w.d * ab + 8 * tk + w.T * w.d * ab + (w.T * w.d * ab if w.f_shared else 0)
     return {"route": float(route), "dispatch": float(dispatch), "combine": float(combine)}
 
@@ -133,7 +147,8 @@ def cpu_baseline(w, L, host_experts, sample):
     # with a capacity factor the sample gets its own slots (factor * sample * k / E)
     cap = O.expert_capacity(getattr(w, "capacity_factor", 0), sample, w.k, w.E)
     t0 = time.perf_counter()
-    O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap)
+    O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap,
+                    fp8_dispatch=w.dispatch_fp8)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
@@ -161,6 +176,8 @@ def main():
     seed = DEFAULT_SEED[w.name] if args.seed is None else args.seed
     if args.capacity_factor > 0:
         w = w.scaled(capacity_factor=args.capacity_factor)
+    if args.dispatch_fp8:
+        w = w.scaled(dispatch_fp8=True)
     L = LayerInputs(w, seed)
     host_experts = {}
 
@@ -230,18 +247,24 @@ def main():
                 "frac_of_measured_read_ceiling": round(achieved / STREAM_READ_GBS, 4)}
     else:
         achieved = flops_gemm1 / gemm1_s / 1e12
-        roof = {"bound": "mfma", "kernel": "routed gate-up GEMM + SwiGLU (gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU)",
-                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "algorithmic_flops": flops_gemm1,
-                "avg_launch_us": round(gemm1_s * 1e6, 2),
-                "frac_of_measured_mfma_ceiling": round(achieved / MFMA_LOOP_TFLOPS, 4)}
+        f8 = fp8_gate_up(w)
+        peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
+        kern = ("gemm_big_fp8_kernel: fp8 x fp8 block-scaled MFMA" if f8 else
+                "gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU")
+        roof = {"bound": "mfma", "kernel": f"routed gate-up GEMM + SwiGLU ({kern})",
+                "mfma_dtype": "fp8" if f8 else "bf16",
+                "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "algorithmic_flops": flops_gemm1,
+                "avg_launch_us": round(gemm1_s * 1e6, 2)}
+        if not f8:
+            roof["frac_of_measured_mfma_ceiling"] = round(achieved / MFMA_LOOP_TFLOPS, 4)
     # HBM bytes per launch of that kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE passes, valid only while the kernels are unchanged
     roof["traffic"] = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
-        ent = tr.get(w.name)
+        ent = tr.get(w.name + ("+dispatch_fp8" if w.dispatch_fp8 else ""))
         if ent and ent.get("source_hash") == kernel_source_hash():
             roof["traffic"] = ent.get("bytes_per_launch")
 
@@ -249,11 +272,12 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.act == "bf16" else "f32", "data": "synthetic",
+        "dtype": ("bf16, fp8 gate-up" if fp8_gate_up(w) else "bf16") if w.act == "bf16" else "f32",
+        "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
                    "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
-                   "capacity_factor": w.capacity_factor},
+                   "capacity_factor": w.capacity_factor, "dispatch_fp8": w.dispatch_fp8},
         "roofline": roof,
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
         "stages_us": stage_us,
