@@ -203,7 +203,86 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Buffer descriptor word 3 for raw 32-bit-format buffers on gfx9-family GPUs.
 [[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
 
+// Output columns of a tile and the LDS bytes of its staged copy.
+template <int BN, int EPI>
+struct OutTile {
+  static constexpr int COLS = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  static constexpr int ROW_BYTES = COLS * 2;  // bf16
+  static constexpr int CPR = COLS / 8;        // 16-byte chunks per row
+  static constexpr int BYTES = BM * ROW_BYTES;
+  static_assert(CPR >= 16 && (CPR & (CPR - 1)) == 0, "chunk swizzle");
+};
+
 #if defined(__HIP_DEVICE_COMPILE__)
+// Epilogue of a whole tile (SwiGLU or plain store, bf16 out) through LDS.
+// Each wave writes its values -- runs of 4 consecutive columns of one row per
+// lane and 32x32 block -- into a row-major copy of the tile in LDS, 16-byte
+// chunk c of row r at c ^ (r & 15) (the 32 rows a write touches spread over
+// the banks); then the block stores whole rows with 16-byte writes, so one
+// wave instruction covers 2-4 full row runs rather than 32 rows x 16 bytes.
+// The operand ring is dead by now: every wave has read its last fragments.
+template <int BN, int WN, int EPI, bool HALF, int WDT>
+__device__ __forceinline__ void store_tile_lds(const TileInfo& ti, const Seg& sg,
+                                               f32x16 (&acc)[BigCfg<BN, WN, HALF>::TW][BigCfg<BN, WN, HALF>::TA],
+                                               int ncol0, char* lds) {
+  using C = BigCfg<BN, WN, HALF>;
+  using O = OutTile<BN, EPI>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int arow = wave_arow<BN, WN, HALF>(wave), wcol = wave_col<BN, WN, HALF, EPI>(wave);
+  const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  barrier_only();
+  auto put = [&](int lrow, int lcol, float v0, float v1, float v2, float v3) {
+    u32x2 o;
+    o[0] = pack_bf16x2(v0, v1);
+    o[1] = pack_bf16x2(v2, v3);
+    *(u32x2*)(lds + lrow * O::ROW_BYTES + (((lcol >> 3) ^ (lrow & 15)) << 4) + (lcol & 7) * 2) = o;
+  };
+  constexpr int NB = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    float4 su[4], sv[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = ncol0 + wcol + i * 32 + g * 8 + (lane >> 5) * 4;
+      su[g] = sv[g] = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (scaled) {
+        su[g] = *(const float4*)(sg.s0 + n);
+        if (EPI == EPI_SWIGLU) sv[g] = *(const float4*)(sg.s1 + n);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::TA; ++j) {
+      const int lrow = arow + j * 32 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int lcol = wcol + i * 32 + g * 8 + (lane >> 5) * 4;
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float u = acc[i][j][g * 4 + q] * su[g][q];
+          if (EPI == EPI_SWIGLU) {
+            const float v = acc[i + C::TW / 2][j][g * 4 + q] * sv[g][q];
+            o[q] = silu(u) * v;
+          } else {
+            o[q] = u;
+          }
+        }
+        put(lrow, lcol, o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  barrier_only();
+  const int rows = ti.nrows;
+  for (int u = tid; u < rows * O::CPR; u += C::NTHR) {
+    const int r = u / O::CPR, ch = u % O::CPR;
+    const u32x4 v = *(const u32x4*)(lds + r * O::ROW_BYTES + ((ch ^ (r & 15)) << 4));
+    if (ncol0 + ch * 8 < sg.N) *(u32x4*)((uint16_t*)sg.C + (size_t)(ti.row0 + r) * sg.N + ncol0 + ch * 8) = v;
+  }
+}
+
 // One tile (or K-piece of a tile) in the full or the half layout.
 template <int BN, int WN, int EPI, bool HALF, int WDT>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
@@ -404,7 +483,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     return;
   }
-  store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+  if constexpr (EPI == EPI_BIAS_F32)
+    store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+  else
+    store_tile_lds<BN, WN, EPI, HALF, WDT>(ti, sg, acc, ncol0, lds);
 }
 #endif
 
@@ -413,7 +495,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
                                                                 int n_cu) {
   // device pass only: the host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, false, WDT>::STAGE_BYTES];
+  constexpr int RING = STAGES * BigMem<BN, WN, false, WDT>::STAGE_BYTES;
+  constexpr int OUT = (EPI == EPI_BIAS_F32) ? 0 : OutTile<BN, EPI>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[RING > OUT ? RING : OUT];
   Work wk;
   if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
@@ -698,7 +782,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     return;
   }
-  store_tile<C::TW, C::TA, GD_FP8, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+  store_tile_lds<BN, WN, EPI, HALF, GD_FP8>(ti, sg, acc, ncol0, lds);
 }
 #endif
 
@@ -706,6 +790,7 @@ template <int BN, int WN, int EPI>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_tiles, int kt_plan,
                                                                     int n_cu) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(OutTile<BN, EPI>::BYTES <= STAGES * BigMem<BN, WN, false, GD_BF16>::STAGE_BYTES, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, false, GD_BF16>::STAGE_BYTES +
                                                      2 * SC_BYTES];
   Work wk;
