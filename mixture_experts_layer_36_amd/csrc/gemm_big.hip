@@ -214,23 +214,30 @@ struct OutTile {
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
-// Epilogue of a whole tile (SwiGLU or plain store, bf16 out) through LDS.
-// Each wave writes its values -- runs of 4 consecutive columns of one row per
-// lane and 32x32 block -- into a row-major copy of the tile in LDS, 16-byte
-// chunk c of row r at c ^ (r & 15) (the 32 rows a write touches spread over
-// the banks); then the block stores whole rows with 16-byte writes, so one
-// wave instruction covers 2-4 full row runs rather than 32 rows x 16 bytes.
-// The operand ring is dead by now: every wave has read its last fragments.
+// End of a tile with the SwiGLU or plain-store epilogue (bf16 out), or of a
+// K-piece of a split tile.
+//   * A whole tile goes out through LDS: each wave writes its values -- runs
+//     of 4 consecutive columns of one row per lane and 32x32 block -- into a
+//     row-major copy of the tile, 16-byte chunk c of row r at c ^ (r & 15)
+//     (the 32 rows one write touches spread over the banks); then the block
+//     stores whole rows with 16-byte writes, so one wave instruction covers
+//     2-4 full row runs rather than 32 rows x 16 bytes.  The operand ring is
+//     dead by then: every wave has read its last fragments.
+//   * A piece stores its raw accumulators to its partial slot, register-major
+//     so that each 16-byte store of a wave is contiguous.
+// Both are handled block by block in one pass.
 template <int BN, int WN, int EPI, bool HALF, int WDT>
-__device__ __forceinline__ void store_tile_lds(const TileInfo& ti, const Seg& sg,
-                                               f32x16 (&acc)[BigCfg<BN, WN, HALF>::TW][BigCfg<BN, WN, HALF>::TA],
-                                               int ncol0, char* lds) {
+__device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
+                                            f32x16 (&acc)[BigCfg<BN, WN, HALF>::TW][BigCfg<BN, WN, HALF>::TA],
+                                            int ncol0, char* lds, int slot) {
   using C = BigCfg<BN, WN, HALF>;
   using O = OutTile<BN, EPI>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int arow = wave_arow<BN, WN, HALF>(wave), wcol = wave_col<BN, WN, HALF, EPI>(wave);
-  const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr;
+  const bool piece = slot >= 0;
+  const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr && !piece;
+  float4* P = (float4*)(a.partial + (size_t)(piece ? slot : 0) * (kPartialSlotBytes / 4));
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   barrier_only();
   auto put = [&](int lrow, int lcol, float v0, float v1, float v2, float v3) {
@@ -238,6 +245,12 @@ __device__ __forceinline__ void store_tile_lds(const TileInfo& ti, const Seg& sg
     o[0] = pack_bf16x2(v0, v1);
     o[1] = pack_bf16x2(v2, v3);
     *(u32x2*)(lds + lrow * O::ROW_BYTES + (((lcol >> 3) ^ (lrow & 15)) << 4) + (lcol & 7) * 2) = o;
+  };
+  auto raw = [&](int i, int j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
+          make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
   };
   constexpr int NB = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
 #pragma unroll
@@ -254,6 +267,12 @@ __device__ __forceinline__ void store_tile_lds(const TileInfo& ti, const Seg& sg
     }
 #pragma unroll
     for (int j = 0; j < C::TA; ++j) {
+      if (piece) {
+        raw(i, j);
+        if (EPI == EPI_SWIGLU) raw(i + C::TW / 2, j);
+      }
+      // a piece also fills the LDS copy (never stored): with no second path
+      // the compiler keeps the accumulators in AGPRs
       const int lrow = arow + j * 32 + (lane & 31);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -271,8 +290,11 @@ __device__ __forceinline__ void store_tile_lds(const TileInfo& ti, const Seg& sg
         }
         put(lrow, lcol, o[0], o[1], o[2], o[3]);
       }
+      // one block at a time: the accumulators leave the AGPRs as needed
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if (piece) return;
   __builtin_amdgcn_s_waitcnt(0xc07f);
   barrier_only();
   const int rows = ti.nrows;
@@ -469,24 +491,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
 
-  if (wk.slot >= 0) {
-    // a K-piece: raw accumulators to its slot, register-major so that each
-    // 16-byte store of a wave is contiguous
-    float4* P = (float4*)(a.partial + (size_t)wk.slot * (kPartialSlotBytes / 4));
-#pragma unroll
-    for (int i = 0; i < C::TW; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TA; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    return;
-  }
-  if constexpr (EPI == EPI_BIAS_F32)
+  if constexpr (EPI == EPI_BIAS_F32)  // router logits: never split (K ranges go to blockIdx.y)
     store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
   else
-    store_tile_lds<BN, WN, EPI, HALF, WDT>(ti, sg, acc, ncol0, lds);
+    finish_tile<BN, WN, EPI, HALF, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot);
 }
 #endif
 
@@ -769,20 +777,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     });
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
-
-  if (wk.slot >= 0) {
-    float4* P = (float4*)(a.partial + (size_t)wk.slot * (kPartialSlotBytes / 4));
-#pragma unroll
-    for (int i = 0; i < C::TW; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TA; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    return;
-  }
-  store_tile_lds<BN, WN, EPI, HALF, GD_FP8>(ti, sg, acc, ncol0, lds);
+  finish_tile<BN, WN, EPI, HALF, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot);
 }
 #endif
 
