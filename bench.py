@@ -53,6 +53,9 @@ def parse():
                    help="expert capacity = factor * T * k / E slots (0: dropless); overflow is dropped")
     p.add_argument("--dispatch-fp8", action="store_true",
                    help="dispatch the block-scaled E4M3 payload of x (fp8 x fp8 gate-up GEMM with E4M3 weights)")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of one HIP graph of the layer forward (captured once); the per-stage "
+                        "times then come from a separate traced eager pass")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -216,11 +219,34 @@ def main():
             ev.record()
     torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(traces[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.graph:
+        # per-stage times from a traced eager pass; the timed steps replay
+        # one captured graph of the forward
+        for i in range(args.steps):
+            step(traces[i])
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(traces[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
 
     stage_ms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
                          for tr in traces])
@@ -277,7 +303,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
                    "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
-                   "capacity_factor": w.capacity_factor, "dispatch_fp8": w.dispatch_fp8},
+                   "capacity_factor": w.capacity_factor, "dispatch_fp8": w.dispatch_fp8,
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": roof,
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
         "stages_us": stage_us,
