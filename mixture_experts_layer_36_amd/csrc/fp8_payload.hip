@@ -30,44 +30,14 @@
 namespace moe {
 namespace {
 
-// Everything is integer arithmetic on the bf16 bits, so subnormal inputs
-// and scaled values are exact whatever the float denormal mode.
-//
-// E4M3 magnitude code of M * 2^q (M: an integer significand, 1..255; the
-// value must be <= 448).  With e the value's binary exponent and eb =
-// max(e, -6), the code's step is 2^(eb - 3) (normal codes hold 8..15 steps,
-// subnormal ones 0..7 steps of 2^-9), so the code is (eb + 6) * 8 + r with r
-// the value in steps rounded to nearest even; r = 16 (or 8 for a subnormal)
-// lands exactly on the next binade's first code.
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t M, int q) {
-  const int nb = 32 - __builtin_clz(M);  // bit length
-  const int e = nb - 1 + q;
-  const int eb = e < -6 ? -6 : e;
-  const int shift = eb - 3 - q;
-  uint32_t r;
-  if (shift <= 0) {
-    r = M << (-shift);
-  } else if (shift > 9) {
-    r = 0;  // below half a step (M < 2^8)
-  } else {
-    r = M >> shift;
-    const uint32_t rem = M & ((1u << shift) - 1u), half = 1u << (shift - 1);
-    r += (rem > half || (rem == half && (r & 1u))) ? 1u : 0u;
-  }
-  return r == 0 ? 0u : (uint32_t)((eb + 6) * 8) + r;
-}
-
-// bf16 magnitude bits (no sign) -> (M, q) with value M * 2^q, M >= 1.
-__device__ __forceinline__ void bf16_sig(uint32_t mag, uint32_t& M, int& q) {
-  const uint32_t ef = mag >> 7, m = mag & 0x7fu;
-  if (ef == 0) {  // subnormal: m * 2^-133
-    M = m;
-    q = -133;
-  } else {
-    M = m | 0x80u;
-    q = (int)ef - 134;  // (128 + m) * 2^(ef - 127 - 7)
-  }
-}
+// The scale comes from integer arithmetic on the bf16 bits of the block's
+// largest magnitude.  Each element is scaled by 2^-s exactly (an exponent
+// change; a bf16 subnormal goes through its integer significand, so no step
+// depends on the float denormal mode) and converted by the hardware
+// f32 -> E4M3 conversion, which rounds to nearest even with OCP subnormals
+// (checked against a brute-force nearest search over a 2^-14 grid up to 16 and
+// against the oracle's codes).  It gives -0 for a negative value that rounds
+// to zero; the payload's zero is +0.
 
 // Scale exponent s of a block whose largest magnitude has bf16 bits amag:
 // with amax = (1 + m/128) * 2^e, the smallest s with amax <= 448 * 2^s =
@@ -102,26 +72,24 @@ __global__ __launch_bounds__(256) void fp8_payload_kernel(Fp8PayloadArgs a) {
       amag = max(amag, (v[i][q] >> 16) & 0x7fffu);
     }
   const int s = block_scale_exp(amag);
-  uint32_t codes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // x * 2^-s as a float (exact: |x| * 2^-s <= 448; values that would leave
+  // the normal range are far below half the smallest E4M3 step)
+  auto scaled = [&](uint32_t b) -> float {
+    const uint32_t mag = b & 0x7fffu;
+    const float v = (mag >> 7) ? ldexpf(__uint_as_float(mag << 16), -s) : ldexpf((float)mag, -133 - s);
+    return (b & 0x8000u) ? -v : v;
+  };
+  uint32_t codes[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t b = h ? (v[i][q] >> 16) : (v[i][q] & 0xffffu);
-        const uint32_t mag = b & 0x7fffu;
-        uint32_t c = 0;
-        if (mag != 0) {
-          uint32_t M;
-          int e2;
-          bf16_sig(mag, M, e2);
-          c = e4m3_code(M, e2 - s);
-          if (c != 0) c |= (b & 0x8000u) ? 0x80u : 0u;
-        }
-        const int idx = (i * 4 + q) * 2 + h;  // element 0..31
-        codes[idx >> 2] |= c << ((idx & 3) * 8);
-      }
+    for (int q = 0; q < 4; q += 2) {  // elements 8i + 2q .. 8i + 2q + 3
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(v[i][q] & 0xffffu), scaled(v[i][q] >> 16), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(v[i][q + 1] & 0xffffu), scaled(v[i][q + 1] >> 16), w, true);
+      const uint32_t u = (uint32_t)w;
+      const uint32_t nz = ((u & 0x7f7f7f7fu) + 0x7f7f7f7fu) & 0x80808080u;  // magnitude != 0, per byte
+      codes[i * 2 + q / 2] = (u & 0x7f7f7f7fu) | (u & nz);                 // -0 -> +0
+    }
   if (a.deq) {  // dequantised bf16 payload
     u32x4* out = (u32x4*)((uint16_t*)a.deq + (size_t)row * a.d + blk * 32);
 #pragma unroll
