@@ -13,9 +13,11 @@ and a Capacity Worked Example, Figure 2; the same chain router -> top-k ->
 dispatch -> expert FFN -> combine -> original token order in "MoE Expert
 Parallelism in Practice", §Core Principles 1; experts run as grouped GEMMs and
 combine is a weighted sum in "Tensor vs Expert vs Data Parallelism for MoE
-Serving", §Deeper Analysis, Figure 2).  Dispatch is drop-free: no token is
-dropped for capacity (the drop-free path preferred in "Expert-Parallel MoE
-Inference", §Capacity factor and token dropping).
+Serving", §Deeper Analysis, Figure 2).  Dispatch is drop-free by default
+(the path preferred in "Expert-Parallel MoE Inference", §Capacity factor and
+token dropping); the same section's capacity variant is here too: a fixed
+number of slots per expert, with overflow dropped (dispatch) or rerouted to
+the token's next-best expert (dispatch_reroute).
 
 Readings the pages leave open, and the workload definitions fix:
   * expert FFN is SwiGLU: h = silu(x W1) * (x W3), y = h W2, silu(u) = u*sigmoid(u);
@@ -346,6 +348,113 @@ def dispatch(topk_idx: np.ndarray, E: int, capacity: int = 0):
             perm_token.astype(np.int32), inv_pos.astype(np.int32))
 
 
+# --------------------------------------------------------------------------
+# Capacity overflow rerouted to the next-best expert
+# --------------------------------------------------------------------------
+
+
+def reroute_candidates(s: np.ndarray, spec: RouteSpec):
+    """The experts a token's overflow may move to, best first: its eligible
+    experts ranked right after its top-k (ranks k .. 2k-1 in the same
+    (score descending, id ascending) order; -1 past the eligible ones), and
+    the gate each would carry: its score, divided by the sum of the chosen
+    k's scores when the gates are renormalised (the denominator of the
+    token's other gates), else the score itself.  ("Expert-Parallel MoE
+    Inference", §Capacity factor and token dropping: overflow tokens are
+    rerouted to their next-best expert.)
+    -> (cand_idx [T, k] int32, cand_w [T, k] float64)."""
+    T, E = s.shape
+    k = spec.k
+    masked = np.where(eligible(s, spec), s, -np.inf)
+    order = _order_desc(masked)
+    cand = np.full((T, k), -1, dtype=np.int64)
+    n = min(k, E - k)
+    if n > 0:
+        c = order[:, k:k + n]
+        ok = np.isfinite(np.take_along_axis(masked, c, axis=1))
+        cand[:, :n] = np.where(ok, c, -1)
+    if spec.renorm:
+        den = np.take_along_axis(s, order[:, :k], axis=1).sum(axis=1, keepdims=True)
+    else:
+        den = np.ones((T, 1))
+    cw = np.where(cand >= 0, np.take_along_axis(s, np.maximum(cand, 0), axis=1) / den, 0.0)
+    return cand.astype(np.int32), cw
+
+
+def dispatch_reroute(topk_idx: np.ndarray, topk_w: np.ndarray, cand_idx: np.ndarray,
+                     cand_w: np.ndarray, E: int, capacity: int):
+    """Expert capacity with overflow rerouted to the next-best expert.
+
+    Pass 1 is dispatch() with the capacity: assignments a = t*k + j claim a
+    slot of their own expert in increasing a; those finding it full overflow.
+    Pass 2: the m-th overflowed assignment of a token (counting in increasing
+    j) is offered the token's candidate m (reroute_candidates); the offers
+    claim the slots their expert has left after pass 1, in increasing a.  An
+    offer finding no slot, or an overflow with no candidate, is dropped.
+    Rows of an expert: its pass-1 rows, then its pass-2 rows, each group in
+    increasing a.
+    Returns counts[E] (the demand of the top-k, as dispatch()), offsets[E+1],
+    perm_token[offsets[E]], inv_pos[T*k] (row of the copy that serves the
+    assignment, or -1), gates [T, k] (the gate of the serving copy: topk_w
+    for its own expert, the candidate's gate when rerouted, 0 when dropped)
+    and served [T, k] (the serving expert, -1 when dropped)."""
+    T, k = topk_idx.shape
+    n = T * k
+    a_exp = topk_idx.reshape(-1).astype(np.int64)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in a_exp:
+        counts[e] += 1
+    # pass 1
+    used = np.zeros(E, dtype=np.int64)
+    own = np.zeros(n, dtype=bool)
+    for a, e in enumerate(a_exp):
+        if used[e] < capacity:
+            used[e] += 1
+            own[a] = True
+    kept1 = used.copy()
+    # offers: the token's m-th overflow gets its candidate m
+    offer = np.full(n, -1, dtype=np.int64)
+    offer_m = np.full(n, -1, dtype=np.int64)
+    for t in range(T):
+        m = 0
+        for j in range(k):
+            a = t * k + j
+            if not own[a]:
+                offer[a] = cand_idx[t, m]
+                offer_m[a] = m
+                m += 1
+    # pass 2: offers claim what pass 1 left, in increasing a
+    rer = np.zeros(n, dtype=bool)
+    for a in range(n):
+        c = offer[a]
+        if c >= 0 and used[c] < capacity:
+            used[c] += 1
+            rer[a] = True
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + used[e]
+    nxt = offsets[:-1].copy()
+    perm_token = np.empty(offsets[E], dtype=np.int64)
+    inv_pos = np.full(n, -1, dtype=np.int64)
+    served = np.full(n, -1, dtype=np.int64)
+    gates = np.zeros(n)
+    for a in range(n):          # pass-1 rows of every expert
+        if own[a]:
+            e = a_exp[a]
+            inv_pos[a], served[a], gates[a] = nxt[e], e, topk_w[a // k, a % k]
+            perm_token[nxt[e]] = a // k
+            nxt[e] += 1
+    assert np.array_equal(nxt, offsets[:-1] + kept1)
+    for a in range(n):          # then the rerouted rows
+        if rer[a]:
+            c = offer[a]
+            inv_pos[a], served[a], gates[a] = nxt[c], c, cand_w[a // k, offer_m[a]]
+            perm_token[nxt[c]] = a // k
+            nxt[c] += 1
+    return (counts.astype(np.int32), offsets.astype(np.int32), perm_token.astype(np.int32),
+            inv_pos.astype(np.int32), gates.reshape(T, k), served.astype(np.int32).reshape(T, k))
+
+
 def gather_rows(x: np.ndarray, perm_token: np.ndarray) -> np.ndarray:
     """x_perm[p] = x[perm_token[p]] (the dispatch payload, one copy per
     assignment)."""
@@ -437,26 +546,38 @@ class LayerResult:
     shared_h: Optional[np.ndarray]
     shared_y: Optional[np.ndarray]
     out: np.ndarray
+    gates: Optional[np.ndarray] = None    # gate of each assignment's serving copy (reroute)
+    served: Optional[np.ndarray] = None   # serving expert per assignment, -1: dropped (reroute)
 
 
 def layer_forward(x, w_router, bias, spec: RouteSpec, E: int, expert_weights: ExpertFn, act: str,
                   shared: Optional[Sequence[np.ndarray]] = None, capacity: int = 0,
-                  fp8_dispatch: bool = False) -> LayerResult:
+                  fp8_dispatch: bool = False, overflow: str = "drop") -> LayerResult:
     """The whole layer: route, dispatch, grouped SwiGLU FFN, shared expert,
     combine.  x, w_router and the weights are float64 values of the stored
     inputs.  Without a capacity the layer is token-wise: running it on a
     subset of the tokens gives exactly those tokens' results.  With a
     capacity (slots per expert) overflow assignments are dropped and the
-    kept ones keep their gates.  With fp8_dispatch the dispatched rows are the
+    kept ones keep their gates; with overflow="reroute" they go to their
+    token's next-best expert first (dispatch_reroute) and carry that
+    expert's gate.  With fp8_dispatch the dispatched rows are the
     block-scaled E4M3 payload of x (quantize_fp8_blocks) as the routed
     experts' input; the router and the shared expert read x itself."""
-    idx, gw, _ = route(x, w_router, bias, spec)
-    counts, offsets, perm_token, inv_pos = dispatch(idx, E, capacity)
+    idx, gw, s = route(x, w_router, bias, spec)
+    gates = served = None
+    if capacity > 0 and overflow == "reroute":
+        cand, cw = reroute_candidates(s, spec)
+        counts, offsets, perm_token, inv_pos, gates, served = dispatch_reroute(idx, gw, cand, cw, E, capacity)
+    elif overflow in ("drop", "reroute"):
+        counts, offsets, perm_token, inv_pos = dispatch(idx, E, capacity)
+    else:
+        raise ValueError(overflow)
     payload = dequantize_fp8_blocks(*quantize_fp8_blocks(x)) if fp8_dispatch else x
     x_perm = gather_rows(payload, perm_token)
     h, y_perm = grouped_ffn(x_perm, offsets, expert_weights, act)
     sh = sy = None
     if shared is not None:
         sh, sy = swiglu_expert(x, shared[0], shared[1], shared[2], act)
-    out = combine(y_perm, inv_pos, gw, act, sy)
-    return LayerResult(idx, gw, counts, offsets, perm_token, inv_pos, x_perm, h, y_perm, sh, sy, out)
+    out = combine(y_perm, inv_pos, gw if gates is None else gates, act, sy)
+    return LayerResult(idx, gw, counts, offsets, perm_token, inv_pos, x_perm, h, y_perm, sh, sy, out,
+                       gates, served)

@@ -448,6 +448,114 @@ def check_capacity():
     assert np.array_equal(got.out, O.round_act(want, "f32"))  # same j order, same rounding
 
 
+def check_reroute():
+    """Overflow rerouted to the next-best expert: special cases that reduce to
+    dispatch(), invariants checked by brute force, and a constructed layer
+    whose output is known in closed form."""
+    rng = np.random.default_rng(33)
+    # candidates: the ranks right after the top-k, by brute force over the order
+    s = rng.random((30, 9))
+    for spec in (O.RouteSpec(k=2), O.RouteSpec(k=3, renorm=False), O.RouteSpec(k=2, n_group=3, topk_group=2)):
+        cand, cw = O.reroute_candidates(s, spec)
+        el = O.eligible(s, spec)
+        for t in range(30):
+            ranked = sorted([e for e in range(9) if el[t, e]], key=lambda e: (-s[t, e], e))
+            want = (ranked[spec.k:2 * spec.k] + [-1] * spec.k)[:spec.k]
+            assert list(cand[t]) == want, (t, list(cand[t]), want)
+            den = sum(s[t, e] for e in ranked[:spec.k]) if spec.renorm else 1.0
+            for m, c in enumerate(want):
+                assert cw[t, m] == (s[t, c] / den if c >= 0 else 0.0)
+    for T, k, E, cap in ((40, 2, 6, 7), (100, 3, 8, 20), (64, 4, 16, 10), (30, 1, 3, 4), (50, 2, 2, 30)):
+        s = rng.random((T, E)) * np.linspace(1.0, 3.0, E)
+        spec = O.RouteSpec(k=k)
+        idx = O.select_topk(s, spec)
+        gw = O.gate_weights(s, idx, True)
+        cand, cw = O.reroute_candidates(s, spec)
+        counts, offsets, perm, inv, gates, served = O.dispatch_reroute(idx, gw, cand, cw, E, cap)
+        drop = O.dispatch(idx, E, cap)
+        assert np.array_equal(counts, drop[0])
+        # a capacity no expert reaches: the dropless layout, every gate its own
+        big = O.dispatch_reroute(idx, gw, cand, cw, E, int(drop[0].max()))
+        full = O.dispatch(idx, E)
+        for u, v in zip(big[:4], full):
+            assert np.array_equal(u, v)
+        assert np.array_equal(big[4], gw)
+        n = T * k
+        a_exp = idx.reshape(-1)
+        own = (drop[3] >= 0)                      # pass 1 keeps what dropping keeps
+        srv = served.reshape(-1)
+        assert np.array_equal(srv[own], a_exp[own])
+        # brute force of pass 2: offers in increasing a take the slots left
+        left = cap - np.minimum(drop[0], cap)
+        want_srv = np.where(own, a_exp, -1)
+        want_g = np.where(own.reshape(T, k), gw, 0.0)
+        # offers ordered by a, one expert at a time
+        offers = {}
+        for t in range(T):
+            over = [j for j in range(k) if not own[t * k + j]]
+            for m, j in enumerate(over):
+                if cand[t, m] >= 0:
+                    offers.setdefault(int(cand[t, m]), []).append((t * k + j, m))
+        for c, lst in offers.items():
+            for a, m in sorted(lst)[:left[c]]:
+                want_srv[a] = c
+                want_g[a // k, a % k] = cw[a // k, m]
+        assert np.array_equal(srv, want_srv)
+        assert np.array_equal(gates, want_g)
+        # rows: per expert its own assignments, then the rerouted ones, each by a
+        for e in range(E):
+            rows = [a for a in range(n) if own[a] and a_exp[a] == e] + \
+                   [a for a in range(n) if not own[a] and srv[a] == e]
+            assert len(rows) <= cap
+            assert np.array_equal(inv[rows], offsets[e] + np.arange(len(rows)))
+            assert np.array_equal(perm[offsets[e]:offsets[e + 1]], np.array(rows, dtype=np.int64) // k)
+        assert np.array_equal(inv >= 0, srv >= 0)
+        assert (inv < 0).sum() <= (drop[3] < 0).sum()
+    # E == k: no candidates, so rerouting drops exactly what dropping drops
+    s = rng.random((20, 3)) * np.array([1.0, 2.0, 5.0])
+    idx = O.select_topk(s, O.RouteSpec(k=3))
+    cand, cw = O.reroute_candidates(s, O.RouteSpec(k=3))
+    assert (cand == -1).all()
+    r = O.dispatch_reroute(idx, O.gate_weights(s, idx, True), cand, cw, 3, 8)
+    d = O.dispatch(idx, 3, 8)
+    for u, v in zip(r[:4], d):
+        assert np.array_equal(u, v)
+    # constructed layer (k = 1, one slot per expert): every token's best expert
+    # is 0 and token t's second best is t + 1, so token 0 is served by expert
+    # 0 with gate 1 and token t > 0 by expert t + 1 with gate s_{t+1} / s_0
+    T, d_, f, E = 6, 8, 16, 7
+    x = rng.standard_normal((T, d_))
+    W = _weights(rng, E, d_, f)
+    wr = np.zeros((E, d_))
+    bias = np.full(E, -30.0)
+    bias[0] = 5.0
+    z = np.tile(bias, (T, 1))
+    for t in range(T):
+        z[t, t + 1] = 1.0 + 0.1 * t
+    # express the per-token logits through x: one-hot rows of x pick them
+    x_route = np.eye(T)
+    wr_route = z.T.copy()
+    spec = O.RouteSpec(k=1)
+    got = O.layer_forward(np.hstack([x_route, x]), np.hstack([wr_route, np.zeros((E, d_))]), None,
+                          spec, E, lambda e: (np.hstack([np.zeros((f, T)), W[e][0]]),
+                                              np.hstack([np.zeros((f, T)), W[e][1]]),
+                                              np.vstack([np.zeros((T, f)), W[e][2]])),
+                          "f32", capacity=1, overflow="reroute")
+    sc = O.expert_scores(z, "softmax")
+    want = np.zeros((T, T + d_))
+    for t in range(T):
+        e, g = (0, 1.0) if t == 0 else (t + 1, sc[t, t + 1] / sc[t, 0])
+        xt = np.hstack([x_route[t], x[t]])[None, :]
+        w1 = np.hstack([np.zeros((f, T)), W[e][0]])
+        w3 = np.hstack([np.zeros((f, T)), W[e][1]])
+        w2 = np.vstack([np.zeros((T, f)), W[e][2]])
+        u, v = xt @ w1.T, xt @ w3.T
+        h = O.round_act(u / (1 + np.exp(-u)) * v, "f32")
+        want[t] = g * O.round_act(h @ w2.T, "f32")[0]
+    assert np.array_equal(got.served.reshape(-1), [0] + [t + 1 for t in range(1, T)])
+    np.testing.assert_allclose(got.out, O.round_act(want, "f32"), rtol=0, atol=1e-6)
+
+
 def _nearest_code_bruteforce(v):
     """Exhaustive nearest E4M3 code of one magnitude, ties to the even mantissa."""
     best = None
@@ -505,7 +613,7 @@ CHECKS = [check_bf16_round, check_decoders, check_router_logits, check_scores,
           check_gates, check_worked_example_counts, check_ep_sizing_and_batch, check_dispatch,
           check_gather, check_dense_special_case, check_identical_experts_closed_form,
           check_uniform_gates_mean, check_combine, check_locality, check_margin_rule,
-          check_capacity, check_fp8_payload]
+          check_capacity, check_fp8_payload, check_reroute]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
@@ -589,6 +697,30 @@ def _m_capacity_keeps_last(topk_idx, E, capacity=0):
     return c, o, p, i
 
 
+_CANDIDATES = M.reroute_candidates
+_REROUTE = M.dispatch_reroute
+
+
+def _m_candidates_skip_one(s, spec):
+    """Offers the rank after the next-best expert."""
+    cand, cw = _CANDIDATES(s, spec)
+    return np.concatenate([cand[:, 1:], np.full((cand.shape[0], 1), -1, np.int32)], axis=1), \
+        np.concatenate([cw[:, 1:], np.zeros((cw.shape[0], 1))], axis=1)
+
+
+def _m_reroute_ignores_pass1(topk_idx, topk_w, cand_idx, cand_w, E, capacity):
+    """Lets the offers use a full capacity on top of the slots pass 1 took."""
+    out = _REROUTE(topk_idx, topk_w, cand_idx, cand_w, E, 2 * capacity)
+    drop = _DISPATCH(topk_idx, E, capacity)
+    return (drop[0],) + out[1:]
+
+
+def _m_reroute_keeps_gate(topk_idx, topk_w, cand_idx, cand_w, E, capacity):
+    """Rerouted copies carry the gate of the expert they were meant for."""
+    c, o, p, i, g, sv = _REROUTE(topk_idx, topk_w, cand_idx, cand_w, E, capacity)
+    return c, o, p, i, np.where(sv >= 0, topk_w, 0.0), sv
+
+
 _RNE_E4M3 = M._rne_e4m3_magnitude
 _QUANT_FP8 = M.quantize_fp8_blocks
 
@@ -642,6 +774,9 @@ MUTATIONS = [
     ("_rne_e4m3_magnitude", _m_e4m3_truncate),
     ("quantize_fp8_blocks", _m_fp8_scale_low),
     ("round_bf16", _m_round_truncate),
+    ("reroute_candidates", _m_candidates_skip_one),
+    ("dispatch_reroute", _m_reroute_ignores_pass1),
+    ("dispatch_reroute", _m_reroute_keeps_gate),
 ]
 
 
