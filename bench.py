@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens for the oracle timing")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="expert capacity = factor * T * k / E slots (0: dropless); overflow is dropped")
+    p.add_argument("--overflow", choices=("drop", "reroute"), default="drop",
+                   help="with --capacity-factor: drop overflow assignments, or reroute them to the token's "
+                        "next-best expert first")
     p.add_argument("--dispatch-fp8", action="store_true",
                    help="dispatch the block-scaled E4M3 payload of x (fp8 x fp8 gate-up GEMM with E4M3 weights)")
     p.add_argument("--graph", action="store_true",
@@ -151,7 +154,7 @@ def cpu_baseline(w, L, host_experts, sample):
     cap = O.expert_capacity(getattr(w, "capacity_factor", 0), sample, w.k, w.E)
     t0 = time.perf_counter()
     O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap,
-                    fp8_dispatch=w.dispatch_fp8)
+                    fp8_dispatch=w.dispatch_fp8, overflow=w.overflow)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
@@ -181,6 +184,8 @@ def main():
         w = w.scaled(capacity_factor=args.capacity_factor)
     if args.dispatch_fp8:
         w = w.scaled(dispatch_fp8=True)
+    if args.overflow != "drop":
+        w = w.scaled(overflow=args.overflow)
     L = LayerInputs(w, seed)
     host_experts = {}
 
@@ -256,8 +261,11 @@ def main():
     c = counts.cpu().numpy()
     assert int(c.sum()) == w.T * w.k, "routing lost assignments"
     cap = desc.capacity
-    kept = np.minimum(c, cap) if cap > 0 else c
-    n_assign = int(kept.sum())  # rows the experts process
+    rows_dev = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    moe.layer_rows(desc, ws, rows_dev)
+    kept = rows_dev.cpu().numpy()
+    n_assign = int(kept.sum())  # rows the experts process (dropped ones removed, rerouted ones added)
+    own_kept = int(np.minimum(c, cap).sum()) if cap > 0 else n_assign
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = w.T * args.steps / elapsed
@@ -303,7 +311,8 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
                    "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
-                   "capacity_factor": w.capacity_factor, "dispatch_fp8": w.dispatch_fp8,
+                   "capacity_factor": w.capacity_factor, "overflow": w.overflow,
+                   "dispatch_fp8": w.dispatch_fp8,
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": roof,
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
@@ -314,7 +323,8 @@ def main():
         "load": {"max_over_mean": round(float(c.max() / c.mean()), 3),
                  "experts_touched": int((c > 0).sum()), "experts": w.E},
         "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,
-                     "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5)},
+                     "overflow": w.overflow, "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5),
+                     "rerouted_fraction": round((n_assign - own_kept) / (w.T * w.k), 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -90,11 +90,36 @@ typedef struct {
                          capacity_factor * T * k / E, rounded up by the caller.
                          Assignments claim slots in increasing a = t*k + j; one
                          that finds its expert full is dropped (contributes 0) */
+  int32_t overflow;   /* with a capacity: MOE_OVERFLOW_DROP (0) drops an
+                         assignment that finds its expert full;
+                         MOE_OVERFLOW_REROUTE (1) first offers it the token's
+                         next-best expert (see "Capacity overflow" below;
+                         moe_layer_forward only)                              */
   int32_t dispatch_fp8; /* 0: the dispatched rows are x itself (act dtype);
                          1: they are the block-scaled E4M3 payload of x (act
                          must be MOE_BF16; see "fp8 dispatch payload" below).
                          The router and the shared expert always read x.    */
 } moe_desc;
+
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow;
+
+/* Capacity overflow rerouted (capacity > 0, overflow = MOE_OVERFLOW_REROUTE).
+ * "Expert-Parallel MoE Inference", section "Capacity factor and token
+ * dropping": overflow tokens are dropped or rerouted to their next-best
+ * expert.  Two passes over the assignments a = t*k + j:
+ *   1. each claims a slot of its own expert in increasing a (as dropping);
+ *   2. the m-th assignment of a token that found its expert full (counting in
+ *      increasing j) is offered the token's candidate m -- its eligible
+ *      expert of rank k + m in the router's order (score descending, id
+ *      ascending) -- and the offers claim the slots left after pass 1, in
+ *      increasing a.  An offer with no slot, or an overflow with no
+ *      candidate, is dropped.
+ * A rerouted copy carries its new expert's gate: the expert's score, divided
+ * by the sum of the token's top-k scores when renorm = 1.  Rows of an expert
+ * are its pass-1 rows, then its pass-2 rows, each in increasing a.  counts
+ * stay the demand of the top-k; topk_idx and topk_w stay the router's top-k.
+ * Only moe_layer_forward takes this mode; moe_dispatch returns
+ * MOE_ERR_UNSUPPORTED for it (the router stage does not return candidates). */
 
 /* fp8 dispatch payload (dispatch_fp8 = 1).  Each row of x is cut into blocks
  * of 32 elements; a block with largest magnitude amax gets the scale 2^s, s
@@ -213,6 +238,16 @@ moe_status moe_layer_forward(const moe_desc* desc, const void* x, const void* w_
                              const void* sw1, const void* sw3, const void* sw2,
                              void* out, int32_t* topk_idx, float* topk_w, int32_t* counts,
                              void* ws, size_t ws_bytes, void* stream, void* const* trace);
+
+/* Rows each expert processed in the last moe_layer_forward enqueued with this
+ * workspace (same desc, same stream, before this call):
+ *   rows[e] = offsets[e+1] - offsets[e]                       int32 [E], device
+ * The demand (counts) less the assignments dropped, plus, when rerouting,
+ * those rerouted to e: the capacity's drop-rate metric ("Expert-Parallel MoE
+ * Inference", section "Capacity factor and token dropping").  Enqueued on
+ * `stream`; ws and ws_bytes as given to moe_layer_forward. */
+moe_status moe_layer_rows(const moe_desc* desc, const void* ws, size_t ws_bytes, int32_t* rows,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,9 +26,11 @@ TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "
 
 # the exported symbols include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_grouped_ffn", "moe_combine", "moe_layer_forward")
+           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows")
 
 _DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
+OVERFLOW_DROP, OVERFLOW_REROUTE = 0, 1
+_OVERFLOW = {"drop": OVERFLOW_DROP, "reroute": OVERFLOW_REROUTE}
 
 
 class MoeError(RuntimeError):
@@ -53,23 +55,25 @@ def capacity_slots(capacity_factor, T: int, k: int, E: int) -> int:
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "f", "E", "k", "score", "renorm", "n_group", "topk_group",
-                 "f_shared", "act", "wdtype", "capacity", "dispatch_fp8")]
+                 "f_shared", "act", "wdtype", "capacity", "overflow", "dispatch_fp8")]
 
     @classmethod
     def make(cls, T, d, f, E, k, score="softmax", renorm=True, n_group=0, topk_group=0,
-             f_shared=0, act="bf16", wdtype="bf16", capacity=0, dispatch_fp8=False) -> "Desc":
+             f_shared=0, act="bf16", wdtype="bf16", capacity=0, dispatch_fp8=False,
+             overflow="drop") -> "Desc":
         return cls(T, d, f, E, k, SOFTMAX if score == "softmax" else SIGMOID, int(bool(renorm)),
                    n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype], capacity,
-                   int(bool(dispatch_fp8)))
+                   _OVERFLOW[overflow], int(bool(dispatch_fp8)))
 
     @classmethod
     def from_attrs(cls, w) -> "Desc":
         """From any object with T, d, f, E, k, score, renorm, n_group,
         topk_group, f_shared, act and wdt attributes (and optionally
-        capacity_factor and dispatch_fp8)."""
+        capacity_factor, overflow and dispatch_fp8)."""
         cap = capacity_slots(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
         return cls.make(w.T, w.d, w.f, w.E, w.k, w.score, w.renorm, w.n_group, w.topk_group,
-                        w.f_shared, w.act, w.wdt, cap, getattr(w, "dispatch_fp8", False))
+                        w.f_shared, w.act, w.wdt, cap, getattr(w, "dispatch_fp8", False),
+                        getattr(w, "overflow", "drop"))
 
 
 # The fp8 dispatch payload of R rows of width d (moe.h): E4M3 codes [R][d] at
@@ -116,6 +120,7 @@ def _lib() -> ctypes.CDLL:
         lib.moe_grouped_ffn.argtypes = [D] + [_P] * 11 + [ctypes.c_size_t, _P]
         lib.moe_combine.argtypes = [D, _P, _P, _P, _P, _P, _P]
         lib.moe_layer_forward.argtypes = [D] + [_P] * 17 + [ctypes.c_size_t, _P, _P]
+        lib.moe_layer_rows.argtypes = [D, _P, ctypes.c_size_t, _P, _P]
         for name in EXPORTS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -205,3 +210,10 @@ def layer_forward(desc, x, w_router, bias, w1, w3, w2, s1, s3, s2, sw1, sw3, sw2
         _ptr(s1), _ptr(s3), _ptr(s2), _ptr(sw1), _ptr(sw3), _ptr(sw2), _ptr(out), _ptr(topk_idx),
         _ptr(topk_w), _ptr(counts), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream), tr), "moe_layer_forward")
+
+
+def layer_rows(desc, ws, rows, stream=None):
+    """rows [E] int32 (device): rows each expert processed in the last
+    layer_forward run with this workspace."""
+    _check(_lib().moe_layer_rows(ctypes.byref(desc), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _ptr(rows), _stream(stream)), "moe_layer_rows")

@@ -17,6 +17,17 @@
 //      a time; a lane's rank among earlier lanes with the same expert comes
 //      from ballot equality masks, so rows within an expert follow the
 //      assignment order a = t*k + j (increasing token).
+//
+// With a capacity and overflow rerouted ("Expert-Parallel MoE Inference",
+// section "Capacity factor and token dropping": overflow goes to the token's
+// next-best expert) the dispatch runs two passes:
+//   1. histogram and scan as above; the scatter only ranks each assignment
+//      within its own expert (rank < capacity: it keeps a slot there);
+//   2. per token, its m-th overflowed assignment (increasing j) is offered
+//      the token's candidate m; a histogram and a scan of the offers per
+//      expert against the slots pass 1 left, then one scatter lays out each
+//      expert's pass-1 rows followed by its accepted offers, both in
+//      increasing a.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -25,16 +36,20 @@ namespace {
 constexpr int kMaxE = 512;
 constexpr int kIdBits = 10;  // ids 0..512 (512 marks an idle lane)
 
-__global__ __launch_bounds__(64) void histogram_kernel(DispatchArgs a) {
+// keys[i] in [0, E), or negative (not counted); per-chunk counts to out.
+__global__ __launch_bounds__(64) void histogram_kernel(DispatchArgs a, const int32_t* keys, int32_t* out) {
   __shared__ int bins[kMaxE];
   const int lane = threadIdx.x;
   for (int e = lane; e < a.E; e += 64) bins[e] = 0;
   __syncthreads();
   const int base = blockIdx.x * kDispatchChunk;
   const int end = min(base + kDispatchChunk, a.n_assign);
-  for (int i = base + lane; i < end; i += 64) atomicAdd(&bins[a.topk_idx[i]], 1);
+  for (int i = base + lane; i < end; i += 64) {
+    const int e = keys[i];
+    if (e >= 0) atomicAdd(&bins[e], 1);
+  }
   __syncthreads();
-  for (int e = lane; e < a.E; e += 64) a.chunk_cnt[(size_t)blockIdx.x * a.E + e] = bins[e];
+  for (int e = lane; e < a.E; e += 64) out[(size_t)blockIdx.x * a.E + e] = bins[e];
 }
 
 __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunks) {
@@ -79,7 +94,10 @@ __global__ __launch_bounds__(kMaxE) void scan_kernel(DispatchArgs a, int n_chunk
   if (e == a.E - 1) a.offsets[a.E] = tot[e];
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
+// rank_out == NULL: rows and inv_pos as described above.  Otherwise only the
+// rank of each assignment within its expert goes to rank_out (pass 1 of the
+// rerouting dispatch).
+__global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a, int32_t* rank_out) {
   __shared__ int next_row[kMaxE];  // rank within the expert of the chunk's next assignment
   const int lane = threadIdx.x;
   for (int e = lane; e < a.E; e += 64) next_row[e] = a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
@@ -104,7 +122,9 @@ __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
     const bool last = (same >> lane) == 1ull;  // highest lane of its group
     if (valid && last) next_row[e] = rel + 1;
     __syncthreads();
-    if (valid) {
+    if (valid && rank_out) {
+      rank_out[i] = rel;
+    } else if (valid) {
       if (rel < a.cap) {  // a free slot of its expert
         const int row = a.offsets[e] + rel;
         a.inv_pos[i] = row;
@@ -112,6 +132,105 @@ __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a) {
       } else {
         a.inv_pos[i] = -1;  // the expert is full: dropped
       }
+    }
+  }
+}
+
+// Pass 2 offers, one thread per token: the m-th assignment of the token that
+// found its own expert full (increasing j) is offered candidate m; the gate of
+// every assignment is that of the copy that would serve it.
+__global__ __launch_bounds__(256) void reroute_offer_kernel(DispatchArgs a, RerouteArgs r, int T) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int m = 0;
+  for (int j = 0; j < a.k; ++j) {
+    const int i = t * a.k + j;
+    if (r.rel[i] < a.cap) {
+      r.target[i] = -1;
+      r.gate[i] = r.topk_w[i];
+    } else {
+      r.target[i] = r.cand_idx[t * a.k + m];
+      r.gate[i] = r.cand_w[t * a.k + m];
+      ++m;
+    }
+  }
+}
+
+// Pass 2 scan: per expert, the offers before each chunk (relative), how many
+// fit in the slots pass 1 left, and the offsets of pass-1 + pass-2 rows.
+__global__ __launch_bounds__(kMaxE) void reroute_scan_kernel(DispatchArgs a, RerouteArgs r, int n_chunks) {
+  __shared__ int tot[kMaxE];
+  const int e = threadIdx.x;
+  int run = 0, kept = 0;
+  if (e < a.E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      int* p = r.chunk_cnt2 + (size_t)c * a.E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    const int kept1 = min(a.counts[e], a.cap);
+    kept = kept1 + min(run, a.cap - kept1);
+  }
+  tot[e] = kept;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = (e >= off) ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < a.E) a.offsets[e] = tot[e] - kept;
+  if (e == a.E - 1) a.offsets[a.E] = tot[e];
+}
+
+// Pass 2 scatter: an assignment ranked below the capacity takes row
+// offsets[e] + rank; an offer to c takes row offsets[c] + kept1[c] + its rank
+// among the offers to c, if that is below the slots pass 1 left; anything
+// else is dropped.  Offer ranks follow a, as in scatter_kernel.
+__global__ __launch_bounds__(64) void reroute_scatter_kernel(DispatchArgs a, RerouteArgs r) {
+  __shared__ int next_row[kMaxE];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < a.E; e += 64) next_row[e] = r.chunk_cnt2[(size_t)blockIdx.x * a.E + e];
+  __syncthreads();
+  const int base = blockIdx.x * kDispatchChunk;
+  const int end = min(base + kDispatchChunk, a.n_assign);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = base; s < end; s += 64) {
+    const int i = s + lane;
+    const bool valid = i < end;
+    const int c = valid ? r.target[i] : -1;
+    const int key = c >= 0 ? c : kMaxE;  // kMaxE: not an offer
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
+    const int rel2 = (c >= 0) ? next_row[c] + rank : 0;
+    __syncthreads();
+    const bool last = (same >> lane) == 1ull;
+    if (c >= 0 && last) next_row[c] = rel2 + 1;
+    __syncthreads();
+    if (!valid) continue;
+    const int rel = r.rel[i];
+    if (rel < a.cap) {
+      const int row = a.offsets[a.topk_idx[i]] + rel;
+      a.inv_pos[i] = row;
+      a.perm_token[row] = i / a.k;
+    } else if (c >= 0) {
+      const int kept1 = min(a.counts[c], a.cap);
+      if (rel2 < a.cap - kept1) {
+        const int row = a.offsets[c] + kept1 + rel2;
+        a.inv_pos[i] = row;
+        a.perm_token[row] = i / a.k;
+      } else {
+        a.inv_pos[i] = -1;
+      }
+    } else {
+      a.inv_pos[i] = -1;
     }
   }
 }
@@ -132,6 +251,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
   }
 }
 
+__global__ __launch_bounds__(256) void segment_rows_kernel(const int32_t* offsets, int E, int32_t* rows) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) rows[e] = offsets[e + 1] - offsets[e];
+}
+
 __global__ void zero_counts_kernel(DispatchArgs a) {
   const int e = threadIdx.x;
   if (e < a.E) a.counts[e] = 0;
@@ -146,9 +270,29 @@ hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int n_chunks = (a.n_assign + kDispatchChunk - 1) / kDispatchChunk;
-  hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a, a.topk_idx, a.chunk_cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, n_chunks);
-  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a, (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_reroute(const DispatchArgs& a, const RerouteArgs& r, hipStream_t s) {
+  if (a.n_assign == 0) return launch_dispatch_index(a, s);
+  const int n_chunks = (a.n_assign + kDispatchChunk - 1) / kDispatchChunk;
+  const int T = a.n_assign / a.k;
+  hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a, a.topk_idx, a.chunk_cnt);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, n_chunks);
+  hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a, r.rel);
+  hipLaunchKernelGGL(reroute_offer_kernel, dim3((T + 255) / 256), dim3(256), 0, s, a, r, T);
+  hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a, (const int32_t*)r.target,
+                     r.chunk_cnt2);
+  hipLaunchKernelGGL(reroute_scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, r, n_chunks);
+  hipLaunchKernelGGL(reroute_scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_rows(const int32_t* offsets, int E, int32_t* rows, hipStream_t s) {
+  hipLaunchKernelGGL(segment_rows_kernel, dim3((E + 255) / 256), dim3(256), 0, s, offsets, E, rows);
   return hipGetLastError();
 }
 

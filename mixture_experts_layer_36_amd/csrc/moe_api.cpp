@@ -54,12 +54,16 @@ moe_status check_desc(const moe_desc* d) {
   if (d->d % 128 != 0 || d->f % 128 != 0 || d->f_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (int64_t(d->T) * d->k >= kMaxAssign) return MOE_ERR_UNSUPPORTED;
   if (d->capacity < 0) return MOE_ERR_INVALID;
+  if (d->overflow != MOE_OVERFLOW_DROP && d->overflow != MOE_OVERFLOW_REROUTE) return MOE_ERR_INVALID;
   if (d->dispatch_fp8 != 0 && d->dispatch_fp8 != 1) return MOE_ERR_INVALID;
   if (d->dispatch_fp8 && d->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 int64_t n_assign(const moe_desc* d) { return int64_t(d->T) * d->k; }
+
+// Capacity overflow rerouted to the next-best expert (moe_layer_forward).
+bool reroute(const moe_desc* d) { return d->capacity > 0 && d->overflow == MOE_OVERFLOW_REROUTE; }
 
 int gemm_dtype(int moe_dt) {
   return moe_dt == MOE_F32 ? GD_F32 : moe_dt == MOE_BF16 ? GD_BF16 : GD_FP8;
@@ -114,6 +118,8 @@ struct Carve {
 struct RouteWs {
   float* z;    // [ksplit][T][E] partial logits
   int ksplit;
+  int32_t* cand_idx;  // reroute candidates [T][k] (NULL: not rerouting)
+  float* cand_w;
 };
 
 // Split-K factor of the router GEMM: enough blocks to fill the GPU when T*E
@@ -150,6 +156,7 @@ int route_splits(const moe_desc* d) {
 }
 struct DispatchWs {
   int32_t* chunk_cnt;
+  RerouteArgs rr;     // rerouting workspace (pointers NULL when not rerouting)
 };
 struct FfnWs {
   int32_t* table;
@@ -172,13 +179,27 @@ struct LayerWs {
   void* sy;
 };
 
-RouteWs carve_route(Carve& c, const moe_desc* d) {
+RouteWs carve_route(Carve& c, const moe_desc* d, bool with_candidates) {
   const int ks = route_splits(d);
-  return RouteWs{c.take<float>(sizeof(float) * size_t(ks) * d->T * d->E), ks};
+  RouteWs w{c.take<float>(sizeof(float) * size_t(ks) * d->T * d->E), ks, nullptr, nullptr};
+  if (with_candidates) {
+    w.cand_idx = c.take<int32_t>(sizeof(int32_t) * size_t(n_assign(d)));
+    w.cand_w = c.take<float>(sizeof(float) * size_t(n_assign(d)));
+  }
+  return w;
 }
-DispatchWs carve_dispatch(Carve& c, const moe_desc* d) {
+DispatchWs carve_dispatch(Carve& c, const moe_desc* d, bool rerouting) {
   const int64_t chunks = (n_assign(d) + kDispatchChunk - 1) / kDispatchChunk;
-  return DispatchWs{c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E)};
+  DispatchWs w{};
+  w.chunk_cnt = c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E);
+  if (rerouting) {
+    const size_t A = size_t(n_assign(d));
+    w.rr.chunk_cnt2 = c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E);
+    w.rr.rel = c.take<int32_t>(sizeof(int32_t) * A);
+    w.rr.target = c.take<int32_t>(sizeof(int32_t) * A);
+    w.rr.gate = c.take<float>(sizeof(float) * A);
+  }
+  return w;
 }
 // The shared expert joins the routed grouped GEMMs as one more segment when
 // its weights have the routed weights' dtype.
@@ -206,8 +227,8 @@ bool fuse_gather(const moe_desc* d) {
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
   LayerWs w;
   const size_t A = n_assign(d), ab = act_bytes(d);
-  w.route = carve_route(c, d);
-  w.disp = carve_dispatch(c, d);
+  w.route = carve_route(c, d, reroute(d));
+  w.disp = carve_dispatch(c, d, reroute(d));
   w.ffn = carve_ffn(c, d, fuse_shared(d));
   w.perm_token = c.take<int32_t>(sizeof(int32_t) * A);
   w.inv_pos = c.take<int32_t>(sizeof(int32_t) * A);
@@ -233,8 +254,8 @@ void* carve_ffn_xdq(Carve& c, const moe_desc* d) {
 size_t stage_bytes(const moe_desc* d, moe_stage stage) {
   Carve c(nullptr);
   switch (stage) {
-    case MOE_STAGE_ROUTE: carve_route(c, d); break;
-    case MOE_STAGE_DISPATCH: carve_dispatch(c, d); break;
+    case MOE_STAGE_ROUTE: carve_route(c, d, false); break;
+    case MOE_STAGE_DISPATCH: carve_dispatch(c, d, false); break;
     case MOE_STAGE_FFN:
       carve_ffn(c, d, false);
       carve_ffn_xdq(c, d);
@@ -269,16 +290,18 @@ moe_status run_route(const moe_desc* d, const void* x, const void* wr, const flo
   g.ksplit = ws.ksplit;
   MOE_TRY(dev(launch_gemm(g, s)));
   RouteSelectArgs r{ws.z, ws.ksplit, d->T, d->E, d->k, d->score, d->renorm, d->n_group, d->topk_group,
-                    idx, w};
+                    idx, w, ws.cand_idx, ws.cand_w};
   return dev(launch_route_select(r, s));
 }
 
+// rr: the rerouting dispatch's inputs (router gates and candidates) and
+// workspace, or NULL for the dispatch of section "Dispatch" of moe.h.
 moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, int32_t* counts,
                         int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
-                        const DispatchWs& ws, hipStream_t s) {
+                        const DispatchWs& ws, hipStream_t s, const RerouteArgs* rr = nullptr) {
   DispatchArgs a{idx, int(n_assign(d)), d->E, d->k, ws.chunk_cnt, counts, offsets, perm_token, inv_pos,
                  d->capacity > 0 ? d->capacity : INT32_MAX};
-  MOE_TRY(dev(launch_dispatch_index(a, s)));
+  MOE_TRY(dev(rr ? launch_dispatch_reroute(a, *rr, s) : launch_dispatch_index(a, s)));
   if (x_perm == nullptr) return MOE_OK;  // fused gather: GEMM1 reads x through perm_token
   // the gather stops at offsets[E] (the rows kept), read on the device
   return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), offsets + d->E, int(d->d * act_bytes(d)),
@@ -471,7 +494,7 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
     return MOE_ERR_INVALID;
   if (ws_bytes < stage_bytes(d, MOE_STAGE_ROUTE)) return MOE_ERR_WORKSPACE;
   Carve c(ws);
-  const RouteWs w = carve_route(c, d);
+  const RouteWs w = carve_route(c, d, false);
   return run_route(d, x, w_router, bias, topk_idx, topk_w, w, static_cast<hipStream_t>(stream));
 }
 
@@ -479,13 +502,14 @@ moe_status moe_dispatch(const moe_desc* d, const int32_t* topk_idx, const void* 
                         int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
                         void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_desc(d));
+  if (reroute(d)) return MOE_ERR_UNSUPPORTED;  // needs the router's candidates: moe_layer_forward only
   if (!need(counts) || !need(offsets)) return MOE_ERR_INVALID;
   if (d->T > 0 && (!need(topk_idx) || !need(x) || !need(perm_token) || !need(inv_pos) ||
                    !need(x_perm) || !need(ws)))
     return MOE_ERR_INVALID;
   if (d->T > 0 && ws_bytes < stage_bytes(d, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
   Carve c(ws);
-  const DispatchWs w = carve_dispatch(c, d);
+  const DispatchWs w = carve_dispatch(c, d, false);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!d->dispatch_fp8)
     return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w, s);
@@ -567,8 +591,12 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(run_route(d, x, w_router, bias, topk_idx, topk_w, w.route, s));
   MOE_TRY(record(trace, 1, s));
   const bool fg = fuse_gather(d);  // GEMM1 reads its rows through perm_token
+  RerouteArgs rr = w.disp.rr;
+  rr.topk_w = topk_w;
+  rr.cand_idx = w.route.cand_idx;
+  rr.cand_w = w.route.cand_w;
   MOE_TRY(run_dispatch(d, topk_idx, x, counts, w.offsets, w.perm_token, w.inv_pos,
-                       d->dispatch_fp8 ? nullptr : w.x_perm, w.disp, s));
+                       d->dispatch_fp8 ? nullptr : w.x_perm, w.disp, s, reroute(d) ? &rr : nullptr));
   // GEMM1's activation rows: x, the gathered x_perm, or the fp8 payload (in
   // token order when the gather is fused, else gathered), as codes when the
   // GEMM takes fp8 activations, else as bf16 values
@@ -601,10 +629,26 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(record(trace, 4, s));
   if (shared && !fused) MOE_TRY(run_shared(d, x, sw1, sw3, sw2, w.sh, w.sy, s));
   MOE_TRY(record(trace, 5, s));
-  CombineArgs a{w.y_perm, w.inv_pos, topk_w, shared ? w.sy : nullptr, out, d->T, d->d, d->k,
-                gemm_dtype(d->act)};
+  // a rerouted copy carries its new expert's gate
+  CombineArgs a{w.y_perm, w.inv_pos, reroute(d) ? rr.gate : topk_w, shared ? w.sy : nullptr, out, d->T, d->d,
+                d->k, gemm_dtype(d->act)};
   MOE_TRY(dev(launch_combine(a, s)));
   return record(trace, 6, s);
+}
+
+moe_status moe_layer_rows(const moe_desc* d, const void* ws, size_t ws_bytes, int32_t* rows, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!need(rows)) return MOE_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->T == 0) {  // moe_layer_forward laid out no rows
+    DispatchArgs a{nullptr, 0, d->E, d->k, nullptr, rows, nullptr, nullptr, nullptr, INT32_MAX};
+    return dev(launch_dispatch_index(a, s));
+  }
+  if (!need(ws)) return MOE_ERR_INVALID;
+  if (ws_bytes < stage_bytes(d, MOE_STAGE_LAYER)) return MOE_ERR_WORKSPACE;
+  Carve c(const_cast<void*>(ws));
+  const LayerWs w = carve_layer(c, d);
+  return dev(launch_segment_rows(w.offsets, d->E, rows, s));
 }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ struct RouteSelectArgs {
   int T, E, k, score, renorm, n_group, topk_group;
   int32_t* topk_idx;     // [T][k]
   float* topk_w;         // [T][k]
+  // Optional (nullable): the token's eligible experts of rank k .. 2k-1 (-1
+  // past the eligible ones) and their gates (score / sum of the top-k scores
+  // when renorm, else the score): the reroute candidates.
+  int32_t* cand_idx;     // [T][k]
+  float* cand_w;         // [T][k]
 };
 hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s);
 
@@ -68,6 +73,25 @@ struct DispatchArgs {
   int cap;                  // slots per expert (INT32_MAX: dropless)
 };
 hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
+
+// Capacity with overflow rerouted: the two-pass dispatch.  Inputs: the
+// DispatchArgs above (cap < INT32_MAX), the router's gates and the reroute
+// candidates; workspace: chunk_cnt2 [n_chunks][E], rel and target [n_assign].
+// Output besides counts/offsets/perm_token/inv_pos: gate [n_assign], the gate
+// of the copy that serves each assignment (combine reads it as its topk_w).
+struct RerouteArgs {
+  const float* topk_w;      // [T*k]
+  const int32_t* cand_idx;  // [T*k]
+  const float* cand_w;      // [T*k]
+  int32_t* chunk_cnt2;
+  int32_t* rel;             // rank of each assignment within its own expert
+  int32_t* target;          // candidate offered to an overflowed assignment, else -1
+  float* gate;              // [T*k]
+};
+hipError_t launch_dispatch_reroute(const DispatchArgs& a, const RerouteArgs& r, hipStream_t s);
+
+// rows[e] = offsets[e+1] - offsets[e], e < E.
+hipError_t launch_segment_rows(const int32_t* offsets, int E, int32_t* rows, hipStream_t s);
 
 // x_perm[p] = x[perm_token[p]] for p < min(rows, *rows_dev) (rows_dev: device
 // row count, nullable), rows of row_bytes (multiple of 16).

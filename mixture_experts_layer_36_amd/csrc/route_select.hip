@@ -159,34 +159,41 @@ __global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectAr
     }
   }
 
-  // top-k: k rounds of wave-wide maximum; the owner retires the winner
+  // top-k: k rounds of wave-wide maximum; the owner retires the winner.
+  // With reroute candidates, k more rounds rank the next eligible experts
+  // (a round whose maximum is 0 found none left).
+  const int rounds = a.cand_idx ? 2 * a.k : a.k;
   uint64_t mine_key = 0ull;  // lane j keeps the j-th winner
-  for (int j = 0; j < a.k; ++j) {
+  for (int j = 0; j < rounds; ++j) {
     uint64_t best = 0ull;
 #pragma unroll
     for (int v = 0; v < kMaxV; ++v) best = key[v] > best ? key[v] : best;
     best = wave_max_u64(best);
 #pragma unroll
     for (int v = 0; v < kMaxV; ++v)
-      if (key[v] == best) key[v] = 0ull;
+      if (best != 0ull && key[v] == best) key[v] = 0ull;
     if (lane == j) mine_key = best;
   }
 
   const bool sel = lane < a.k;
+  const bool cand = !sel && lane < rounds && mine_key != 0ull;
   const int e_sel = (int)(~(uint32_t)mine_key);
   const float z_sel = from_ordered_bits((uint32_t)(mine_key >> 32));
-  float g;
-  if (a.score == 0) {
-    g = sel ? expf(z_sel - zmax) : 0.f;
-    const float denom = a.renorm ? wave_sum(g) : esum;
-    g = g / denom;
-  } else {
-    g = sel ? 1.f / (1.f + expf(-z_sel)) : 0.f;
-    if (a.renorm) g = g / wave_sum(g);
-  }
+  // raw scores of the chosen (and candidate) experts; gates divide by the sum
+  // over the chosen k (renorm), by the softmax sum, or by 1
+  float r = 0.f;
+  if (sel || cand) r = (a.score == 0) ? expf(z_sel - zmax) : 1.f / (1.f + expf(-z_sel));
+  float denom = 1.f;
+  if (a.renorm) denom = wave_sum(sel ? r : 0.f);
+  else if (a.score == 0) denom = esum;
+  const float g = r / denom;
   if (live && sel) {
     a.topk_idx[(size_t)t * a.k + lane] = e_sel;
     a.topk_w[(size_t)t * a.k + lane] = g;
+  }
+  if (live && a.cand_idx && !sel && lane < rounds) {
+    a.cand_idx[(size_t)t * a.k + lane - a.k] = cand ? e_sel : -1;
+    a.cand_w[(size_t)t * a.k + lane - a.k] = cand ? g : 0.f;
   }
 }
 

@@ -272,11 +272,14 @@ def route(x, w_router, bias, spec: RouteSpec):
     return idx, gate_weights(s, idx, spec.renorm), s
 
 
-def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3) -> np.ndarray:
+def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3,
+                        ranks: int = 0, rank_margin: Optional[float] = None) -> np.ndarray:
     """Rows whose routing decisions are separated by at least ``margin``:
     the k-th vs (k+1)-th eligible expert score and, with a group limit, the
-    topk_group-th vs next group score.  Used to redraw synthetic token rows so
-    that a float32 router must reach the same decisions as this one."""
+    topk_group-th vs next group score.  With ranks > k (reroute candidates),
+    also every adjacent pair of eligible scores from rank k to rank ranks,
+    by ``rank_margin`` (default ``margin``).  Used to redraw synthetic token
+    rows so that a float32 router must reach the same decisions as this one."""
     s = expert_scores(router_logits(x, w_router, bias), spec.score)
     T, E = s.shape
     ok = np.ones(T, dtype=bool)
@@ -284,6 +287,10 @@ def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3
     srt = -np.sort(-masked, axis=1)
     if spec.k < E and np.isfinite(srt[:, spec.k]).all():
         ok &= (srt[:, spec.k - 1] - srt[:, spec.k]) >= margin
+    rm = margin if rank_margin is None else rank_margin
+    for i in range(spec.k, min(ranks, E - 1)):
+        hi, lo = srt[:, i], srt[:, i + 1]
+        ok &= ~np.isfinite(lo) | ((hi - lo) >= rm)
     if spec.n_group and spec.topk_group < spec.n_group:
         g = -np.sort(-group_scores(s, spec.n_group), axis=1)
         ok &= (g[:, spec.topk_group - 1] - g[:, spec.topk_group]) >= margin

@@ -33,6 +33,7 @@ class Workload:
     bias_scale: float  # router bias b_e = -bias_scale * ln(rank_e); 0 = no bias
     capacity_factor: float = 0.0  # 0 = dropless; else slots = ceil(cf * T * k / E)
     dispatch_fp8: bool = False    # dispatched rows as the block-scaled E4M3 payload
+    overflow: str = "drop"        # with a capacity: "drop" or "reroute" (next-best expert)
 
     @property
     def assignments(self) -> int:

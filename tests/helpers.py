@@ -45,7 +45,8 @@ def oracle_layer(L: LayerInputs, tokens=None) -> O.LayerResult:
     assert tokens is None or cap == 0, "a capacity couples the tokens: no subsets"
     return O.layer_forward(x, wr, b, O.workload_spec(w), w.E, ew, w.act,
                            O.adapters.decoded_shared(L), capacity=cap,
-                           fp8_dispatch=getattr(w, "dispatch_fp8", False))
+                           fp8_dispatch=getattr(w, "dispatch_fp8", False),
+                           overflow=getattr(w, "overflow", "drop"))
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

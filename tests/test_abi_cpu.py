@@ -59,12 +59,19 @@ def test_status_strings():
     (dict(n_group=4, topk_group=2, k=3), moe.MOE_OK),
     (dict(capacity=5), moe.MOE_OK),
     (dict(capacity=-1), moe.MOE_ERR_INVALID),
+    (dict(capacity=5, overflow="reroute"), moe.MOE_OK),
     (dict(dispatch_fp8=True, act="bf16", wdtype="e4m3"), moe.MOE_OK),
     (dict(dispatch_fp8=True, act="bf16", wdtype="bf16"), moe.MOE_OK),
     (dict(dispatch_fp8=True, act="f32", wdtype="f32"), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_validate(kw, code):
     assert moe.validate(_good(**kw)) == code
+
+
+def test_overflow_mode_is_drop_or_reroute():
+    d = _good(capacity=5)
+    d.overflow = 2
+    assert moe.validate(d) == moe.MOE_ERR_INVALID
 
 
 def test_dispatch_fp8_flag_is_0_or_1():

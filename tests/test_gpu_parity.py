@@ -64,6 +64,20 @@ CASES = {
     "mixtral_f8d": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384, dispatch_fp8=True),
     "mixtral_big_f8d": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6, dispatch_fp8=True),
     "decode_f8d": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, dispatch_fp8=True),
+    # capacity overflow rerouted to the next-best expert: every GEMM path, the
+    # group limit and the shared expert, the fp8 payload, and a case where
+    # some tokens have fewer candidates than overflows (E = 5, k = 3)
+    "mixtral_cap_rr": MIXTRAL_PREFILL.scaled(T=300, d=256, f=384, capacity_factor=1.0, overflow="reroute"),
+    "mixtral_big_cap_rr": MIXTRAL_PREFILL.scaled(T=1500, d=384, f=384, E=6, capacity_factor=1.0,
+                                                 overflow="reroute"),
+    "dsv3_skew_cap_rr": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128, capacity_factor=1.0,
+                                                 overflow="reroute"),
+    "qwen_fp8_cap_rr": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32, capacity_factor=1.25, overflow="reroute"),
+    "qwen_f8d_cap_rr": QWEN_FP8_SKEW.scaled(T=800, d=512, f=384, E=16, k=4, capacity_factor=1.25,
+                                            dispatch_fp8=True, overflow="reroute"),
+    "decode_cap_rr": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, capacity_factor=1.0,
+                                        overflow="reroute"),
+    "tiny_f32_cap_rr": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3, capacity_factor=1.0, overflow="reroute"),
 }
 
 _CACHE = {}
@@ -124,6 +138,14 @@ def test_stages_chain(name):
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(A, dtype=torch.int32, device="cuda")
     inv = torch.empty(A, dtype=torch.int32, device="cuda")
+    if w.overflow == "reroute":
+        # the router stage returns no candidates: the stage API refuses
+        x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+        with pytest.raises(moe.MoeError) as err:
+            moe.dispatch(desc, idx, dev.x, counts, offsets, perm, inv, x_perm,
+                         moe.workspace(desc, moe.STAGE_DISPATCH))
+        assert err.value.status == moe.MOE_ERR_UNSUPPORTED
+        return
     if w.dispatch_fp8:
         x_perm = torch.empty(moe.fp8_payload_bytes(A, w.d), dtype=torch.uint8, device="cuda")
     else:
@@ -208,7 +230,7 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
                                   "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big", "dsv3_skew_cap",
-                                  "qwen_f8d_split", "decode_f8d"])
+                                  "qwen_f8d_split", "decode_f8d", "dsv3_skew_cap_rr", "qwen_f8d_cap_rr"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
