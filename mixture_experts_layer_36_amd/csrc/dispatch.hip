@@ -8,7 +8,7 @@
 // asks to export (section "Trade-offs, Gotchas, and What Goes Wrong").
 //
 // Three index kernels, all deterministic (no result depends on atomic order):
-//   1. histogram: one wavefront per chunk of kDispatchChunk assignments,
+//   1. histogram: one wavefront per chunk of a.chunk assignments,
 //      LDS-privatised bins -> chunk_cnt[chunk][e];
 //   2. scan (one block): per-expert running sums over chunks give each
 //      chunk's first row per expert; an exclusive scan over experts gives
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(64) void histogram_kernel(DispatchArgs a, const int
   const int lane = threadIdx.x;
   for (int e = lane; e < a.E; e += 64) bins[e] = 0;
   __syncthreads();
-  const int base = blockIdx.x * kDispatchChunk;
-  const int end = min(base + kDispatchChunk, a.n_assign);
+  const int base = blockIdx.x * a.chunk;
+  const int end = min(base + a.chunk, a.n_assign);
   for (int i = base + lane; i < end; i += 64) {
     const int e = keys[i];
     if (e >= 0) atomicAdd(&bins[e], 1);
@@ -102,8 +102,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a, int32_t* ra
   const int lane = threadIdx.x;
   for (int e = lane; e < a.E; e += 64) next_row[e] = a.chunk_cnt[(size_t)blockIdx.x * a.E + e];
   __syncthreads();
-  const int base = blockIdx.x * kDispatchChunk;
-  const int end = min(base + kDispatchChunk, a.n_assign);
+  const int base = blockIdx.x * a.chunk;
+  const int end = min(base + a.chunk, a.n_assign);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int s = base; s < end; s += 64) {
     const int i = s + lane;
@@ -193,8 +193,8 @@ __global__ __launch_bounds__(64) void reroute_scatter_kernel(DispatchArgs a, Rer
   const int lane = threadIdx.x;
   for (int e = lane; e < a.E; e += 64) next_row[e] = r.chunk_cnt2[(size_t)blockIdx.x * a.E + e];
   __syncthreads();
-  const int base = blockIdx.x * kDispatchChunk;
-  const int end = min(base + kDispatchChunk, a.n_assign);
+  const int base = blockIdx.x * a.chunk;
+  const int end = min(base + a.chunk, a.n_assign);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int s = base; s < end; s += 64) {
     const int i = s + lane;
@@ -264,21 +264,25 @@ __global__ void zero_counts_kernel(DispatchArgs a) {
 
 }  // namespace
 
-hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s) {
+hipError_t launch_dispatch_index(const DispatchArgs& a_in, hipStream_t s) {
+  DispatchArgs a = a_in;
+  a.chunk = dispatch_chunk(a.n_assign);
   if (a.n_assign == 0) {  // a fill kernel, not a memset node (graph-safe)
     hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kMaxE + 64), 0, s, a);
     return hipGetLastError();
   }
-  const int n_chunks = (a.n_assign + kDispatchChunk - 1) / kDispatchChunk;
+  const int n_chunks = (a.n_assign + a.chunk - 1) / a.chunk;
   hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a, a.topk_idx, a.chunk_cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, n_chunks);
   hipLaunchKernelGGL(scatter_kernel, dim3(n_chunks), dim3(64), 0, s, a, (int32_t*)nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_reroute(const DispatchArgs& a, const RerouteArgs& r, hipStream_t s) {
-  if (a.n_assign == 0) return launch_dispatch_index(a, s);
-  const int n_chunks = (a.n_assign + kDispatchChunk - 1) / kDispatchChunk;
+hipError_t launch_dispatch_reroute(const DispatchArgs& a_in, const RerouteArgs& r, hipStream_t s) {
+  if (a_in.n_assign == 0) return launch_dispatch_index(a_in, s);
+  DispatchArgs a = a_in;
+  a.chunk = dispatch_chunk(a.n_assign);
+  const int n_chunks = (a.n_assign + a.chunk - 1) / a.chunk;
   const int T = a.n_assign / a.k;
   hipLaunchKernelGGL(histogram_kernel, dim3(n_chunks), dim3(64), 0, s, a, a.topk_idx, a.chunk_cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxE), 0, s, a, n_chunks);

@@ -189,7 +189,7 @@ RouteWs carve_route(Carve& c, const moe_desc* d, bool with_candidates) {
   return w;
 }
 DispatchWs carve_dispatch(Carve& c, const moe_desc* d, bool rerouting) {
-  const int64_t chunks = (n_assign(d) + kDispatchChunk - 1) / kDispatchChunk;
+  const int64_t chunks = (n_assign(d) + kMinDispatchChunk - 1) / kMinDispatchChunk;
   DispatchWs w{};
   w.chunk_cnt = c.take<int32_t>(sizeof(int32_t) * size_t(chunks) * d->E);
   if (rerouting) {

@@ -60,8 +60,16 @@ struct RouteSelectArgs {
 };
 hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s);
 
-// Dispatch: assignments are processed in chunks of kDispatchChunk.
-constexpr int kDispatchChunk = 1024;
+// Dispatch: assignments are processed in chunks of dispatch_chunk(n_assign)
+// (a power of two in [kMinDispatchChunk, kMaxDispatchChunk], about 64 chunks:
+// one wavefront walks a chunk, the scan walks the chunks); workspaces are
+// sized for the smallest chunk.
+constexpr int kMinDispatchChunk = 256, kMaxDispatchChunk = 1024;
+inline int dispatch_chunk(long long n_assign) {
+  int c = kMinDispatchChunk;
+  while (c < kMaxDispatchChunk && (long long)c * 64 < n_assign) c *= 2;
+  return c;
+}
 struct DispatchArgs {
   const int32_t* topk_idx;  // [T*k]
   int n_assign, E, k;
@@ -71,6 +79,7 @@ struct DispatchArgs {
   int32_t* perm_token;      // [n_assign]
   int32_t* inv_pos;         // [n_assign]
   int cap;                  // slots per expert (INT32_MAX: dropless)
+  int chunk;                // assignments per chunk (set by the launchers)
 };
 hipError_t launch_dispatch_index(const DispatchArgs& a, hipStream_t s);
 
