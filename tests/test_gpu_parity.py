@@ -350,6 +350,28 @@ def test_token_counts(T):
     _check_custom(_custom(MIXTRAL_PREFILL.scaled(T=T, d=256, f=256)))
 
 
+@pytest.mark.parametrize("T", [1, 2, 129])
+def test_token_counts_fp8_payload(T):
+    _check_custom(_custom(QWEN_FP8_SKEW.scaled(T=T, d=256, f=256, E=16, k=4, dispatch_fp8=True)))
+
+
+@pytest.mark.parametrize("T,cf", [(1, 1.0), (2, 0.5), (129, 1.0)])
+def test_token_counts_reroute(T, cf):
+    # cf 0.5 at T = 2: one slot per expert, so the second token's repeated
+    # choices overflow onto its candidates
+    ref = _check_custom(_custom(DSV3_DECODE.scaled(T=T, d=256, f=256, E=16, k=4, f_shared=128,
+                                                   capacity_factor=cf, overflow="reroute")))
+    assert ref.served is not None
+
+
+def test_reroute_k_equals_e_has_no_candidates():
+    # every expert is chosen, so an overflow has no next-best expert: dropped
+    ref = _check_custom(_custom(MIXTRAL_PREFILL.scaled(T=64, d=256, f=256, E=4, k=4, capacity_factor=0.5,
+                                                       overflow="reroute")))
+    assert (ref.served < 0).any()
+    assert np.array_equal(ref.served >= 0, ref.inv_pos.reshape(ref.served.shape) >= 0)
+
+
 def test_zero_tokens():
     w = MIXTRAL_PREFILL.scaled(T=0, d=256, f=256)
     desc = moe.Desc.from_attrs(w)
