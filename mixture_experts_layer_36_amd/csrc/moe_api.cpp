@@ -276,6 +276,10 @@ moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 // ---------------------------------------------------------------- stages
 moe_status run_route(const moe_desc* d, const void* x, const void* wr, const float* bias,
                      int32_t* idx, float* w, const RouteWs& ws, hipStream_t s) {
+  if (router_fused_ok(d->T, d->d, d->E, d->k, d->n_group, gemm_dtype(d->act))) {
+    RouterFusedArgs r{x, wr, bias, d->T, d->d, d->E, d->k, d->score, d->renorm, idx, w, ws.cand_idx, ws.cand_w};
+    return dev(launch_router_fused(r, s));
+  }
   GemmArgs g{};
   g.A = x;
   g.rows = d->T;

@@ -60,6 +60,22 @@ struct RouteSelectArgs {
 };
 hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s);
 
+// The whole router in one kernel for few experts: logits x Wr^T + b, scores,
+// top-k, gates (and reroute candidates), with the selection rules of
+// route_select.  Taken when router_fused_ok().
+struct RouterFusedArgs {
+  const void* x;         // [T][d] bf16
+  const void* w_router;  // [E][d] bf16
+  const float* bias;     // [E] or NULL
+  int T, d, E, k, score, renorm;
+  int32_t* topk_idx;     // [T][k]
+  float* topk_w;         // [T][k]
+  int32_t* cand_idx;     // [T][k] or NULL
+  float* cand_w;
+};
+bool router_fused_ok(int T, int d, int E, int k, int n_group, int act);
+hipError_t launch_router_fused(const RouterFusedArgs& a, hipStream_t s);
+
 // Dispatch: assignments are processed in chunks of dispatch_chunk(n_assign)
 // (a power of two in [kMinDispatchChunk, kMaxDispatchChunk], about 64 chunks:
 // one wavefront walks a chunk, the scan walks the chunks); workspaces are

@@ -197,7 +197,152 @@ __global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few experts (E <= 32, no group limit, bf16): the whole router in one kernel.
+// A block takes TB = 64 / EM tokens; its four wavefronts split d into four
+// ranges, and each lane runs over 16-byte chunks of its wavefront's range
+// (lane-strided), loading each chunk for the E router rows and the TB tokens
+// and accumulating the E x TB dot products with the packed bf16 dot
+// instruction (fp32 accumulate).  The 4 x 64 partial sums of each product go
+// through LDS and wavefront 0's lane l = tb * EM + e adds them in a fixed
+// order (identical router rows give identical logits), so token tb's logits
+// sit in lanes [tb * EM, tb * EM + EM).  Scores, top-k and gates follow in
+// those lane groups with shuffles that stay inside the group.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A dword as two bf16.  Taken by value: a bit cast applied directly to a
+// component of a vector (v.y) compiles to a cast of its first component.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// acc + sum of the 8 bf16 products of two 16-byte chunks (packed dot, fp32
+// accumulate, pairs in element order).
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), acc, false);
+  return acc;
+}
+
+template <int EM>
+__global__ __launch_bounds__(256) void router_fused_kernel(RouterFusedArgs a) {
+  constexpr int TB = 64 / EM;  // tokens per block
+  __shared__ float s_part[4][64][65];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TB;
+  const int nch = a.d / 8;  // 16-byte chunks per row
+  const int c_lo = wave * nch / 4, c_hi = (wave + 1) * nch / 4;
+  float acc[EM][TB];
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[e][j] = 0.f;
+  const u32x4* wr = (const u32x4*)a.w_router;
+  const u32x4* x = (const u32x4*)a.x;
+  for (int c = c_lo + lane; c < c_hi; c += 64) {
+    u32x4 xv[TB];
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int t = min(t0 + j, a.T - 1);
+      xv[j] = x[(size_t)t * nch + c];
+    }
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      if (e >= a.E) break;
+      const u32x4 wv = wr[(size_t)e * nch + c];
+#pragma unroll
+      for (int j = 0; j < TB; ++j) acc[e][j] = dot8(wv, xv[j], acc[e][j]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) s_part[wave][lane][j * EM + e] = acc[e][j];
+  __syncthreads();
+  if (wave != 0) return;
+  float z = 0.f;  // entry `lane` summed over the waves' ranges, then lanes
+  for (int w = 0; w < 4; ++w)
+    for (int l = 0; l < 64; ++l) z += s_part[w][l][lane];
+  const int e = lane % EM, tb = lane / EM, t = t0 + tb;
+  const bool real = e < a.E;
+  if (real && a.bias) z += a.bias[e];
+  // group reductions over the EM lanes of a token (xor offsets < EM stay inside)
+  auto gmax = [&](float v) {
+#pragma unroll
+    for (int off = EM / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+  };
+  auto gsum = [&](float v) {
+#pragma unroll
+    for (int off = EM / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+  };
+  auto gmax_u64 = [&](uint64_t v) {
+#pragma unroll
+    for (int off = EM / 2; off >= 1; off >>= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, 64);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, 64);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      v = o > v ? o : v;
+    }
+    return v;
+  };
+  const float zl = real ? z : -INFINITY;
+  const float zmax = gmax(zl);
+  const float esum = (a.score == 0) ? gsum(real ? expf(zl - zmax) : 0.f) : 0.f;
+  uint64_t key = real ? (((uint64_t)ordered_bits(z) << 32) | (uint32_t)(~e)) : 0ull;
+  // rank of this lane's expert among the token's (k rounds; 2k with candidates)
+  const int rounds = a.cand_idx ? 2 * a.k : a.k;
+  int rank = -1;
+  for (int j = 0; j < rounds; ++j) {
+    const uint64_t best = gmax_u64(key);
+    if (best != 0ull && key == best) {
+      rank = j;
+      key = 0ull;
+    }
+  }
+  const bool sel = rank >= 0 && rank < a.k;
+  const bool cand = rank >= a.k;
+  float r = 0.f;
+  if (sel || cand) r = (a.score == 0) ? expf(z - zmax) : 1.f / (1.f + expf(-z));
+  float denom = 1.f;
+  if (a.renorm) denom = gsum(sel ? r : 0.f);
+  else if (a.score == 0) denom = esum;
+  const float g = r / denom;
+  if (t < a.T && sel) {
+    a.topk_idx[(size_t)t * a.k + rank] = e;
+    a.topk_w[(size_t)t * a.k + rank] = g;
+  }
+  if (t < a.T && a.cand_idx) {
+    if (cand) {
+      a.cand_idx[(size_t)t * a.k + rank - a.k] = e;
+      a.cand_w[(size_t)t * a.k + rank - a.k] = g;
+    }
+    // ranks past the experts there are: no candidate
+    if (e == 0)
+      for (int m = max(a.E - a.k, 0); m < a.k; ++m) {
+        a.cand_idx[(size_t)t * a.k + m] = -1;
+        a.cand_w[(size_t)t * a.k + m] = 0.f;
+      }
+  }
+}
+
 }  // namespace
+
+bool router_fused_ok(int T, int d, int E, int k, int n_group, int act) {
+  return act == GD_BF16 && E <= 32 && n_group == 0 && k <= E && T > 0 && d % 8 == 0;
+}
+
+hipError_t launch_router_fused(const RouterFusedArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int em = a.E <= 8 ? 8 : a.E <= 16 ? 16 : 32;
+  const int per_block = 64 / em;  // tokens per block
+  const dim3 grid((a.T + per_block - 1) / per_block);
+  if (em == 8) hipLaunchKernelGGL(router_fused_kernel<8>, grid, dim3(256), 0, s, a);
+  else if (em == 16) hipLaunchKernelGGL(router_fused_kernel<16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(router_fused_kernel<32>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_select(const RouteSelectArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
