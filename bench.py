@@ -156,8 +156,17 @@ def cpu_baseline(w, L, host_experts, sample):
     O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap,
                     fp8_dispatch=w.dispatch_fp8, overflow=w.overflow)
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools if p.get("user_api") == "blas"})
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "cpu_model": cpu_model, "blas": blas,
             "kind": "oracle",
             "sample": f"first {sample} of {w.T} tokens, full layer forward in float64 "
                       f"(routing, dispatch, experts, combine), {dt:.2f} s"}
@@ -257,7 +266,8 @@ def main():
                          for tr in traces])
     stage_us = {name: round(float(stage_ms[:, j].mean()) * 1e3, 2)
                 for j, name in enumerate(moe.TRACE_STAGES)}
-    step_event_ms = float(np.mean([tr[0].elapsed_time(tr[-1]) for tr in traces]))
+    step_events = [tr[0].elapsed_time(tr[-1]) for tr in traces]
+    step_event_ms = float(np.mean(step_events))
     c = counts.cpu().numpy()
     assert int(c.sum()) == w.T * w.k, "routing lost assignments"
     cap = desc.capacity
@@ -315,11 +325,15 @@ def main():
                    "dispatch_fp8": w.dispatch_fp8,
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": roof,
+        # all expert GEMMs (routed gate-up and down, shared expert) over their stages
         "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
+        "ffn_frac_of_bf16_peak": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12
+                                       / PEAK_BF16_TFLOPS, 4),
         "stages_us": stage_us,
         "stages_gbps": {k: round(v / (stage_us[k] * 1e-6) / 1e9, 1)
                         for k, v in stage_bytes(w, dev.bias is not None, n_assign).items()},
         "step_event_ms": round(step_event_ms, 4),
+        "step_event_ms_median": round(float(np.median(step_events)), 4),
         "load": {"max_over_mean": round(float(c.max() / c.mean()), 3),
                  "experts_touched": int((c > 0).sum()), "experts": w.E},
         "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,

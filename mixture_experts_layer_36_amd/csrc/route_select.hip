@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectAr
 }
 
 // ---------------------------------------------------------------------------
-// Few experts (E <= 32, no group limit, bf16): the whole router in one kernel.
+// Few experts (E <= 8, no group limit, bf16): the whole router in one kernel.
 // A block takes TB = 64 / EM tokens; its four wavefronts split d into four
 // ranges, and each lane runs over 16-byte chunks of its wavefront's range
 // (lane-strided), loading each chunk for the E router rows and the TB tokens
@@ -329,8 +329,11 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterFusedArgs a) {
 
 }  // namespace
 
+// Every block re-reads all of Wr for its 64 / E' tokens, so Wr traffic is
+// (E / (64 / E')) times that of x: at most x's for E <= 8.  Wider routers
+// stay on the split-K GEMM.
 bool router_fused_ok(int T, int d, int E, int k, int n_group, int act) {
-  return act == GD_BF16 && E <= 32 && n_group == 0 && k <= E && T > 0 && d % 8 == 0;
+  return act == GD_BF16 && E <= 8 && n_group == 0 && k <= E && T > 0 && d % 8 == 0;
 }
 
 hipError_t launch_router_fused(const RouterFusedArgs& a, hipStream_t s) {
