@@ -298,6 +298,17 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
   __builtin_amdgcn_s_waitcnt(0xc07f);
   barrier_only();
   const int rows = ti.nrows;
+  if (sg.c_prows) {
+    // K-blocked C: the tile's 32-column planes in turn, each a contiguous run
+    // of rows x 64 bytes (4 chunks per row)
+    for (int u = tid; u < rows * O::CPR; u += C::NTHR) {
+      const int p = u / (rows * 4), rem = u % (rows * 4), r = rem >> 2, ch = p * 4 + (rem & 3);
+      const u32x4 v = *(const u32x4*)(lds + r * O::ROW_BYTES + ((ch ^ (r & 15)) << 4));
+      if (ncol0 + p * 32 < sg.N)
+        *(u32x4*)((uint16_t*)sg.C + ((size_t)(ncol0 / 32 + p) * sg.c_prows + ti.row0 + r) * 32 + (rem & 3) * 8) = v;
+    }
+    return;
+  }
   for (int u = tid; u < rows * O::CPR; u += C::NTHR) {
     const int r = u / O::CPR, ch = u % O::CPR;
     const u32x4 v = *(const u32x4*)(lds + r * O::ROW_BYTES + ((ch ^ (r & 15)) << 4));
@@ -329,19 +340,29 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // chunk (s % CH) ^ swz(row).
   const int KT = kt1 - kt0;
   // With a row map (fused dispatch gather) the descriptor spans all of A and
-  // each lane's offset starts at its row's A row.
+  // each lane's offset starts at its row's A row.  A K-blocked A (planes of
+  // a_prows rows, no row map) spans all planes: a lane's offset is its row's
+  // 64 bytes in plane 0 and a stage adds its plane, so a load of the stage's
+  // 32-column slice reads consecutive rows as one contiguous run.
+  const int a_plane = sg.a_prows * BK * 2;  // 0: row-major
+  const int a_step = a_plane ? a_plane : BK * 2;  // bytes from one stage's slice to the next
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K * 2, kBufferFlags)
-              : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0,
-                                                  ti.nrows * K * 2, kBufferFlags);
+      a_plane ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, (K / BK) * a_plane, kBufferFlags)
+      : sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K * 2, kBufferFlags)
+                : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0,
+                                                    ti.nrows * K * 2, kBufferFlags);
   uint32_t a_off[M::A_LOADS];
 #pragma unroll
   for (int j = 0; j < M::A_LOADS; ++j) {
     const int s = (wave * M::A_LOADS + j) * 64 + lane;
     const int r = s / CH, c = (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
-    const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
-    a_off[j] = (uint32_t)(ar * K + c * 8) * 2u;
+    if (a_plane) {
+      a_off[j] = (uint32_t)((ti.row0 + rr) * BK + c * 8) * 2u;
+    } else {
+      const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
+      a_off[j] = (uint32_t)(ar * K + c * 8) * 2u;
+    }
   }
   // B: SwiGLU tiles take each wave column's RW rows as RW/2 rows of W1 then
   // the same columns of W3 (one descriptor each); the 64 slots of one load
@@ -383,7 +404,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
 #pragma unroll
       for (int j = 0; j < M::A_LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * BK * 2, 0, 0);
+            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * a_step, 0, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < M::B_LOADS; ++j) {
@@ -861,7 +882,10 @@ __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& t
     u32x2 v;
     v[0] = pack_bf16x2(o[0], o[1]);
     v[1] = pack_bf16x2(o[2], o[3]);
-    *(u32x2*)((uint16_t*)sg.C + (size_t)(ti.row0 + row) * sg.N + n) = v;
+    // n is a multiple of 4: the four columns lie in one 32-column plane
+    const size_t at = sg.c_prows ? ((size_t)(n / 32) * sg.c_prows + ti.row0 + row) * 32 + n % 32
+                                 : (size_t)(ti.row0 + row) * sg.N + n;
+    *(u32x2*)((uint16_t*)sg.C + at) = v;
   }
 }
 

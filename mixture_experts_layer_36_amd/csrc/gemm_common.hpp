@@ -23,6 +23,8 @@ struct Seg {
   char* C;
   int N, K;
   const int32_t* amap;      // routed rows through the row map (NULL: rows in order)
+  int a_prows;              // A K-blocked with planes of a_prows rows (0: row-major)
+  int c_prows;              // C K-blocked likewise (0: row-major)
 };
 
 // A row of segment row `r` (tile-relative row r of a tile starting at row0).
@@ -56,6 +58,8 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.N = a.shN;
     sg.K = a.shK;
     sg.amap = nullptr;
+    sg.a_prows = a.a_blk ? a.sh_rows : 0;
+    sg.c_prows = a.c_blk ? a.sh_rows : 0;
     return ti.nrows > 0;
   }
   if (a.tile_table == nullptr) {
@@ -76,6 +80,8 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.N = a.N;
   sg.K = a.K;
   sg.amap = a.a_map;
+  sg.a_prows = a.a_blk ? a.rows : 0;
+  sg.c_prows = a.c_blk ? a.rows : 0;
   return ti.nrows > 0;
 }
 

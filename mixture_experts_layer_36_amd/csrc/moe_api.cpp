@@ -224,6 +224,15 @@ FfnWs carve_ffn(Carve& c, const moe_desc* d, bool with_shared) {
 bool fuse_gather(const moe_desc* d) {
   return size_t(d->T) * size_t(d->d) * act_bytes(d) < (size_t(1) << 31);
 }
+// The layer's h between the routed GEMMs in K-blocked planes (GemmArgs::c_blk
+// then a_blk): when the prefill kernel runs both in bf16, so each stage of the
+// down projection reads one contiguous run per 32-column slice.  The matrices
+// stay under 2^31 bytes, the reach of the kernel's 32-bit buffer offsets.
+bool h_blocked(const moe_desc* d) {
+  if (d->act != MOE_BF16 || block_m(d) != 256) return false;
+  const size_t lim = size_t(1) << 31;
+  return n_assign(d) * size_t(d->f) * 2 < lim && (!fuse_shared(d) || size_t(d->T) * d->f_shared * 2 < lim);
+}
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
   LayerWs w;
   const size_t A = n_assign(d), ab = act_bytes(d);
@@ -347,8 +356,9 @@ struct SharedSeg {
 moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map, const int32_t* offsets,
                          const void* w1, const void* w3, const float* s1, const float* s3, void* h,
                          const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr,
-                         const uint8_t* a_scales = nullptr) {
+                         const uint8_t* a_scales = nullptr, bool h_blk = false) {
   GemmArgs g{};
+  g.c_blk = h_blk;
   g.a_scales = a_scales;
   g.a_sstride = a_scales ? int(payload_sstride(d)) : 0;
   g.ksplit = 1;
@@ -386,8 +396,9 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map,
 
 moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offsets, const void* w2,
                          const float* s2, void* y, const FfnWs& ws, hipStream_t s,
-                         const SharedSeg* sh = nullptr) {
+                         const SharedSeg* sh = nullptr, bool h_blk = false) {
   GemmArgs g{};
+  g.a_blk = h_blk;
   g.ksplit = 1;
   if (sh) {
     g.sh_rows = d->T;
@@ -625,11 +636,12 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
     sh.y = w.sy;
   }
   MOE_TRY(run_tables(d, w.offsets, w.ffn, s, fused));
+  const bool hb = h_blocked(d);
   MOE_TRY(record(trace, 2, s));
   MOE_TRY(run_ffn_gemm1(d, a_rows, fg ? w.perm_token : nullptr, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s,
-                        fused ? &sh : nullptr, a_scales));
+                        fused ? &sh : nullptr, a_scales, hb));
   MOE_TRY(record(trace, 3, s));
-  MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr));
+  MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr, hb));
   MOE_TRY(record(trace, 4, s));
   if (shared && !fused) MOE_TRY(run_shared(d, x, sw1, sw3, sw2, w.sh, w.sy, s));
   MOE_TRY(record(trace, 5, s));

@@ -207,6 +207,15 @@ struct GemmArgs {
   // a_sstride bytes (a multiple of 16), indexed like A's rows.
   const uint8_t* a_scales;
   int a_sstride;
+  // Prefill kernel only, bf16: K-blocked operands.  A K-blocked matrix of P
+  // rows and K columns is K/32 planes of [P][32] elements, element (r, k) at
+  // (k / 32) * P * 32 + r * 32 + k % 32, so the 32-column slice of a tile's
+  // rows is one contiguous run.  a_blk (no row map): A in this layout with
+  // P = rows, and the extra segment's shA with P = sh_rows.  c_blk (SwiGLU
+  // only): C with P = rows and shC with P = sh_rows.  The whole matrix must
+  // stay under 2^31 bytes.
+  int a_blk;
+  int c_blk;
 };
 
 // Bytes of one partial-sum slot (one 256 x 256 tile of fp32 accumulators) and

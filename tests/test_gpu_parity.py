@@ -78,6 +78,12 @@ CASES = {
     "decode_cap_rr": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256, capacity_factor=1.0,
                                         overflow="reroute"),
     "tiny_f32_cap_rr": TINY_F32.scaled(T=77, d=256, f=384, E=5, k=3, capacity_factor=1.0, overflow="reroute"),
+    # the shared expert as an extra segment of the 256-row kernel, wider than
+    # the routed experts and with a half-tile tail: x and h (routed and shared)
+    # in K-blocked planes, also with the payload values written blocked
+    "dsv3_big_shared": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384),
+    "dsv3_big_shared_f8d": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384,
+                                                    dispatch_fp8=True),
 }
 
 _CACHE = {}
@@ -237,6 +243,36 @@ def test_deterministic(name):
     b = _run_layer(w, dev)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("name", ["mixtral_big_tiles", "mixtral_big_k128", "mixtral_big_split", "qwen_fp8_big",
+                                  "qwen_fp8_big_n128", "mixtral_big_f8d", "qwen_f8d_split", "mixtral_big_cap"])
+def test_layer_matches_stage_chain_bitwise(name):
+    """The layer keeps x and h in K-blocked planes on the 256-row kernel (and
+    reads x through the row map); the stage entry points use row-major x_perm
+    and h.  Same products in the same order: identical outputs."""
+    w, L, dev, ref = _setup(name)
+    out_l, idx, gw, counts = _run_layer(w, dev)
+    desc = moe.Desc.from_attrs(w)
+    T, A = w.T, w.T * w.k
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(A, dtype=torch.int32, device="cuda")
+    inv = torch.empty(A, dtype=torch.int32, device="cuda")
+    counts2 = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    if w.dispatch_fp8:
+        x_perm = torch.empty(moe.fp8_payload_bytes(A, w.d), dtype=torch.uint8, device="cuda")
+    else:
+        x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.dispatch(desc, idx, dev.x, counts2, offsets, perm, inv, x_perm, moe.workspace(desc, moe.STAGE_DISPATCH))
+    h = torch.empty((A, w.f), dtype=dev.x.dtype, device="cuda")
+    y = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.grouped_ffn(desc, x_perm, offsets, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3, dev.s2, h, y,
+                    moe.workspace(desc, moe.STAGE_FFN))
+    out_c = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.combine(desc, y, inv, gw, None, out_c)
+    torch.cuda.synchronize()
+    assert torch.equal(counts, counts2)
+    assert torch.equal(out_l, out_c)
 
 
 # ----------------------------------------------------------------- edge cases
