@@ -251,6 +251,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
   }
 }
 
+// The same rows into K/32 planes of [rows][32] bf16: thread g moves the 16
+// bytes at g, so a wave stores one contiguous kilobyte (16 rows x 64 bytes of
+// one plane) and loads 16 row runs of 64 bytes.
+__global__ __launch_bounds__(256) void gather_blocked_kernel(const u32x4* __restrict__ x,
+                                                             const int32_t* __restrict__ perm, int rows,
+                                                             const int32_t* __restrict__ rows_dev, int d,
+                                                             u32x4* __restrict__ out) {
+  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per_plane = (size_t)rows * 4;
+  if (g >= per_plane * (d / 32)) return;
+  const int p = (int)(g / per_plane), rem = (int)(g % per_plane), r = rem >> 2, q = rem & 3;
+  const int n = rows_dev ? min(*rows_dev, rows) : rows;
+  if (r >= n) return;
+  out[g] = x[((size_t)perm[r] * d + p * 32 + q * 8) / 8];
+}
+
 __global__ __launch_bounds__(256) void segment_rows_kernel(const int32_t* offsets, int E, int32_t* rows) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e < E) rows[e] = offsets[e + 1] - offsets[e];
@@ -305,6 +321,16 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(gather_kernel, dim3((rows + 7) / 8), dim3(256), 0, s,
                      (const u32x4*)x, perm_token, rows, rows_dev, row_bytes / 16, (u32x4*)x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_blocked(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
+                                      int d, void* x_perm, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (d % 32 != 0) return hipErrorInvalidValue;
+  const size_t threads = (size_t)rows * (d / 8);
+  hipLaunchKernelGGL(gather_blocked_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)x, perm_token, rows, rows_dev, d, (u32x4*)x_perm);
   return hipGetLastError();
 }
 

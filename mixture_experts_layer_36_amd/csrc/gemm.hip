@@ -367,9 +367,10 @@ int gemm_max_slots(int rows, int E, int block_m, int sh_rows) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   // K-blocked operands: bf16 A / the SwiGLU output, on the prefill kernel only
-  if ((a.a_blk || a.c_blk) && !(a.act != GD_F32 && !use_decode(a) && use_big(a) && a.epi != EPI_BIAS_F32 &&
-                                 (!a.c_blk || a.epi == EPI_SWIGLU) &&
-                                 (!a.a_blk || (a.act == GD_BF16 && a.a_map == nullptr))))
+  if ((a.a_blk || a.sh_a_blk || a.c_blk) &&
+      !(a.act != GD_F32 && !use_decode(a) && use_big(a) && a.epi != EPI_BIAS_F32 &&
+        (!a.c_blk || a.epi == EPI_SWIGLU) && (!a.a_blk || (a.act == GD_BF16 && a.a_map == nullptr)) &&
+        (!a.sh_a_blk || a.act == GD_BF16)))
     return hipErrorInvalidValue;
   if (a.act == GD_F32) {
     switch (a.epi) {

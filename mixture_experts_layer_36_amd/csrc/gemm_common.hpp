@@ -58,7 +58,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.N = a.shN;
     sg.K = a.shK;
     sg.amap = nullptr;
-    sg.a_prows = a.a_blk ? a.sh_rows : 0;
+    sg.a_prows = a.sh_a_blk ? a.sh_rows : 0;
     sg.c_prows = a.c_blk ? a.sh_rows : 0;
     return ti.nrows > 0;
   }

@@ -81,6 +81,10 @@ CASES = {
     # the shared expert as an extra segment of the 256-row kernel, wider than
     # the routed experts and with a half-tile tail: x and h (routed and shared)
     # in K-blocked planes, also with the payload values written blocked
+    # f >= 4096 on the 256-row kernel: the layer gathers x_perm into K-blocked
+    # planes (ragged expert tails; with a capacity the gather stops early)
+    "mixtral_wide_f": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4),
+    "mixtral_wide_f_cap": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4, capacity_factor=1.0),
     "dsv3_big_shared": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384),
     "dsv3_big_shared_f8d": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384,
                                                     dispatch_fp8=True),
@@ -236,7 +240,8 @@ def test_shared_expert_and_combine_from_oracle_inputs():
 
 @pytest.mark.parametrize("name", ["mixtral_tiles", "dsv3_skew_small", "qwen_fp8_small", "mixtral_big_tiles",
                                   "decode_shared_wide", "mixtral_big_split", "qwen_fp8_big", "dsv3_skew_cap",
-                                  "qwen_f8d_split", "decode_f8d", "dsv3_skew_cap_rr", "qwen_f8d_cap_rr"])
+                                  "qwen_f8d_split", "decode_f8d", "dsv3_skew_cap_rr", "qwen_f8d_cap_rr",
+                                  "mixtral_wide_f", "dsv3_big_shared"])
 def test_deterministic(name):
     w, L, dev, ref = _setup(name)
     a = _run_layer(w, dev)
@@ -246,11 +251,13 @@ def test_deterministic(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_big_tiles", "mixtral_big_k128", "mixtral_big_split", "qwen_fp8_big",
-                                  "qwen_fp8_big_n128", "mixtral_big_f8d", "qwen_f8d_split", "mixtral_big_cap"])
+                                  "qwen_fp8_big_n128", "mixtral_big_f8d", "qwen_f8d_split", "mixtral_big_cap",
+                                  "mixtral_wide_f", "mixtral_wide_f_cap"])
 def test_layer_matches_stage_chain_bitwise(name):
-    """The layer keeps x and h in K-blocked planes on the 256-row kernel (and
-    reads x through the row map); the stage entry points use row-major x_perm
-    and h.  Same products in the same order: identical outputs."""
+    """On the 256-row kernel the layer keeps h (and for f >= 4096 x_perm) in
+    K-blocked planes, or reads x through the row map; the stage entry points
+    use row-major x_perm and h.  Same products in the same order: identical
+    outputs."""
     w, L, dev, ref = _setup(name)
     out_l, idx, gw, counts = _run_layer(w, dev)
     desc = moe.Desc.from_attrs(w)
