@@ -14,6 +14,9 @@ inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline the float64 oracle on a bounded token sample, host cores
   stages_gbps achieved GB/s of the route, dispatch and combine stages
               (algorithmic bytes over the stage's event time)
+  cold_cache  after the timed steps, as many more steps each preceded by a
+              512 MiB write that evicts the L2s and the 256 MB Infinity Cache,
+              each timed by its own events: medians of the step and stages
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -59,6 +62,7 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time replays of one HIP graph of the layer forward (captured once); the per-stage "
                         "times then come from a separate traced eager pass")
+    p.add_argument("--no-cold", action="store_true", help="skip the cold-cache repetitions")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -114,10 +118,13 @@ def stage_bytes(w, has_bias: bool, kept: int) -> dict:
 
 
 # Ceilings measured on MI355X by separate probes (not in this run): a
-# register-only loop of 32x32x16 bf16 MFMAs on every SIMD, and a streaming
-# read of 8 GiB with 16-byte loads.
+# register-only loop of 32x32x16 bf16 MFMAs on every SIMD, the same with the
+# block-scaled fp8 32x32x64 MFMA, and a streaming read of 8 GiB with 16-byte
+# loads.
 MFMA_LOOP_TFLOPS = 1785.0
+MFMA_LOOP_TFLOPS_FP8 = 4614.0
 STREAM_READ_GBS = 6300.0
+EVICT_BYTES = 512 << 20
 
 
 def calibrate_copy():
@@ -262,6 +269,30 @@ def main():
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
+    cold = None
+    if not args.no_cold:
+        # cold-cache repetitions, outside the timed region: the eviction
+        # write runs between a step's events, never inside them
+        evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
+        cold_tr = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)]
+                   for _ in range(args.steps)]
+        for tr in cold_tr:
+            for ev in tr:
+                ev.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            evict.fill_(i & 0xff)
+            step(cold_tr[i])
+        torch.cuda.synchronize()
+        cms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
+                        for tr in cold_tr])
+        cstep = float(np.median([tr[0].elapsed_time(tr[-1]) for tr in cold_tr]))
+        cold = {"evict_bytes": EVICT_BYTES, "reps": args.steps, "step_ms_median": round(cstep, 4),
+                "tokens_per_s": round(w.T / (cstep * 1e-3), 1),
+                "stages_us_median": {name: round(float(np.median(cms[:, j])) * 1e3, 2)
+                                     for j, name in enumerate(moe.TRACE_STAGES)}}
+        del evict
+
     stage_ms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
                          for tr in traces])
     stage_us = {name: round(float(stage_ms[:, j].mean()) * 1e3, 2)
@@ -300,8 +331,8 @@ def main():
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "algorithmic_flops": flops_gemm1,
                 "avg_launch_us": round(gemm1_s * 1e6, 2)}
-        if not f8:
-            roof["frac_of_measured_mfma_ceiling"] = round(achieved / MFMA_LOOP_TFLOPS, 4)
+        roof["frac_of_measured_mfma_ceiling"] = round(achieved / (MFMA_LOOP_TFLOPS_FP8 if f8 else MFMA_LOOP_TFLOPS),
+                                                      4)
     # HBM bytes per launch of that kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE passes, valid only while the kernels are unchanged
     roof["traffic"] = None
@@ -339,6 +370,7 @@ def main():
         "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,
                      "overflow": w.overflow, "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5),
                      "rerouted_fraction": round((n_assign - own_kept) / (w.T * w.k), 5)},
+        "cold_cache": cold,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
