@@ -63,6 +63,9 @@ def parse():
                    help="time replays of one HIP graph of the layer forward (captured once); the per-stage "
                         "times then come from a separate traced eager pass")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache repetitions")
+    p.add_argument("--w-layout", choices=("auto", "rowmajor", "kblocked"), default="auto",
+                   help="routed expert weight layout; auto: kblocked for bf16 / fp8 weights (packed "
+                        "once after upload, before any timing), rowmajor for fp32")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -218,7 +221,12 @@ def main():
     dev = DeviceLayer(L)
     L.expert = orig
 
+    layout = args.w_layout if args.w_layout != "auto" else ("rowmajor" if w.wdt == "f32" else "kblocked")
+    if layout == "kblocked":  # the one-time load-time transform; weights stay resident
+        dev.w1, dev.w3, dev.w2 = (moe.pack_weights(t) for t in (dev.w1, dev.w3, dev.w2))
+        torch.cuda.synchronize()
     desc = moe.Desc.from_attrs(w)
+    desc.w_layout = moe.W_KBLOCKED if layout == "kblocked" else moe.W_ROWMAJOR
     out = torch.empty((w.T, w.d), dtype=dev.x.dtype, device="cuda")
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
     gw = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
@@ -353,7 +361,7 @@ def main():
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
                    "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
                    "capacity_factor": w.capacity_factor, "overflow": w.overflow,
-                   "dispatch_fp8": w.dispatch_fp8,
+                   "dispatch_fp8": w.dispatch_fp8, "weight_layout": layout,
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": roof,
         # all expert GEMMs (routed gate-up and down, shared expert) over their stages

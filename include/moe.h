@@ -99,9 +99,23 @@ typedef struct {
                          1: they are the block-scaled E4M3 payload of x (act
                          must be MOE_BF16; see "fp8 dispatch payload" below).
                          The router and the shared expert always read x.    */
+  int32_t w_layout;   /* moe_w_layout of the routed w1, w3, w2 (see "Weight
+                         layout" below); the router's and the shared expert's
+                         weights are always row-major                        */
 } moe_desc;
 
 typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow;
+typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_KBLOCKED = 1 } moe_w_layout;
+
+/* Weight layout.  Each routed expert matrix has N output rows and K input
+ * columns (w1, w3: N = f, K = d; w2: N = d, K = f).
+ *   MOE_W_ROWMAJOR: element (n, c) at n*K + c, K contiguous.
+ *   MOE_W_KBLOCKED: K/32 planes of [N][32]; element (n, c) at
+ *     (c/32)*N*32 + n*32 + c%32, so a tile's 32-column slice of consecutive
+ *     rows is one contiguous run (whole cache lines for the direct-to-LDS
+ *     loads of the MFMA kernels).  Requires wdtype MOE_BF16 or MOE_FP8_E4M3;
+ *     moe_pack_weights converts once, e.g. at load time.
+ * Experts stay consecutive ([E][...]) and the fp8 scales keep their layout. */
 
 /* Capacity overflow rerouted (capacity > 0, overflow = MOE_OVERFLOW_REROUTE).
  * "Expert-Parallel MoE Inference", section "Capacity factor and token
@@ -205,10 +219,18 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const voi
  * SwiGLU, silu(u) = u / (1 + exp(-u)).
  *   offsets  [E+1] int32 (device), as produced by moe_dispatch; offsets[E]
  *            <= T*k (rows past it are not touched)
- *   w1, w3   [E][f][d], w2 [E][d][f] in wdtype
+ *   w1, w3   [E][f][d], w2 [E][d][f] in wdtype, laid out per w_layout
  *   s1, s3   [E][f], s2 [E][d] fp32 per-output-channel scales when wdtype is
  *            MOE_FP8_E4M3, else NULL
  *   h, y_perm outputs; ws: moe_workspace_size(MOE_STAGE_FFN) bytes. */
+/* Row-major [mats][rows][cols] -> K-blocked [mats][cols/32][rows][32]
+ * (MOE_W_KBLOCKED with N = rows, K = cols), elem_bytes 1 (E4M3) or 2 (bf16).
+ * src and dst: device, 16-byte aligned, not overlapping; cols a multiple of
+ * 32; mats * rows * cols * elem_bytes at most 2^40.  One kernel on `stream`.
+ * MOE_ERR_INVALID for bad arguments. */
+moe_status moe_pack_weights(const void* src, int64_t mats, int32_t rows, int32_t cols, int32_t elem_bytes,
+                            void* dst, void* stream);
+
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2,
                            const float* s1, const float* s3, const float* s2,
@@ -225,7 +247,9 @@ moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* 
 /* The whole layer: route, dispatch, grouped FFN, shared expert (when
  * f_shared > 0: the SwiGLU expert of every token with gate 1, weights in the
  * act dtype), combine.  Intermediates (perm_token, inv_pos, offsets, x_perm,
- * h, y_perm, shared h and y) live in ws (moe_workspace_size(MOE_STAGE_LAYER)).
+ * h, y_perm, shared h and y) live in ws (moe_workspace_size(MOE_STAGE_LAYER))
+ * in layouts of the library's choosing.
+ *   w1, w3, w2, s1, s3, s2 as for moe_grouped_ffn (w_layout applies).
  *   out [T][d] act dtype; topk_idx [T][k], topk_w [T][k], counts [E] outputs.
  *   sw1, sw3, sw2: shared expert, NULL when f_shared == 0.
  *   trace: NULL, or MOE_TRACE_EVENTS hipEvent_t (host array of handles)

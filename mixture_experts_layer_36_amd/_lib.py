@@ -26,11 +26,13 @@ TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "
 
 # the exported symbols include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows")
+           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows", "moe_pack_weights")
 
 _DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
 OVERFLOW_DROP, OVERFLOW_REROUTE = 0, 1
 _OVERFLOW = {"drop": OVERFLOW_DROP, "reroute": OVERFLOW_REROUTE}
+W_ROWMAJOR, W_KBLOCKED = 0, 1
+_W_LAYOUT = {"rowmajor": W_ROWMAJOR, "kblocked": W_KBLOCKED}
 
 
 class MoeError(RuntimeError):
@@ -55,25 +57,25 @@ def capacity_slots(capacity_factor, T: int, k: int, E: int) -> int:
 class Desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "f", "E", "k", "score", "renorm", "n_group", "topk_group",
-                 "f_shared", "act", "wdtype", "capacity", "overflow", "dispatch_fp8")]
+                 "f_shared", "act", "wdtype", "capacity", "overflow", "dispatch_fp8", "w_layout")]
 
     @classmethod
     def make(cls, T, d, f, E, k, score="softmax", renorm=True, n_group=0, topk_group=0,
              f_shared=0, act="bf16", wdtype="bf16", capacity=0, dispatch_fp8=False,
-             overflow="drop") -> "Desc":
+             overflow="drop", w_layout="rowmajor") -> "Desc":
         return cls(T, d, f, E, k, SOFTMAX if score == "softmax" else SIGMOID, int(bool(renorm)),
                    n_group, topk_group, f_shared, _DTYPES[act], _DTYPES[wdtype], capacity,
-                   _OVERFLOW[overflow], int(bool(dispatch_fp8)))
+                   _OVERFLOW[overflow], int(bool(dispatch_fp8)), _W_LAYOUT[w_layout])
 
     @classmethod
     def from_attrs(cls, w) -> "Desc":
         """From any object with T, d, f, E, k, score, renorm, n_group,
         topk_group, f_shared, act and wdt attributes (and optionally
-        capacity_factor, overflow and dispatch_fp8)."""
+        capacity_factor, overflow, dispatch_fp8 and w_layout)."""
         cap = capacity_slots(getattr(w, "capacity_factor", 0), w.T, w.k, w.E)
         return cls.make(w.T, w.d, w.f, w.E, w.k, w.score, w.renorm, w.n_group, w.topk_group,
                         w.f_shared, w.act, w.wdt, cap, getattr(w, "dispatch_fp8", False),
-                        getattr(w, "overflow", "drop"))
+                        getattr(w, "overflow", "drop"), getattr(w, "w_layout", "rowmajor"))
 
 
 # The fp8 dispatch payload of R rows of width d (moe.h): E4M3 codes [R][d] at
@@ -121,6 +123,8 @@ def _lib() -> ctypes.CDLL:
         lib.moe_combine.argtypes = [D, _P, _P, _P, _P, _P, _P]
         lib.moe_layer_forward.argtypes = [D] + [_P] * 17 + [ctypes.c_size_t, _P, _P]
         lib.moe_layer_rows.argtypes = [D, _P, ctypes.c_size_t, _P, _P]
+        lib.moe_pack_weights.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         _P, _P]
         for name in EXPORTS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -217,3 +221,19 @@ def layer_rows(desc, ws, rows, stream=None):
     layer_forward run with this workspace."""
     _check(_lib().moe_layer_rows(ctypes.byref(desc), _ptr(ws), ws.numel() if ws is not None else 0,
                                  _ptr(rows), _stream(stream)), "moe_layer_rows")
+
+
+def pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Expert matrices [..., N, K] (bf16, or E4M3 codes as uint8) in the
+    K-blocked layout of moe_desc.w_layout = kblocked (moe_pack_weights):
+    K/32 planes of [N][32] per matrix.  Returns `out` (a new tensor of w's
+    shape and dtype when None), whose element order is the packed one."""
+    if w.dim() < 2 or not w.is_contiguous():
+        raise ValueError("pack_weights takes contiguous [..., N, K] matrices")
+    if out is None:
+        out = torch.empty_like(w)
+    N, K = w.shape[-2], w.shape[-1]
+    mats = w.numel() // (N * K) if N * K else 0
+    _check(_lib().moe_pack_weights(_ptr(w), mats, N, K, w.element_size(), _ptr(out), _stream(stream)),
+           "moe_pack_weights")
+    return out

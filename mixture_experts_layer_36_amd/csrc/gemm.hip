@@ -101,9 +101,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
       n = min(ncol0 + r, sg.N - 1);
     }
     const int esz = (WDT == GD_FP8) ? 1 : 2;
-    b_src[j] = (const uint8_t*)base + ((size_t)n * K + k_begin + c * 8) * esz;
+    // K-blocked weights: element (n, k) at (k / 32) * N * 32 + n * 32 + k % 32
+    // (the chunk of 8 or 16 elements at k = c * 8 stays in one plane)
+    b_src[j] = (const uint8_t*)base +
+               (sg.b_blk ? (size_t)(c * 8 / 32) * sg.N * 32 + (size_t)n * 32 + (c * 8) % 32
+                         : (size_t)n * K + k_begin + c * 8) * esz;
     b_dst[j] = BM * C::BK + swz(r, c);
   }
+  // elements from one k tile's slice to the next: K-blocked, k0 columns
+  // start k0 / 32 planes of N * 32 further
+  const size_t b_kstride = sg.b_blk ? (size_t)sg.N : 1;
 
   u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
   auto load = [&](int k0) {
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
     for (int j = 0; j < C::A_CHUNKS; ++j) ra[j] = *(const u32x4*)(a_src[j] + k0);
 #pragma unroll
     for (int j = 0; j < C::B_CHUNKS; ++j)
-      rb[j] = *(const u32x4*)(b_src[j] + (size_t)k0 * (WDT == GD_FP8 ? 1 : 2));
+      rb[j] = *(const u32x4*)(b_src[j] + (size_t)k0 * b_kstride * (WDT == GD_FP8 ? 1 : 2));
   };
   auto store = [&](int buf) {
     __bf16* L = lds[buf];
@@ -322,7 +329,32 @@ hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// Row-major [mats][rows][cols] -> [mats][cols/32][rows][32], 16 bytes per
+// thread in output order: a wave stores one contiguous kilobyte and loads
+// runs of 32 * elem_bytes bytes from 32 / (2 / elem_bytes) rows.
+__global__ __launch_bounds__(256) void pack_kblocked_kernel(const u32x4* __restrict__ src, int64_t mats, int rows,
+                                                            int cols, int elem_bytes, u32x4* __restrict__ dst) {
+  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = 2 * elem_bytes;                   // 16-byte pieces of a plane row (32 elements)
+  const size_t per_plane = (size_t)rows * per_row;
+  const size_t per_mat = per_plane * (cols / 32);
+  if (g >= per_mat * (size_t)mats) return;
+  const size_t m = g / per_mat, in = g % per_mat;
+  const int p = (int)(in / per_plane), rem = (int)(in % per_plane), r = rem / per_row, q = rem % per_row;
+  const size_t row_pieces = (size_t)cols * elem_bytes / 16;  // 16-byte pieces of a source row
+  dst[g] = src[m * rows * row_pieces + (size_t)r * row_pieces + (size_t)p * per_row + q];
+}
+
 }  // namespace
+
+hipError_t launch_pack_kblocked(const void* src, int64_t mats, int rows, int cols, int elem_bytes, void* dst,
+                                hipStream_t s) {
+  const size_t pieces = (size_t)mats * rows * cols * elem_bytes / 16;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kblocked_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
+                     (const u32x4*)src, mats, rows, cols, elem_bytes, (u32x4*)dst);
+  return hipGetLastError();
+}
 
 // Prefill-shaped problems with bf16 activations and bf16 or fp8 weights
 // (enough rows per expert to fill 256-row tiles), and router logits of at
@@ -367,6 +399,9 @@ int gemm_max_slots(int rows, int E, int block_m, int sh_rows) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   // K-blocked operands: bf16 A / the SwiGLU output, on the prefill kernel only
+  // K-blocked routed weights: bf16 / fp8 expert GEMMs (never the router's)
+  if (a.b_blk && (a.act == GD_F32 || a.wdt == GD_F32 || a.epi == EPI_BIAS_F32 || a.ksplit > 1))
+    return hipErrorInvalidValue;
   if ((a.a_blk || a.sh_a_blk || a.c_blk) &&
       !(a.act != GD_F32 && !use_decode(a) && use_big(a) && a.epi != EPI_BIAS_F32 &&
         (!a.c_blk || a.epi == EPI_SWIGLU) && (!a.a_blk || (a.act == GD_BF16 && a.a_map == nullptr)) &&

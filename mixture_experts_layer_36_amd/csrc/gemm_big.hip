@@ -368,12 +368,18 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // the same columns of W3 (one descriptor each); the 64 slots of one load
   // are 64/CH consecutive rows inside one half, so the choice is uniform per
   // load.
+  // K-blocked weights: the descriptor starts at the tile's first row in plane
+  // 0 and spans the rest of the matrix; a lane's offset is its row's piece
+  // in plane 0 and a stage adds its plane (one contiguous run per load).
   const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : min(BN, sg.N - ncol0);
-  const size_t b_start = (size_t)ncol0 * K * M::WB;
+  const int b_plane = sg.b_blk ? sg.N * BK * M::WB : 0;
+  const int b_step = sg.b_blk ? b_plane : BK * M::WB;  // bytes from one stage's slice to the next
+  const size_t b_start = (size_t)ncol0 * (sg.b_blk ? BK : K) * M::WB;
+  const int b_bytes = sg.b_blk ? (K / BK) * b_plane - ncol0 * BK * M::WB : b_rows * K * M::WB;
   const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sg.B0 + b_start), (short)0, b_rows * K * M::WB, kBufferFlags);
+      (void*)(sg.B0 + b_start), (short)0, b_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K * M::WB, kBufferFlags);
+      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_bytes, kBufferFlags);
   constexpr int BCH = BK * M::WB / 16;  // 16-byte chunks per weight row
   uint32_t b_off[M::B_LOADS];
   bool b_w3[M::B_LOADS];
@@ -390,7 +396,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
       b_w3[j] = (r0 % C::RW) >= half;
       n = (r / C::RW) * half + (r % C::RW) % half;
     }
-    b_off[j] = (uint32_t)(n * K * M::WB + c * 16);
+    b_off[j] = (uint32_t)(n * (sg.b_blk ? BK : K) * M::WB + c * 16);
   }
 
   // Stages past the end re-load the last stage into a buffer that is never
@@ -410,9 +416,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
       for (int j = 0; j < M::B_LOADS; ++j) {
         const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
         if (b_w3[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * BK * M::WB, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * BK * M::WB, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
       }
     }
   };
@@ -627,11 +633,15 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     a_off[j] = (uint32_t)(ar * K + c * 16);
   }
   const int b_rows = (EPI == EPI_SWIGLU) ? BN / 2 : min(BN, sg.N - ncol0);
-  const size_t b_start = (size_t)ncol0 * K;
+  // K-blocked weights: a 64-k stage spans two 32-column planes of N x 32 bytes
+  const int b_plane = sg.b_blk ? sg.N * 32 : 0;
+  const size_t b_start = (size_t)ncol0 * (sg.b_blk ? 32 : K);
+  const int b_bytes = sg.b_blk ? (K / 32) * b_plane - ncol0 * 32 : b_rows * K;
   const __amdgpu_buffer_rsrc_t b0_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(sg.B0 + b_start), (short)0, b_rows * K, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(sg.B0 + b_start), (short)0, b_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_rows * K, kBufferFlags);
+      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_bytes, kBufferFlags);
+  const int b_step = sg.b_blk ? 2 * b_plane : BK8;
   uint32_t b_off[M::B_LOADS];
   bool b_w3[M::B_LOADS];
 #pragma unroll
@@ -646,7 +656,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
       b_w3[j] = (r0 % C::RW) >= half;
       n = (r / C::RW) * half + (r % C::RW) % half;
     }
-    b_off[j] = (uint32_t)(n * K + c * 16);
+    b_off[j] = sg.b_blk ? (uint32_t)((c >> 1) * b_plane + n * 32 + (c & 1) * 16) : (uint32_t)(n * K + c * 16);
   }
   // scales: thread t loads the chunk of tile row t (rows past the tile's
   // end repeat its last row); waves past the loaded rows load nothing
@@ -675,9 +685,9 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
       for (int j = 0; j < M::B_LOADS; ++j) {
         const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
         if (b_w3[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * BK8, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * BK8, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
       }
     }
   };

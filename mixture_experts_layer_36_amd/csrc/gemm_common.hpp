@@ -25,6 +25,7 @@ struct Seg {
   const int32_t* amap;      // routed rows through the row map (NULL: rows in order)
   int a_prows;              // A K-blocked with planes of a_prows rows (0: row-major)
   int c_prows;              // C K-blocked likewise (0: row-major)
+  int b_blk;                // B0/B1 K-blocked with planes of N rows
 };
 
 // A row of segment row `r` (tile-relative row r of a tile starting at row0).
@@ -60,6 +61,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.amap = nullptr;
     sg.a_prows = a.sh_a_blk ? a.sh_rows : 0;
     sg.c_prows = a.c_blk ? a.sh_rows : 0;
+    sg.b_blk = 0;
     return ti.nrows > 0;
   }
   if (a.tile_table == nullptr) {
@@ -82,6 +84,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.amap = a.a_map;
   sg.a_prows = a.a_blk ? a.rows : 0;
   sg.c_prows = a.c_blk ? a.rows : 0;
+  sg.b_blk = a.b_blk;
   return ti.nrows > 0;
 }
 

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
   const char *A, *B0, *B1;
   char* Cp;
   int N, K;
+  bool wblk = false;  // weights K-blocked (routed experts only)
   if (shared) {
     row0 = 0;
     nrows = a.sh_rows;
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
     Cp = (char*)a.C;
     N = a.N;
     K = a.K;
+    wblk = a.b_blk != 0;
   }
   const int ncol = (EPI == EPI_SWIGLU) ? WR / 2 : WR;  // output columns per slice
   const int ncol0 = slice * ncol;
@@ -95,13 +97,19 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KT = K / BK;
 
-  // weight rows of this slice: SwiGLU = 64 W1 rows then the same 64 W3 rows
+  // weight rows of this slice: SwiGLU = 64 W1 rows then the same 64 W3 rows.
+  // K-blocked weights: the descriptor starts at the slice's first row in
+  // plane 0 and spans the rest of the matrix; a 64-k stage covers two
+  // 32-column planes of N rows x 64 bytes.
   const int wrows = (EPI == EPI_SWIGLU) ? WR / 2 : WR;
+  const int wplane = wblk ? N * 64 : 0;
+  const size_t wstart = (size_t)ncol0 * (wblk ? 64 : K * 2);
+  const int wbytes = wblk ? (K / 32) * wplane - ncol0 * 64 : wrows * K * 2;
+  const int wstep = wblk ? 2 * wplane : BK * 2;  // bytes from one stage's slice to the next
   const __amdgpu_buffer_rsrc_t w0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B0 + (size_t)ncol0 * K * 2), (short)0, wrows * K * 2, kBufferFlags);
+      (void*)(B0 + wstart), (short)0, wbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t w1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? B1 : B0) + (size_t)ncol0 * K * 2), (short)0, wrows * K * 2,
-      kBufferFlags);
+      (void*)((EPI == EPI_SWIGLU ? B1 : B0) + wstart), (short)0, wbytes, kBufferFlags);
   // slot s of a load instruction's 64 slots: row s / 8, physical chunk s % 8
   // holding logical chunk (s % 8) ^ dswz(row)
   uint32_t w_off[W_LOADS];
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
     const int r = s >> 3, c = (s & 7) ^ dswz(r);
     w_is1[j] = (EPI == EPI_SWIGLU) && ((wave * W_LOADS + j) * 8 >= WR / 2);  // uniform per load
     const int n = (EPI == EPI_SWIGLU) ? (r % (WR / 2)) : r;
-    w_off[j] = (uint32_t)(n * K + c * 8) * 2u;
+    w_off[j] = wblk ? (uint32_t)((c >> 2) * wplane + n * 64 + (c & 3) * 16) : (uint32_t)(n * K + c * 8) * 2u;
   }
   const int tr = lane >> 3;  // token rows lane/8 + 8 j
   const int tc = (lane & 7);
@@ -134,13 +142,14 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
     auto issue = [&](int kt, int buf) {
       __bf16* st = lds + buf * STAGE;
       const int kb = min(kt, KT - 1) * BK * 2;
+      const int wk = min(kt, KT - 1) * wstep;
 #pragma unroll
       for (int j = 0; j < W_LOADS; ++j) {
         const lds_ptr_t dst = (lds_ptr_t)(st + (wave * W_LOADS + j) * 512);
         if (w_is1[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(w1, dst, 16, w_off[j], kb, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w1, dst, 16, w_off[j], wk, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(w0, dst, 16, w_off[j], kb, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w0, dst, 16, w_off[j], wk, 0, 0);
       }
       if (wave == 0) {
 #pragma unroll

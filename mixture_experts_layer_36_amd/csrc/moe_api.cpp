@@ -57,6 +57,14 @@ moe_status check_desc(const moe_desc* d) {
   if (d->overflow != MOE_OVERFLOW_DROP && d->overflow != MOE_OVERFLOW_REROUTE) return MOE_ERR_INVALID;
   if (d->dispatch_fp8 != 0 && d->dispatch_fp8 != 1) return MOE_ERR_INVALID;
   if (d->dispatch_fp8 && d->act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->w_layout != MOE_W_ROWMAJOR && d->w_layout != MOE_W_KBLOCKED) return MOE_ERR_INVALID;
+  if (d->w_layout == MOE_W_KBLOCKED) {
+    // bf16 / fp8 expert kernels only; each matrix within the kernels' 32-bit
+    // buffer offsets
+    if (d->wdtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+    const int64_t wb = d->wdtype == MOE_BF16 ? 2 : 1;
+    if (int64_t(d->d) * d->f * wb >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -369,6 +377,7 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map,
                          const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr,
                          const uint8_t* a_scales = nullptr, bool h_blk = false, bool a_blk = false) {
   GemmArgs g{};
+  g.b_blk = d->w_layout == MOE_W_KBLOCKED;
   g.a_blk = a_blk;
   g.c_blk = h_blk;
   g.a_scales = a_scales;
@@ -410,6 +419,7 @@ moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offset
                          const float* s2, void* y, const FfnWs& ws, hipStream_t s,
                          const SharedSeg* sh = nullptr, bool h_blk = false) {
   GemmArgs g{};
+  g.b_blk = d->w_layout == MOE_W_KBLOCKED;
   g.a_blk = h_blk;
   g.sh_a_blk = h_blk;
   g.ksplit = 1;
@@ -505,6 +515,20 @@ const char* moe_status_str(moe_status s) {
 }
 
 moe_status moe_validate(const moe_desc* desc) { return check_desc(desc); }
+
+moe_status moe_pack_weights(const void* src, int64_t mats, int32_t rows, int32_t cols, int32_t elem_bytes,
+                            void* dst, void* stream) {
+  if (mats < 0 || rows < 0 || cols < 0 || cols % 32 != 0 || (elem_bytes != 1 && elem_bytes != 2))
+    return MOE_ERR_INVALID;
+  const unsigned __int128 wide = (unsigned __int128)mats * uint32_t(rows) * uint32_t(cols) * uint32_t(elem_bytes);
+  if (wide > ((unsigned __int128)1 << 40)) return MOE_ERR_INVALID;
+  const int64_t bytes = int64_t(wide);
+  if (bytes == 0) return MOE_OK;
+  if (!need(src) || !need(dst)) return MOE_ERR_INVALID;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + uint64_t(bytes) && d0 < s0 + uint64_t(bytes)) return MOE_ERR_INVALID;  // overlap
+  return dev(launch_pack_kblocked(src, mats, rows, cols, elem_bytes, dst, static_cast<hipStream_t>(stream)));
+}
 
 moe_status moe_workspace_size(const moe_desc* desc, moe_stage stage, size_t* bytes) {
   MOE_TRY(check_desc(desc));

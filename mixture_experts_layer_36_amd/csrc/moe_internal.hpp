@@ -221,7 +221,15 @@ struct GemmArgs {
   int a_blk;
   int sh_a_blk;
   int c_blk;
+  // Routed weights B0/B1 in the K-blocked layout (P = N per expert matrix);
+  // the extra segment's weights are row-major.  bf16 / fp8 weights only.
+  int b_blk;
 };
+
+// Row-major [mats][rows][cols] -> K-blocked [mats][cols/32][rows][32] of
+// elem_bytes-byte elements (1 or 2).
+hipError_t launch_pack_kblocked(const void* src, int64_t mats, int rows, int cols, int elem_bytes, void* dst,
+                                hipStream_t s);
 
 // Bytes of one partial-sum slot (one 256 x 256 tile of fp32 accumulators) and
 // the slots a launch may use (at most one per compute unit).

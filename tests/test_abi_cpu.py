@@ -63,6 +63,11 @@ def test_status_strings():
     (dict(dispatch_fp8=True, act="bf16", wdtype="e4m3"), moe.MOE_OK),
     (dict(dispatch_fp8=True, act="bf16", wdtype="bf16"), moe.MOE_OK),
     (dict(dispatch_fp8=True, act="f32", wdtype="f32"), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act="bf16", wdtype="bf16", w_layout="kblocked"), moe.MOE_OK),
+    (dict(act="bf16", wdtype="e4m3", w_layout="kblocked"), moe.MOE_OK),
+    (dict(w_layout="kblocked"), moe.MOE_ERR_UNSUPPORTED),                     # f32 weights
+    (dict(act="bf16", wdtype="bf16", w_layout="kblocked", d=32768, f=32768), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act="bf16", wdtype="e4m3", w_layout="kblocked", d=32768, f=32768), moe.MOE_OK),
 ])
 def test_validate(kw, code):
     assert moe.validate(_good(**kw)) == code
@@ -72,6 +77,26 @@ def test_overflow_mode_is_drop_or_reroute():
     d = _good(capacity=5)
     d.overflow = 2
     assert moe.validate(d) == moe.MOE_ERR_INVALID
+
+
+def test_w_layout_is_rowmajor_or_kblocked():
+    d = _good(act="bf16", wdtype="bf16")
+    d.w_layout = 2
+    assert moe.validate(d) == moe.MOE_ERR_INVALID
+
+
+def test_pack_weights_rejects_bad_arguments_before_launch():
+    P = ctypes.c_void_p
+    src, dst = P(FAKE), P(FAKE + (1 << 24))
+    f = _lib._lib().moe_pack_weights
+    assert f(src, 2, 64, 48, 2, dst, None) == moe.MOE_ERR_INVALID        # cols % 32
+    assert f(src, 2, 64, 64, 4, dst, None) == moe.MOE_ERR_INVALID        # element size
+    assert f(src, -1, 64, 64, 2, dst, None) == moe.MOE_ERR_INVALID
+    assert f(None, 2, 64, 64, 2, dst, None) == moe.MOE_ERR_INVALID
+    assert f(P(FAKE + 4), 2, 64, 64, 2, dst, None) == moe.MOE_ERR_INVALID  # misaligned
+    assert f(src, 2, 64, 64, 2, P(FAKE + 4096), None) == moe.MOE_ERR_INVALID  # overlapping
+    assert f(src, 1 << 30, 1 << 10, 1 << 10, 2, dst, None) == moe.MOE_ERR_INVALID  # > 2^40 bytes
+    assert f(None, 0, 64, 64, 2, None, None) == moe.MOE_OK               # nothing to pack
 
 
 def test_dispatch_fp8_flag_is_0_or_1():

@@ -107,15 +107,16 @@ def _scores(L):
     return O.expert_scores(O.router_logits(x, wr, b), L.w.score)
 
 
-def _run_layer(w, dev, desc=None):
+def _run_layer(w, dev, desc=None, weights=None):
     desc = desc or moe.Desc.from_attrs(w)
+    w1, w3, w2 = weights or (dev.w1, dev.w3, dev.w2)
     T = w.T
     out = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
     idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
     gw = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
     counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
     ws = moe.workspace(desc)
-    moe.layer_forward(desc, dev.x, dev.w_router, dev.bias, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3,
+    moe.layer_forward(desc, dev.x, dev.w_router, dev.bias, w1, w3, w2, dev.s1, dev.s3,
                       dev.s2, dev.sw1, dev.sw3, dev.sw2, out, idx, gw, counts, ws)
     torch.cuda.synchronize()
     return out, idx, gw, counts
@@ -280,6 +281,92 @@ def test_layer_matches_stage_chain_bitwise(name):
     torch.cuda.synchronize()
     assert torch.equal(counts, counts2)
     assert torch.equal(out_l, out_c)
+
+
+# ------------------------------------------------- K-blocked expert weights
+
+@pytest.mark.parametrize("shape,dtype", [((3, 384, 256), torch.bfloat16), ((2, 128, 96), torch.uint8),
+                                         ((1, 1, 32), torch.bfloat16), ((5, 7, 64), torch.uint8)])
+def test_pack_weights_layout(shape, dtype):
+    """moe_pack_weights against the layout's definition: element (n, c) of a
+    matrix at (c / 32) * N * 32 + n * 32 + c % 32."""
+    g = torch.Generator().manual_seed(5)
+    w = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    if dtype == torch.bfloat16:
+        w = torch.randint(-2 ** 15, 2 ** 15, shape, generator=g, dtype=torch.int32).to(torch.int16).view(dtype)
+    wd = w.cuda()
+    packed = moe.pack_weights(wd)
+    torch.cuda.synchronize()
+    M, N, K = shape
+    expect = w.view(M, N, K // 32, 32).permute(0, 2, 1, 3).contiguous().view(shape)
+    bits = torch.uint8 if dtype == torch.uint8 else torch.int16  # random patterns include NaNs
+    assert torch.equal(packed.cpu().view(bits), expect.view(bits))
+
+
+def _packed(dev):
+    return moe.pack_weights(dev.w1), moe.pack_weights(dev.w3), moe.pack_weights(dev.w2)
+
+
+KBLOCKED_CASES = [
+    # weight-streaming decode kernel (with the shared segment)
+    "dsv3_decode_small", "decode_k128", "decode_shared_wide", "decode_f8d", "decode_cap",
+    # 128-row kernel: bf16 and fp8 weights, shared expert
+    "mixtral_small", "mixtral_tiles", "qwen_fp8_small", "dsv3_skew_small", "qwen_f8d_small",
+    # 256-row kernel: half tiles, K-split tiles, K = 128, N = 128 tiles, fp8
+    # weights, wide f (blocked x_perm), shared segment, payload values
+    "mixtral_big_tiles", "mixtral_big_split", "mixtral_big_k128", "qwen_fp8_big", "qwen_fp8_big_n128",
+    "mixtral_wide_f", "dsv3_big_shared", "mixtral_big_f8d",
+    # fp8 x fp8 gate-up kernel
+    "qwen_f8d_big", "qwen_f8d_split", "qwen_f8d_n128",
+    # capacity: dropped and rerouted rows
+    "mixtral_big_cap", "qwen_f8d_cap_rr", "dsv3_skew_cap_rr",
+]
+
+
+@pytest.mark.parametrize("name", KBLOCKED_CASES)
+def test_layer_kblocked_weights_bitwise(name):
+    """Routed weights packed K-blocked: every kernel multiplies the same
+    values in the same order, so the layer's outputs are those of the
+    row-major weights bit for bit (which the oracle checks elsewhere)."""
+    w, L, dev, ref = _setup(name)
+    a = _run_layer(w, dev)
+    desc = moe.Desc.from_attrs(w)
+    desc.w_layout = moe.W_KBLOCKED
+    b = _run_layer(w, dev, desc, _packed(dev))
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("name", ["mixtral_big_split", "qwen_f8d_split", "dsv3_decode_small", "qwen_fp8_small",
+                                  "qwen_fp8_big"])
+def test_grouped_ffn_kblocked_weights_bitwise(name):
+    w, L, dev, ref = _setup(name)
+    desc = moe.Desc.from_attrs(w)
+    T, A = w.T, w.T * w.k
+    idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+    moe.route(desc, dev.x, dev.w_router, dev.bias, idx, gw, moe.workspace(desc, moe.STAGE_ROUTE))
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(A, dtype=torch.int32, device="cuda")
+    inv = torch.empty(A, dtype=torch.int32, device="cuda")
+    if w.dispatch_fp8:
+        x_perm = torch.empty(moe.fp8_payload_bytes(A, w.d), dtype=torch.uint8, device="cuda")
+    else:
+        x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.dispatch(desc, idx, dev.x, counts, offsets, perm, inv, x_perm, moe.workspace(desc, moe.STAGE_DISPATCH))
+    outs = []
+    for layout, (w1, w3, w2) in ((moe.W_ROWMAJOR, (dev.w1, dev.w3, dev.w2)), (moe.W_KBLOCKED, _packed(dev))):
+        desc.w_layout = layout
+        h = torch.zeros((A, w.f), dtype=dev.x.dtype, device="cuda")
+        y = torch.zeros((A, w.d), dtype=dev.x.dtype, device="cuda")
+        moe.grouped_ffn(desc, x_perm, offsets, w1, w3, w2, dev.s1, dev.s3, dev.s2, h, y,
+                        moe.workspace(desc, moe.STAGE_FFN))
+        torch.cuda.synchronize()
+        outs.append((h, y))
+    n = int(offsets[-1])
+    assert torch.equal(outs[0][0][:n], outs[1][0][:n])
+    assert torch.equal(outs[0][1][:n], outs[1][1][:n])
 
 
 # ----------------------------------------------------------------- edge cases
