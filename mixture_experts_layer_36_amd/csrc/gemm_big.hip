@@ -967,7 +967,8 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
 
 hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t s) {
   if (a.act == GD_FP8) return launch_big<256, EPI_SWIGLU, GD_FP8, true>(a, s);  // checked by the caller
-  if (a.epi == EPI_BIAS_F32) return launch_big<256, EPI_BIAS_F32, GD_BF16>(a, s);
+  if (a.epi == EPI_BIAS_F32)  // router logits: 128-wide tiles unless E fills 256-wide ones
+    return (a.N % 256 == 0) ? launch_big<256, EPI_BIAS_F32, GD_BF16>(a, s) : launch_big<128, EPI_BIAS_F32, GD_BF16>(a, s);
   if (a.wdt == GD_FP8) {
     if (a.epi == EPI_SWIGLU) return launch_big<256, EPI_SWIGLU, GD_FP8>(a, s);
     return (a.N % 256 == 0) ? launch_big<256, EPI_STORE, GD_FP8>(a, s) : launch_big<128, EPI_STORE, GD_FP8>(a, s);

@@ -145,9 +145,11 @@ int route_splits(const moe_desc* d) {
   const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
   const int64_t part_bytes = int64_t(d->T) * d->E * 4;
   if (bm == 256) {
-    // 256 x 256 tiles: split K until one wave of the GPU is filled, each
-    // range at least 8 stages of 32, the partial sums at most twice the input
-    const int64_t tiles = int64_t((d->T + 255) / 256) * ((d->E + 255) / 256);
+    // 256-row tiles, 256 or 128 wide: split K until one wave of the GPU is
+    // filled, each range at least 8 stages of 32, the partial sums at most
+    // twice the input
+    const int bn = d->E % 256 == 0 ? 256 : 128;
+    const int64_t tiles = int64_t((d->T + 255) / 256) * ((d->E + bn - 1) / bn);
     int64_t want = (256 + tiles - 1) / tiles;
     want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
     want = std::min<int64_t>(want, std::max<int64_t>(1, d->d / 256));

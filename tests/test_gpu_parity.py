@@ -85,6 +85,10 @@ CASES = {
     # planes (ragged expert tails; with a capacity the gather stops early)
     "mixtral_wide_f": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4),
     "mixtral_wide_f_cap": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4, capacity_factor=1.0),
+    # router logits on the 256-row kernel (T >= 1024, E >= 128): one 128-wide
+    # column tile (E = 128) and three (E = 384), K split across the GPU
+    "router_big_e128": QWEN_FP8_SKEW.scaled(T=1100, d=512, f=128, E=128, k=2),
+    "router_big_e384": QWEN_FP8_SKEW.scaled(T=1100, d=384, f=128, E=384, k=4),
     "dsv3_big_shared": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384),
     "dsv3_big_shared_f8d": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384,
                                                     dispatch_fp8=True),
