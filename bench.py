@@ -102,18 +102,30 @@ def fp8_gate_up(w) -> bool:
             and w.d % 64 == 0)
 
 
+def gathers_blocked(w) -> bool:
+    """Whether the layer gathers x_perm into K-blocked planes rather than
+    fusing the gather into the gate-up GEMM: bf16 activations without the
+    payload, f >= 4096, on the prefill kernel's shapes (the library's rule)."""
+    rows = w.T * w.k
+    return (w.act == "bf16" and not w.dispatch_fp8 and w.f >= 4096 and rows >= 1024
+            and rows // w.E >= 128 and rows * w.d * 2 < (1 << 31))
+
+
 def stage_bytes(w, has_bias: bool, kept: int) -> dict:
     """Algorithmic bytes of the memory-bound stages of the layer path:
     route = x + router weight (+ bias) + the top-k indices and gates written;
     dispatch = the index work (top-k ids read, per-expert counts and offsets,
     perm_token and inv_pos written) -- the row gather itself is fused into the
-    gate-up GEMM's activation loads; combine = the routed rows read (T*k, or
+    gate-up GEMM's activation loads, or, for wide experts, the kept rows of x
+    read and x_perm written; combine = the routed rows read (T*k, or
     those kept under a capacity), the
     indices and gates, out written (+ the shared expert's rows read)."""
     ab = 4 if w.act == "f32" else 2
     tk = w.T * w.k
     route = w.T * w.d * ab + w.E * w.d * ab + (w.E * 4 if has_bias else 0) + 8 * tk
     dispatch = 4 * tk + 8 * tk + 8 * w.E
+    if gathers_blocked(w):
+        dispatch += 2 * kept * w.d * ab
     if w.dispatch_fp8:  # x read once, its payload (codes + scale rows) written in token order
         dispatch += w.T * w.d * ab + w.T * (w.d + (w.d // 32 + 15) // 16 * 16)
     combine = kept * w.d * ab + 8 * tk + w.T * w.d * ab + (w.T * w.d * ab if w.f_shared else 0)
