@@ -85,6 +85,11 @@ CASES = {
     # planes (ragged expert tails; with a capacity the gather stops early)
     "mixtral_wide_f": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4),
     "mixtral_wide_f_cap": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4, capacity_factor=1.0),
+    # ... with fp8 weights, and beside a fused shared expert (which keeps
+    # reading x row-major while the routed rows come K-blocked)
+    "qwen_wide_f": QWEN_FP8_SKEW.scaled(T=1100, d=256, f=4096, E=4, k=2),
+    "dsv3_wide_f_shared": DSV3_PREFILL_SKEW.scaled(T=1100, d=256, f=4096, E=8, k=2, n_group=4, topk_group=2,
+                                                   f_shared=256),
     # router logits on the 256-row kernel (T >= 1024, E >= 128): one 128-wide
     # column tile (E = 128) and three (E = 384), K split across the GPU
     "router_big_e128": QWEN_FP8_SKEW.scaled(T=1100, d=512, f=128, E=128, k=2),
@@ -257,7 +262,7 @@ def test_deterministic(name):
 
 @pytest.mark.parametrize("name", ["mixtral_big_tiles", "mixtral_big_k128", "mixtral_big_split", "qwen_fp8_big",
                                   "qwen_fp8_big_n128", "mixtral_big_f8d", "qwen_f8d_split", "mixtral_big_cap",
-                                  "mixtral_wide_f", "mixtral_wide_f_cap"])
+                                  "mixtral_wide_f", "mixtral_wide_f_cap", "qwen_wide_f"])
 def test_layer_matches_stage_chain_bitwise(name):
     """On the 256-row kernel the layer keeps h (and for f >= 4096 x_perm) in
     K-blocked planes, or reads x through the row map; the stage entry points
@@ -319,7 +324,7 @@ KBLOCKED_CASES = [
     # 256-row kernel: half tiles, K-split tiles, K = 128, N = 128 tiles, fp8
     # weights, wide f (blocked x_perm), shared segment, payload values
     "mixtral_big_tiles", "mixtral_big_split", "mixtral_big_k128", "qwen_fp8_big", "qwen_fp8_big_n128",
-    "mixtral_wide_f", "dsv3_big_shared", "mixtral_big_f8d",
+    "mixtral_wide_f", "qwen_wide_f", "dsv3_wide_f_shared", "dsv3_big_shared", "mixtral_big_f8d",
     # fp8 x fp8 gate-up kernel
     "qwen_f8d_big", "qwen_f8d_split", "qwen_f8d_n128",
     # capacity: dropped and rerouted rows
