@@ -203,6 +203,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Buffer descriptor word 3 for raw 32-bit-format buffers on gfx9-family GPUs.
 [[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
 
+// A buffer descriptor from block-uniform values, stated uniform: a base
+// whose 64-bit offset was computed on the vector unit otherwise leaves the
+// compiler unsure, and it wraps every load through the descriptor in a
+// loop over distinct lane values.
+[[maybe_unused]] __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
 // Output columns of a tile and the LDS bytes of its staged copy.
 template <int BN, int EPI>
 struct OutTile {
@@ -347,10 +359,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   const int a_plane = sg.a_prows * BK * 2;  // 0: row-major
   const int a_step = a_plane ? a_plane : BK * 2;  // bytes from one stage's slice to the next
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      a_plane ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, (K / BK) * a_plane, kBufferFlags)
-      : sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K * 2, kBufferFlags)
-                : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K * 2), (short)0,
-                                                    ti.nrows * K * 2, kBufferFlags);
+      a_plane ? uniform_rsrc(sg.A, (K / BK) * a_plane)
+      : sg.amap ? uniform_rsrc(sg.A, a.a_map_rows * K * 2)
+                : uniform_rsrc(sg.A + (size_t)ti.row0 * K * 2, ti.nrows * K * 2);
   uint32_t a_off[M::A_LOADS];
 #pragma unroll
   for (int j = 0; j < M::A_LOADS; ++j) {
@@ -376,10 +387,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   const int b_step = sg.b_blk ? b_plane : BK * M::WB;  // bytes from one stage's slice to the next
   const size_t b_start = (size_t)ncol0 * (sg.b_blk ? BK : K) * M::WB;
   const int b_bytes = sg.b_blk ? (K / BK) * b_plane - ncol0 * BK * M::WB : b_rows * K * M::WB;
-  const __amdgpu_buffer_rsrc_t b0_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sg.B0 + b_start), (short)0, b_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t b0_rsrc = uniform_rsrc(sg.B0 + b_start, b_bytes);
+  const __amdgpu_buffer_rsrc_t b1_rsrc = uniform_rsrc((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start, b_bytes);
   constexpr int BCH = BK * M::WB / 16;  // 16-byte chunks per weight row
   uint32_t b_off[M::B_LOADS];
   bool b_w3[M::B_LOADS];
@@ -620,9 +629,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
   const int kt0 = ck0 * SC_STAGES, KT = min(ck1 * SC_STAGES, KT_all) - kt0, NC = ck1 - ck0;
 
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      sg.amap ? __builtin_amdgcn_make_buffer_rsrc((void*)sg.A, (short)0, a.a_map_rows * K, kBufferFlags)
-              : __builtin_amdgcn_make_buffer_rsrc((void*)(sg.A + (size_t)ti.row0 * K), (short)0, ti.nrows * K,
-                                                  kBufferFlags);
+      sg.amap ? uniform_rsrc(sg.A, a.a_map_rows * K) : uniform_rsrc(sg.A + (size_t)ti.row0 * K, ti.nrows * K);
   uint32_t a_off[M::A_LOADS];
 #pragma unroll
   for (int j = 0; j < M::A_LOADS; ++j) {
@@ -637,10 +644,8 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
   const int b_plane = sg.b_blk ? sg.N * 32 : 0;
   const size_t b_start = (size_t)ncol0 * (sg.b_blk ? 32 : K);
   const int b_bytes = sg.b_blk ? (K / 32) * b_plane - ncol0 * 32 : b_rows * K;
-  const __amdgpu_buffer_rsrc_t b0_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(sg.B0 + b_start), (short)0, b_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t b1_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start), (short)0, b_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t b0_rsrc = uniform_rsrc(sg.B0 + b_start, b_bytes);
+  const __amdgpu_buffer_rsrc_t b1_rsrc = uniform_rsrc((EPI == EPI_SWIGLU ? sg.B1 : sg.B0) + b_start, b_bytes);
   const int b_step = sg.b_blk ? 2 * b_plane : BK8;
   uint32_t b_off[M::B_LOADS];
   bool b_w3[M::B_LOADS];
@@ -662,8 +667,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
   // end repeat its last row); waves past the loaded rows load nothing
   const uint8_t* s_base = sg.amap ? a.a_scales : a.a_scales + (size_t)ti.row0 * a.a_sstride;
   const int s_rows = sg.amap ? a.a_map_rows : ti.nrows;
-  const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)s_base, (short)0, s_rows * a.a_sstride, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t s_rsrc = uniform_rsrc(s_base, s_rows * a.a_sstride);
   uint32_t s_off;
   {
     const int rr = min(tid, ti.nrows - 1);
