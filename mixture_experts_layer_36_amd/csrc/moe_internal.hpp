@@ -25,9 +25,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15): gfx950's pair
+// conversion (v_cvt_pk_bf16_f32), one instruction.  It rounds to nearest,
+// ties to even, like f32_to_bf16: a probe over 8.4 M bit patterns (ties,
+// f32 subnormals, the largest finite values, infinities) matched it bit for
+// bit; only a NaN's payload bits may differ (a NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // OCP E4M3 byte -> bf16 bits (exact: every E4M3 value is a bf16 value).
