@@ -258,43 +258,40 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
     o[1] = pack_bf16x2(v2, v3);
     *(u32x2*)(lds + lrow * O::ROW_BYTES + (((lcol >> 3) ^ (lrow & 15)) << 4) + (lcol & 7) * 2) = o;
   };
-  auto raw = [&](int i, int j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      P[((i * C::TA + j) * 4 + q) * C::NTHR + tid] =
-          make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  auto raw = [&](int i, int j, int g) {
+    P[((i * C::TA + j) * 4 + g) * C::NTHR + tid] =
+        make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
   };
   constexpr int NB = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
 #pragma unroll
+  // Column group by column group (4 columns of 32 activation rows per lane
+  // and block): only that group's fp8 channel scales stay live, which cuts
+  // the fp8-weight epilogue's register spills by more than half.
   for (int i = 0; i < NB; ++i) {
-    float4 su[4], sv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int n = ncol0 + wcol + i * 32 + g * 8 + (lane >> 5) * 4;
-      su[g] = sv[g] = make_float4(1.f, 1.f, 1.f, 1.f);
+      const int lcol = wcol + i * 32 + g * 8 + (lane >> 5) * 4;
+      float4 su = make_float4(1.f, 1.f, 1.f, 1.f), sv = su;
       if (scaled) {
-        su[g] = *(const float4*)(sg.s0 + n);
-        if (EPI == EPI_SWIGLU) sv[g] = *(const float4*)(sg.s1 + n);
+        su = *(const float4*)(sg.s0 + ncol0 + lcol);
+        if (EPI == EPI_SWIGLU) sv = *(const float4*)(sg.s1 + ncol0 + lcol);
       }
-    }
+      const float s4u[4] = {su.x, su.y, su.z, su.w}, s4v[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-    for (int j = 0; j < C::TA; ++j) {
-      if (piece) {
-        raw(i, j);
-        if (EPI == EPI_SWIGLU) raw(i + C::TW / 2, j);
-      }
-      // a piece also fills the LDS copy (never stored): with no second path
-      // the compiler keeps the accumulators in AGPRs
-      const int lrow = arow + j * 32 + (lane & 31);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int lcol = wcol + i * 32 + g * 8 + (lane >> 5) * 4;
+      for (int j = 0; j < C::TA; ++j) {
+        if (piece) {
+          raw(i, j, g);
+          if (EPI == EPI_SWIGLU) raw(i + C::TW / 2, j, g);
+        }
+        // a piece also fills the LDS copy (never stored): with no second
+        // path the compiler keeps the accumulators in AGPRs
+        const int lrow = arow + j * 32 + (lane & 31);
         float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float u = acc[i][j][g * 4 + q] * su[g][q];
+          const float u = acc[i][j][g * 4 + q] * s4u[q];
           if (EPI == EPI_SWIGLU) {
-            const float v = acc[i + C::TW / 2][j][g * 4 + q] * sv[g][q];
+            const float v = acc[i + C::TW / 2][j][g * 4 + q] * s4v[q];
             o[q] = silu(u) * v;
           } else {
             o[q] = u;
@@ -302,7 +299,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
         }
         put(lrow, lcol, o[0], o[1], o[2], o[3]);
       }
-      // one block at a time: the accumulators leave the AGPRs as needed
+      // one group at a time: the accumulators leave the AGPRs as needed
       __builtin_amdgcn_sched_barrier(0);
     }
   }
