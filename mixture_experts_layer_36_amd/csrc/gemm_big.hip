@@ -35,7 +35,16 @@
 //     measured on gfx950 (64 banks; a 128-bit read is served 16 lanes at a
 //     time), these make the fragment reads of 32 rows x 1 chunk
 //     conflict-free.  A direct load writes 64 consecutive 16-byte slots, so
-//     each lane fetches the global chunk that belongs in its slot.
+//     each lane fetches the global chunk that belongs in its slot;
+//   * operands row-major or K-blocked (32-column planes of [rows][32]: the
+//     expert weights when packed, h between the two routed GEMMs, x_perm for
+//     wide experts): K-blocked, a stage's slice of a tile's consecutive rows
+//     is one contiguous run, so a 1 KB direct load covers 8 whole cache
+//     lines instead of 16 half lines;
+//   * every buffer descriptor is built from block-uniform values stated
+//     uniform (readfirstlane): otherwise the compiler cannot prove a base
+//     computed on the vector unit uniform and wraps each load through it in a
+//     loop over distinct lane values.
 #include "gemm_common.hpp"
 
 namespace moe {
