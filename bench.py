@@ -72,11 +72,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library's sources without their comments and blank lines:
+    it changes with the code the counters in profiles/traffic.json were
+    taken on, not with its documentation."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_36_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            code = [ln.split("//", 1)[0].rstrip() for ln in fh]
+        h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 
