@@ -132,8 +132,9 @@ typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_KBLOCKED = 1 } moe_w_layout;
  * by the sum of the token's top-k scores when renorm = 1.  Rows of an expert
  * are its pass-1 rows, then its pass-2 rows, each in increasing a.  counts
  * stay the demand of the top-k; topk_idx and topk_w stay the router's top-k.
- * Only moe_layer_forward takes this mode; moe_dispatch returns
- * MOE_ERR_UNSUPPORTED for it (the router stage does not return candidates). */
+ * moe_layer_forward runs it whole; as stages, moe_route_candidates returns
+ * the candidates and moe_dispatch_reroute dispatches with them (moe_dispatch
+ * returns MOE_ERR_UNSUPPORTED for this mode). */
 
 /* fp8 dispatch payload (dispatch_fp8 = 1).  Each row of x is cut into blocks
  * of 32 elements; a block with largest magnitude amax gets the scale 2^s, s
@@ -186,6 +187,20 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
                      const float* bias, int32_t* topk_idx, float* topk_w,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The router plus each token's rerouting candidates (capacity overflow
+ * rerouted, overflow = MOE_OVERFLOW_REROUTE; see "Capacity overflow" above):
+ * moe_route's outputs, and
+ *   cand_idx [T][k] int32 out: candidate m of token t is its eligible expert
+ *            of rank k + m in the router's order, -1 where fewer than k + m + 1
+ *            experts are eligible
+ *   cand_w   [T][k] fp32  out: the candidate's gate, with the normalisation of
+ *            topk_w (its score over the sum of the top-k scores when renorm)
+ *   ws: moe_workspace_size(MOE_STAGE_ROUTE) bytes.
+ * For moe_dispatch_reroute; any overflow mode of desc is accepted. */
+moe_status moe_route_candidates(const moe_desc* desc, const void* x, const void* w_router, const float* bias,
+                                int32_t* topk_idx, float* topk_w, int32_t* cand_idx, float* cand_w, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* Dispatch.  For the T*k assignments a = t*k + j (expert topk_idx[t][j]):
  *   counts[e]      = number of assignments to expert e          int32 [E]
  *   kept[e]        = counts[e], or min(counts[e], capacity) with a capacity
@@ -209,6 +224,21 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const voi
                         int32_t* counts, int32_t* offsets, int32_t* perm_token,
                         int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* Dispatch with capacity overflow rerouted (desc: capacity > 0 and overflow =
+ * MOE_OVERFLOW_REROUTE, else MOE_ERR_INVALID): the two passes of "Capacity
+ * overflow" above, from moe_route_candidates' outputs.  Outputs as
+ * moe_dispatch -- inv_pos[a] is the row of the copy that serves assignment a
+ * (its own expert's, or its candidate's when rerouted), or -1 when dropped;
+ * an expert's rows are its pass-1 rows, then its pass-2 rows -- and
+ *   gates [T*k] fp32 out: the gate of the copy serving assignment a (topk_w,
+ *         or the candidate's cand_w when rerouted), to pass to moe_combine in
+ *         place of topk_w; unspecified where inv_pos[a] = -1.
+ * ws: moe_workspace_size(MOE_STAGE_DISPATCH) bytes for this desc. */
+moe_status moe_dispatch_reroute(const moe_desc* desc, const int32_t* topk_idx, const float* topk_w,
+                                const int32_t* cand_idx, const float* cand_w, const void* x, int32_t* counts,
+                                int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, float* gates,
+                                void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* Grouped expert FFN over the expert-contiguous rows.  Expert e transforms
  * rows [offsets[e], offsets[e+1]) of x_perm (act dtype [T*k][d], or with

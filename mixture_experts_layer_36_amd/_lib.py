@@ -26,7 +26,8 @@ TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "
 
 # the exported symbols include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows", "moe_pack_weights")
+           "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows", "moe_pack_weights",
+           "moe_route_candidates", "moe_dispatch_reroute")
 
 _DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
 OVERFLOW_DROP, OVERFLOW_REROUTE = 0, 1
@@ -125,6 +126,8 @@ def _lib() -> ctypes.CDLL:
         lib.moe_layer_rows.argtypes = [D, _P, ctypes.c_size_t, _P, _P]
         lib.moe_pack_weights.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          _P, _P]
+        lib.moe_route_candidates.argtypes = [D] + [_P] * 8 + [ctypes.c_size_t, _P]
+        lib.moe_dispatch_reroute.argtypes = [D] + [_P] * 12 + [ctypes.c_size_t, _P]
         for name in EXPORTS[1:]:
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -175,6 +178,20 @@ def route(desc, x, w_router, bias, topk_idx, topk_w, ws, stream=None):
     _check(_lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_idx),
                             _ptr(topk_w), _ptr(ws), ws.numel() if ws is not None else 0,
                             _stream(stream)), "moe_route")
+
+
+def route_candidates(desc, x, w_router, bias, topk_idx, topk_w, cand_idx, cand_w, ws, stream=None):
+    _check(_lib().moe_route_candidates(ctypes.byref(desc), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_idx),
+                                       _ptr(topk_w), _ptr(cand_idx), _ptr(cand_w), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)), "moe_route_candidates")
+
+
+def dispatch_reroute(desc, topk_idx, topk_w, cand_idx, cand_w, x, counts, offsets, perm_token, inv_pos, gates,
+                     x_perm, ws, stream=None):
+    _check(_lib().moe_dispatch_reroute(ctypes.byref(desc), _ptr(topk_idx), _ptr(topk_w), _ptr(cand_idx),
+                                       _ptr(cand_w), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(perm_token),
+                                       _ptr(inv_pos), _ptr(gates), _ptr(x_perm), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)), "moe_dispatch_reroute")
 
 
 def dispatch(desc, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, ws, stream=None):

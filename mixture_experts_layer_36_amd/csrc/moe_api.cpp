@@ -283,7 +283,7 @@ size_t stage_bytes(const moe_desc* d, moe_stage stage) {
   Carve c(nullptr);
   switch (stage) {
     case MOE_STAGE_ROUTE: carve_route(c, d, false); break;
-    case MOE_STAGE_DISPATCH: carve_dispatch(c, d, false); break;
+    case MOE_STAGE_DISPATCH: carve_dispatch(c, d, reroute(d)); break;
     case MOE_STAGE_FFN:
       carve_ffn(c, d, false);
       carve_ffn_xdq(c, d);
@@ -550,6 +550,47 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
   Carve c(ws);
   const RouteWs w = carve_route(c, d, false);
   return run_route(d, x, w_router, bias, topk_idx, topk_w, w, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_route_candidates(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                                int32_t* topk_idx, float* topk_w, int32_t* cand_idx, float* cand_w, void* ws,
+                                size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (d->T == 0) return MOE_OK;
+  if (!need(x) || !need(w_router) || !maybe(bias) || !need(topk_idx) || !need(topk_w) || !need(cand_idx) ||
+      !need(cand_w) || !need(ws))
+    return MOE_ERR_INVALID;
+  if (ws_bytes < stage_bytes(d, MOE_STAGE_ROUTE)) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  RouteWs w = carve_route(c, d, false);
+  w.cand_idx = cand_idx;
+  w.cand_w = cand_w;
+  return run_route(d, x, w_router, bias, topk_idx, topk_w, w, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch_reroute(const moe_desc* d, const int32_t* topk_idx, const float* topk_w,
+                                const int32_t* cand_idx, const float* cand_w, const void* x, int32_t* counts,
+                                int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, float* gates,
+                                void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(d));
+  if (!reroute(d)) return MOE_ERR_INVALID;
+  if (!need(counts) || !need(offsets)) return MOE_ERR_INVALID;
+  if (d->T > 0 && (!need(topk_idx) || !need(topk_w) || !need(cand_idx) || !need(cand_w) || !need(x) ||
+                   !need(perm_token) || !need(inv_pos) || !need(gates) || !need(x_perm) || !need(ws)))
+    return MOE_ERR_INVALID;
+  if (d->T > 0 && ws_bytes < stage_bytes(d, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
+  Carve c(ws);
+  const DispatchWs w = carve_dispatch(c, d, true);
+  RerouteArgs rr = w.rr;
+  rr.topk_w = topk_w;
+  rr.cand_idx = cand_idx;
+  rr.cand_w = cand_w;
+  rr.gate = gates;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, d->dispatch_fp8 ? nullptr : x_perm,
+                       w, s, &rr));
+  if (d->T == 0 || !d->dispatch_fp8) return MOE_OK;
+  return run_payload(d, x, perm_token, int(n_assign(d)), offsets + d->E, false, x_perm, s);
 }
 
 moe_status moe_dispatch(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t* counts,

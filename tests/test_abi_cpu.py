@@ -174,6 +174,28 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert _call("moe_combine", ctypes.byref(bad), ok, ok, ok, null, ok, null) == moe.MOE_ERR_INVALID
 
 
+def test_reroute_stage_entry_points_reject_bad_arguments():
+    d = _good(capacity=5, overflow="reroute")
+    D = ctypes.byref(d)
+    P = ctypes.c_void_p
+    ok, null = P(FAKE), None
+    # route + candidates: missing candidate outputs, short workspace
+    assert _call("moe_route_candidates", D, ok, ok, null, ok, ok, null, ok, ok, 1 << 30, null) == moe.MOE_ERR_INVALID
+    assert _call("moe_route_candidates", D, ok, ok, null, ok, ok, ok, ok, ok, 16, null) == moe.MOE_ERR_WORKSPACE
+    # rerouting dispatch: a descriptor without the reroute mode, a missing
+    # gates output, a short workspace
+    args = [ok] * 11  # topk_idx .. x_perm
+    drop = _good(capacity=5)
+    assert _call("moe_dispatch_reroute", ctypes.byref(drop), *args, ok, 1 << 30, null) == moe.MOE_ERR_INVALID
+    no_gates = list(args)
+    no_gates[9] = null
+    assert _call("moe_dispatch_reroute", D, *no_gates, ok, 1 << 30, null) == moe.MOE_ERR_INVALID
+    assert _call("moe_dispatch_reroute", D, *args, ok, 8, null) == moe.MOE_ERR_WORKSPACE
+    # the plain dispatch still refuses the mode; its workspace covers the reroute passes
+    assert _call("moe_dispatch", D, ok, ok, ok, ok, ok, ok, ok, ok, 1 << 30, null) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.workspace_size(d, moe.STAGE_DISPATCH) > moe.workspace_size(_good(capacity=5), moe.STAGE_DISPATCH)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(_lib, "_LIB", None)

@@ -14,7 +14,7 @@ import oracle as O
 from synth import LayerInputs
 from synth.workloads import (DSV3_DECODE, DSV3_PREFILL_SKEW, MIXTRAL_PREFILL, QWEN_FP8_SKEW,
                              TINY_F32)
-from tests.helpers import (DeviceLayer, assert_dispatch, assert_routing, assert_values,
+from tests.helpers import (GATE_TOL, DeviceLayer, assert_dispatch, assert_routing, assert_values,
                            from_torch, oracle_layer, to_torch)
 
 pytestmark = pytest.mark.gpu
@@ -290,6 +290,78 @@ def test_layer_matches_stage_chain_bitwise(name):
     torch.cuda.synchronize()
     assert torch.equal(counts, counts2)
     assert torch.equal(out_l, out_c)
+
+
+@pytest.mark.parametrize("name", ["mixtral_cap_rr", "mixtral_big_cap_rr", "dsv3_skew_cap_rr", "qwen_fp8_cap_rr",
+                                  "qwen_f8d_cap_rr", "decode_cap_rr", "tiny_f32_cap_rr"])
+def test_stages_chain_reroute(name):
+    """Rerouting as stages: moe_route_candidates -> moe_dispatch_reroute ->
+    moe_grouped_ffn -> moe_combine with the serving gates, each output checked
+    against the oracle, and the result equal to the whole layer's."""
+    w, L, dev, ref = _setup(name)
+    desc = moe.Desc.from_attrs(w)
+    T, A, k = w.T, w.T * w.k, w.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    cidx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    cw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.route_candidates(desc, dev.x, dev.w_router, dev.bias, idx, gw, cidx, cw, moe.workspace(desc, moe.STAGE_ROUTE))
+    torch.cuda.synchronize()
+    s = _scores(L)
+    assert_routing(idx.cpu().numpy(), gw.cpu().numpy(), ref, s)
+    # candidates: the oracle's from the same scores (indices exactly -- the
+    # inputs keep ranks up to 2k apart -- and gates to the gate tolerance)
+    ref_ci, ref_cw = O.reroute_candidates(s, O.workload_spec(w))
+    assert np.array_equal(cidx.cpu().numpy(), ref_ci)
+    have = ref_ci >= 0
+    np.testing.assert_allclose(cw.cpu().numpy()[have], ref_cw[have], rtol=0, atol=GATE_TOL)
+
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(A, dtype=torch.int32, device="cuda")
+    inv = torch.empty(A, dtype=torch.int32, device="cuda")
+    gates = torch.empty(A, dtype=torch.float32, device="cuda")
+    if w.dispatch_fp8:
+        x_perm = torch.empty(moe.fp8_payload_bytes(A, w.d), dtype=torch.uint8, device="cuda")
+    else:
+        x_perm = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.dispatch_reroute(desc, idx, gw, cidx, cw, dev.x, counts, offsets, perm, inv, gates, x_perm,
+                         moe.workspace(desc, moe.STAGE_DISPATCH))
+    torch.cuda.synchronize()
+    # the permutation and serving gates against the oracle's two passes, run
+    # on the GPU's own routing outputs
+    r_counts, r_off, r_perm, r_inv, r_gates, _ = O.dispatch_reroute(
+        idx.cpu().numpy(), gw.cpu().numpy().astype(np.float64), cidx.cpu().numpy(),
+        cw.cpu().numpy().astype(np.float64), w.E, desc.capacity)
+    assert np.array_equal(counts.cpu().numpy(), r_counts)
+    assert np.array_equal(offsets.cpu().numpy(), r_off)
+    n = int(r_off[-1])
+    assert np.array_equal(perm[:n].cpu().numpy(), r_perm)
+    inv_h = inv.cpu().numpy()
+    assert np.array_equal(inv_h, r_inv)
+    kept = inv_h >= 0
+    assert np.array_equal(gates.cpu().numpy()[kept], r_gates.reshape(-1)[kept].astype(np.float32))
+
+    h = torch.empty((A, w.f), dtype=dev.x.dtype, device="cuda")
+    y = torch.empty((A, w.d), dtype=dev.x.dtype, device="cuda")
+    moe.grouped_ffn(desc, x_perm, offsets, dev.w1, dev.w3, dev.w2, dev.s1, dev.s3, dev.s2, h, y,
+                    moe.workspace(desc, moe.STAGE_FFN))
+    out = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
+    shared_y = None
+    if w.f_shared:  # the shared expert as its own 1-segment FFN over all tokens, in order
+        sh_desc = moe.Desc.make(T, w.d, w.f_shared, 1, 1, act=w.act, wdtype=w.act)
+        sh_off = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+        sh_h = torch.empty((T, w.f_shared), dtype=dev.x.dtype, device="cuda")
+        shared_y = torch.empty((T, w.d), dtype=dev.x.dtype, device="cuda")
+        moe.grouped_ffn(sh_desc, dev.x, sh_off, dev.sw1.unsqueeze(0).contiguous(), dev.sw3.unsqueeze(0).contiguous(),
+                        dev.sw2.unsqueeze(0).contiguous(), None, None, None, sh_h, shared_y,
+                        moe.workspace(sh_desc, moe.STAGE_FFN))
+    moe.combine(desc, y, inv, gates, shared_y, out)
+    torch.cuda.synchronize()
+    assert_values(from_torch(out, w.act), ref.out, w, "out (stages)")
+    if not w.f_shared:  # the layer runs the same products in the same order
+        out_l, _, _, _ = _run_layer(w, dev)
+        assert torch.equal(out, out_l)
 
 
 # ------------------------------------------------- K-blocked expert weights
