@@ -85,6 +85,8 @@ CASES = {
     # planes (ragged expert tails; with a capacity the gather stops early)
     "mixtral_wide_f": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4),
     "mixtral_wide_f_cap": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4, capacity_factor=1.0),
+    "mixtral_wide_f_rr": MIXTRAL_PREFILL.scaled(T=1100, d=256, f=4096, E=4, capacity_factor=1.0,
+                                                overflow="reroute"),
     # ... with fp8 weights, and beside a fused shared expert (which keeps
     # reading x row-major while the routed rows come K-blocked)
     "qwen_wide_f": QWEN_FP8_SKEW.scaled(T=1100, d=256, f=4096, E=4, k=2),
@@ -293,7 +295,7 @@ def test_layer_matches_stage_chain_bitwise(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_cap_rr", "mixtral_big_cap_rr", "dsv3_skew_cap_rr", "qwen_fp8_cap_rr",
-                                  "qwen_f8d_cap_rr", "decode_cap_rr", "tiny_f32_cap_rr"])
+                                  "qwen_f8d_cap_rr", "decode_cap_rr", "tiny_f32_cap_rr", "mixtral_wide_f_rr"])
 def test_stages_chain_reroute(name):
     """Rerouting as stages: moe_route_candidates -> moe_dispatch_reroute ->
     moe_grouped_ffn -> moe_combine with the serving gates, each output checked
@@ -400,7 +402,7 @@ KBLOCKED_CASES = [
     # fp8 x fp8 gate-up kernel
     "qwen_f8d_big", "qwen_f8d_split", "qwen_f8d_n128",
     # capacity: dropped and rerouted rows
-    "mixtral_big_cap", "qwen_f8d_cap_rr", "dsv3_skew_cap_rr",
+    "mixtral_big_cap", "qwen_f8d_cap_rr", "dsv3_skew_cap_rr", "mixtral_wide_f_rr",
 ]
 
 
