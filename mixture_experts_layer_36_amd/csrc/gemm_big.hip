@@ -17,9 +17,10 @@
 //   * the LDS fragments of the next k16 step are read while the current
 //     step's MFMAs run (two fragment sets, interleaved by
 //     sched_group_barrier), across the stage boundary too;
-//   * an expert's last tile with at most 128 rows runs a half-height layout
-//     (all four wavefronts on the 128 rows, each with half the weight rows),
-//     so a short tail costs half a tile rather than a whole one;
+//   * an expert's last tile with at most 128 (64) rows runs a half-height
+//     (quarter-height) layout: all four wavefronts on those rows, each with
+//     half the weight rows, so a short tail loads and multiplies only its
+//     own rows rather than a whole tile's;
 //   * tiles that remain after the last full wave of tiles (one tile per
 //     compute unit) are split along K into pieces that fill that wave; each
 //     piece stores its raw fp32 accumulators and a fixup kernel adds the
@@ -57,23 +58,28 @@ constexpr int BM = 256, BK = 32, STAGES = 4;
 constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
 [[maybe_unused]] constexpr int KK = BK / 16;       // k16 MFMA steps per stage
 
-// Full layout: WN wavefronts along the weight rows, 2 along the 256
-// activation rows, each wave 128 activation rows x RW weight rows.  Half
-// layout (tiles of at most 128 rows): all 2*WN wavefronts on the 128
-// activation rows, each with RW/2 weight rows.  The LDS ring is the same.
-template <int BN, int WN, bool HALF>
+// Tile layouts, LAY = 0, 1, 2.  Full (0): WN wavefronts along the weight
+// rows, 2 along the 256 activation rows, each wave 128 activation rows x RW
+// weight rows.  Half (1, tiles of at most 128 rows): all 2*WN wavefronts on
+// the 128 activation rows, each with RW/2 weight rows.  Quarter (2, at most
+// 64 rows): the same weight split over 64 activation rows.  The LDS ring is
+// the same; a shorter layout loads and multiplies only its rows.
+template <int BN, int WN, int LAY>
 struct BigCfg {
   static constexpr int NTHR = 128 * WN;
   static constexpr int RW = BN / WN;                 // weight rows per wave column (full layout)
-  static constexpr int TA = 4;                       // 128 activation rows per wave
-  static constexpr int TW = HALF ? RW / 64 : RW / 32;
-  static constexpr int A_ROWS = HALF ? BM / 2 : BM;  // activation rows loaded
-  static_assert(TW >= 1, "layout");
+  static constexpr int TA = LAY == 2 ? 2 : 4;        // 32-row activation blocks per wave
+  static constexpr int TW = LAY ? RW / 64 : RW / 32;
+  static constexpr int A_ROWS = BM >> LAY;           // activation rows loaded
+  static_assert(TW >= 1 && LAY >= 0 && LAY <= 2, "layout");
 };
+
+// The layout of a tile with `nrows` rows.
+__device__ __forceinline__ int tile_layout(int nrows) { return nrows <= BM / 4 ? 2 : nrows <= BM / 2 ? 1 : 0; }
 
 // Stage bytes and 16-byte loads per thread.  bf16 weight rows are BK * 2 = 64
 // bytes (4 chunks); fp8 (E4M3) rows are 32 bytes (2 chunks), half the traffic.
-template <int BN, int WN, bool HALF, int WDT>
+template <int BN, int WN, int LAY, int WDT>
 struct BigMem {
   static constexpr int NTHR = 128 * WN;
   static constexpr int WB = (WDT == GD_FP8) ? 1 : 2;  // weight bytes per element
@@ -81,7 +87,7 @@ struct BigMem {
   static constexpr int B_BYTES = BN * BK * WB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
-  static constexpr int A_LOADS = BigCfg<BN, WN, HALF>::A_ROWS * BK * 2 / 16 / NTHR;
+  static constexpr int A_LOADS = BigCfg<BN, WN, LAY>::A_ROWS * BK * 2 / 16 / NTHR;
   static constexpr int B_LOADS = B_BYTES / 16 / NTHR;
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "layout");
@@ -112,23 +118,23 @@ struct BigMem {
 // tiles hold, per wave column of the full layout, RW/2 rows of W1 followed
 // by the same columns of W3, and a wave's blocks i < TW/2 are W1 (u), the
 // blocks i + TW/2 the matching W3 (v).
-template <int BN, int WN, bool HALF, int EPI>
+template <int BN, int WN, int LAY, int EPI>
 __device__ __forceinline__ int wave_wrow(int wave, int i) {
-  using C = BigCfg<BN, WN, HALF>;
-  if (!HALF) return (wave % WN) * C::RW + i * 32;
+  using C = BigCfg<BN, WN, LAY>;
+  if (!LAY) return (wave % WN) * C::RW + i * 32;
   if (EPI != EPI_SWIGLU) return wave * (C::RW / 2) + i * 32;
   const int slab = wave >> 1, sub = wave & 1;
   return i < C::TW / 2 ? slab * C::RW + sub * (C::RW / 4) + i * 32
                        : slab * C::RW + C::RW / 2 + sub * (C::RW / 4) + (i - C::TW / 2) * 32;
 }
-template <int BN, int WN, bool HALF>
+template <int BN, int WN, int LAY>
 __device__ __forceinline__ int wave_arow(int wave) {
-  return HALF ? 0 : (wave / WN) * 128;
+  return LAY ? 0 : (wave / WN) * 128;
 }
-template <int BN, int WN, bool HALF, int EPI>
+template <int BN, int WN, int LAY, int EPI>
 __device__ __forceinline__ int wave_col(int wave) {
-  using C = BigCfg<BN, WN, HALF>;
-  if (!HALF) return (wave % WN) * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
+  using C = BigCfg<BN, WN, LAY>;
+  if (!LAY) return (wave % WN) * (EPI == EPI_SWIGLU ? C::RW / 2 : C::RW);
   if (EPI != EPI_SWIGLU) return wave * (C::RW / 2);
   return (wave >> 1) * (C::RW / 2) + (wave & 1) * (C::RW / 4);
 }
@@ -247,15 +253,15 @@ struct OutTile {
 //   * A piece stores its raw accumulators to its partial slot, register-major
 //     so that each 16-byte store of a wave is contiguous.
 // Both are handled block by block in one pass.
-template <int BN, int WN, int EPI, bool HALF, int WDT>
+template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
-                                            f32x16 (&acc)[BigCfg<BN, WN, HALF>::TW][BigCfg<BN, WN, HALF>::TA],
+                                            f32x16 (&acc)[BigCfg<BN, WN, LAY>::TW][BigCfg<BN, WN, LAY>::TA],
                                             int ncol0, char* lds, int slot) {
-  using C = BigCfg<BN, WN, HALF>;
+  using C = BigCfg<BN, WN, LAY>;
   using O = OutTile<BN, EPI>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int arow = wave_arow<BN, WN, HALF>(wave), wcol = wave_col<BN, WN, HALF, EPI>(wave);
+  const int arow = wave_arow<BN, WN, LAY>(wave), wcol = wave_col<BN, WN, LAY, EPI>(wave);
   const bool piece = slot >= 0;
   const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr && !piece;
   float4* P = (float4*)(a.partial + (size_t)(piece ? slot : 0) * (kPartialSlotBytes / 4));
@@ -334,12 +340,12 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
   }
 }
 
-// One tile (or K-piece of a tile) in the full or the half layout.
-template <int BN, int WN, int EPI, bool HALF, int WDT>
+// One tile (or K-piece of a tile) in the full, half or quarter layout.
+template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
                                          int ncol0, char* lds) {
-  using C = BigCfg<BN, WN, HALF>;
-  using M = BigMem<BN, WN, HALF, WDT>;
+  using C = BigCfg<BN, WN, LAY>;
+  using M = BigMem<BN, WN, LAY, WDT>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int K = sg.K;
@@ -447,7 +453,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   // Fragments of one k16 step: the wave's weight blocks and activation blocks.
-  const int arow = wave_arow<BN, WN, HALF>(wave);
+  const int arow = wave_arow<BN, WN, LAY>(wave);
   struct Frags {
     bf16x8 w[C::TW], x[C::TA];
   };
@@ -462,7 +468,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     const int c = (WDT == GD_FP8) ? 2 * h + kk : kk * 2 + h;
 #pragma unroll
     for (int i = 0; i < C::TW; ++i) {
-      const int wr = wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31);
+      const int wr = wave_wrow<BN, WN, LAY, EPI>(wave, i) + (lane & 31);
       if (WDT == GD_FP8) {
         if (kk == 0) w8[i] = *(const u32x4*)(L + M::A_BYTES + f8_off(wr, h));
         F.w[i] = kk == 0 ? e4m3x8_to_bf16(w8[i][0], w8[i][1]) : e4m3x8_to_bf16(w8[i][2], w8[i][3]);
@@ -534,9 +540,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
 
   if constexpr (EPI == EPI_BIAS_F32)  // router logits: never split (K ranges go to blockIdx.y)
-    store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, HALF, EPI>(wave), lane);
+    store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, LAY, EPI>(wave), lane);
   else
-    finish_tile<BN, WN, EPI, HALF, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot);
+    finish_tile<BN, WN, EPI, LAY, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot);
 }
 #endif
 
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
                                                                 int n_cu) {
   // device pass only: the host pass needs just the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int RING = STAGES * BigMem<BN, WN, false, WDT>::STAGE_BYTES;
+  constexpr int RING = STAGES * BigMem<BN, WN, 0, WDT>::STAGE_BYTES;
   constexpr int OUT = (EPI == EPI_BIAS_F32) ? 0 : OutTile<BN, EPI>::BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[RING > OUT ? RING : OUT];
   Work wk;
@@ -555,10 +561,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   if (!tile_info(a, wk.mt, BM, ti, sg)) return;
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
-  if (ti.nrows <= BM / 2)
-    big_tile<BN, WN, EPI, true, WDT>(a, ti, sg, wk, ncol0, lds);
-  else
-    big_tile<BN, WN, EPI, false, WDT>(a, ti, sg, wk, ncol0, lds);
+  switch (tile_layout(ti.nrows)) {
+    case 2: big_tile<BN, WN, EPI, 2, WDT>(a, ti, sg, wk, ncol0, lds); break;
+    case 1: big_tile<BN, WN, EPI, 1, WDT>(a, ti, sg, wk, ncol0, lds); break;
+    default: big_tile<BN, WN, EPI, 0, WDT>(a, ti, sg, wk, ncol0, lds);
+  }
 #endif
 }
 
@@ -618,11 +625,11 @@ __device__ __forceinline__ void sched_quarter() {
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)
-template <int BN, int WN, int EPI, bool HALF>
+template <int BN, int WN, int EPI, int LAY>
 __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
                                              int ncol0, char* lds) {
-  using C = BigCfg<BN, WN, HALF>;
-  using M = BigMem<BN, WN, HALF, GD_BF16>;  // 64-byte rows on both operands: the bf16 stage geometry
+  using C = BigCfg<BN, WN, LAY>;
+  using M = BigMem<BN, WN, LAY, GD_BF16>;  // 64-byte rows on both operands: the bf16 stage geometry
   static_assert(C::NTHR == BM, "one scale row per thread");
   constexpr int TW2 = C::TW / 2, TA2 = C::TA / 2;
   static_assert(TW2 >= 1 && TA2 >= 1, "quarters");
@@ -715,7 +722,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  const int arow = wave_arow<BN, WN, HALF>(wave);
+  const int arow = wave_arow<BN, WN, LAY>(wave);
   // The lane's 32 bytes of an LDS row: the MFMA takes k values 16h..16h+15
   // from bytes 0-15 and 32+16h..32+16h+15 from bytes 16-31 of lane half h
   // (16-byte chunks h and h + 2 of the 64-k row), and lane half h's scale
@@ -726,7 +733,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     return __builtin_shufflevector(p, q, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto wfrag = [&](const char* L, int i) {
-    return frag(L + M::A_BYTES, wave_wrow<BN, WN, HALF, EPI>(wave, i) + (lane & 31));
+    return frag(L + M::A_BYTES, wave_wrow<BN, WN, LAY, EPI>(wave, i) + (lane & 31));
   };
   auto xfrag = [&](const char* L, int j) { return frag(L, arow + j * 32 + (lane & 31)); };
   u32x4 SC[C::TA];  // this chunk's 16 scale bytes of each activation block's row
@@ -818,7 +825,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     });
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
-  finish_tile<BN, WN, EPI, HALF, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot);
+  finish_tile<BN, WN, EPI, LAY, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot);
 }
 #endif
 
@@ -826,8 +833,8 @@ template <int BN, int WN, int EPI>
 __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, int n_tiles, int kt_plan,
                                                                     int n_cu) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(OutTile<BN, EPI>::BYTES <= STAGES * BigMem<BN, WN, false, GD_BF16>::STAGE_BYTES, "LDS");
-  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, false, GD_BF16>::STAGE_BYTES +
+  static_assert(OutTile<BN, EPI>::BYTES <= STAGES * BigMem<BN, WN, 0, GD_BF16>::STAGE_BYTES, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, 0, GD_BF16>::STAGE_BYTES +
                                                      2 * SC_BYTES];
   Work wk;
   if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
@@ -836,10 +843,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
   if (!tile_info(a, wk.mt, BM, ti, sg)) return;
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
-  if (ti.nrows <= BM / 2)
-    big_tile_fp8<BN, WN, EPI, true>(a, ti, sg, wk, ncol0, lds);
-  else
-    big_tile_fp8<BN, WN, EPI, false>(a, ti, sg, wk, ncol0, lds);
+  switch (tile_layout(ti.nrows)) {
+    case 2: big_tile_fp8<BN, WN, EPI, 2>(a, ti, sg, wk, ncol0, lds); break;
+    case 1: big_tile_fp8<BN, WN, EPI, 1>(a, ti, sg, wk, ncol0, lds); break;
+    default: big_tile_fp8<BN, WN, EPI, 0>(a, ti, sg, wk, ncol0, lds);
+  }
 #endif
 }
 
@@ -851,10 +859,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
 // to those four columns.  SwiGLU units pair block i (u) with block i + TW/2
 // (v).  Spreading units over many blocks keeps the reads in flight.
 constexpr int kFixupChunks = 16;  // blocks per split tile
-template <int BN, int WN, int EPI, bool HALF, int WDT>
+template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
                                             int first_slot, int s) {
-  using C = BigCfg<BN, WN, HALF>;
+  using C = BigCfg<BN, WN, LAY>;
   constexpr int NT = 128 * WN;  // threads of the GEMM block
   constexpr int TWO = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
   constexpr int UNITS = NT * TWO * C::TA * 4;
@@ -875,9 +883,9 @@ __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& t
     const int t = u % NT, r = u / NT;
     const int g = r & 3, j = (r >> 2) % C::TA, i = (r >> 2) / C::TA;
     const int wave = t >> 6, lane = t & 63;
-    const int row = wave_arow<BN, WN, HALF>(wave) + j * 32 + (lane & 31);
+    const int row = wave_arow<BN, WN, LAY>(wave) + j * 32 + (lane & 31);
     if (row >= ti.nrows) continue;
-    const int n = ncol0 + wave_col<BN, WN, HALF, EPI>(wave) + i * 32 + g * 8 + (lane >> 5) * 4;
+    const int n = ncol0 + wave_col<BN, WN, LAY, EPI>(wave) + i * 32 + g * 8 + (lane >> 5) * 4;
     float o[4];
     const float4 x = sum(((i * C::TA + j) * 4 + g) * NT + t);
     if (EPI == EPI_SWIGLU) {
@@ -923,10 +931,11 @@ __global__ __launch_bounds__(256) void gemm_big_fixup_kernel(GemmArgs a, int n_t
     if (!tile_info(a, mt, BM, ti, sg)) return;
     const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
     if (ncol0 >= sg.N) return;
-    if (ti.nrows <= BM / 2)
-      fixup_units<BN, WN, EPI, true, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
-    else
-      fixup_units<BN, WN, EPI, false, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+    switch (tile_layout(ti.nrows)) {
+      case 2: fixup_units<BN, WN, EPI, 2, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
+      case 1: fixup_units<BN, WN, EPI, 1, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
+      default: fixup_units<BN, WN, EPI, 0, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+    }
   }
 }
 
