@@ -9,7 +9,8 @@
 // Figure 2).  No atomics: a token gathers its own k rows through inv_pos, so
 // the result is deterministic.  The sum runs j = 0..k-1, then the shared row;
 // an assignment dropped for capacity (inv_pos = -1) contributes nothing.
-// One block per token row; 16-byte loads and stores, HBM-bound.
+// One block per token row; 16-byte loads and stores, HBM-bound; a thread
+// has its k row loads in flight together.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -17,6 +18,10 @@ namespace {
 
 constexpr int kMaxK = 16;
 
+// KM >= k bounds the token's rows at compile time, so all k row loads (and
+// the shared row's) are issued before the first is consumed: one 16-byte
+// load per row in flight per thread rather than one in all.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
   __shared__ int s_row[kMaxK];
   __shared__ float s_g[kMaxK];
@@ -26,28 +31,37 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
     s_g[threadIdx.x] = a.topk_w[(size_t)t * a.k + threadIdx.x];
   }
   __syncthreads();
+  int row[KM];
+  float g[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    row[j] = j < a.k ? s_row[j] : -1;  // -1: no row (past k, or dropped for capacity)
+    g[j] = j < a.k ? s_g[j] : 0.f;
+  }
   const int nvec = a.d / 8;  // 8 bf16 per 16 bytes
-  const u32x4* y = (const u32x4*)a.y_perm;
-  const u32x4* ys = (const u32x4*)a.shared_y;
-  u32x4* out = (u32x4*)a.out;
+  const u32x4* __restrict__ y = (const u32x4*)a.y_perm;
+  const u32x4* __restrict__ ys = (const u32x4*)a.shared_y;
+  u32x4* __restrict__ out = (u32x4*)a.out;
   for (int v = threadIdx.x; v < nvec; v += 256) {
+    u32x4 r[KM], rs = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < KM; ++j) r[j] = row[j] >= 0 ? y[(size_t)row[j] * nvec + v] : rs;
+    if (ys) rs = ys[(size_t)t * nvec + v];
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < a.k; ++j) {
-      if (s_row[j] < 0) continue;  // dropped for capacity: no contribution
-      const u32x4 r = y[(size_t)s_row[j] * nvec + v];
-      const float g = s_g[j];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (row[j] < 0) continue;  // no contribution
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += g * bf16_to_f32(r[q] & 0xffffu);
-        acc[2 * q + 1] += g * bf16_to_f32(r[q] >> 16);
+        acc[2 * q] += g[j] * bf16_to_f32(r[j][q] & 0xffffu);
+        acc[2 * q + 1] += g[j] * bf16_to_f32(r[j][q] >> 16);
       }
     }
     if (ys) {
-      const u32x4 r = ys[(size_t)t * nvec + v];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_to_f32(r[q] & 0xffffu);
-        acc[2 * q + 1] += bf16_to_f32(r[q] >> 16);
+        acc[2 * q] += bf16_to_f32(rs[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(rs[q] >> 16);
       }
     }
     u32x4 o;
@@ -92,10 +106,16 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.act == GD_BF16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(a.T), dim3(256), 0, s, a);
-  else
+  if (a.act != GD_BF16)
     hipLaunchKernelGGL(combine_f32_kernel, dim3(a.T), dim3(256), 0, s, a);
+  else if (a.k <= 2)
+    hipLaunchKernelGGL(combine_bf16_kernel<2>, dim3(a.T), dim3(256), 0, s, a);
+  else if (a.k <= 4)
+    hipLaunchKernelGGL(combine_bf16_kernel<4>, dim3(a.T), dim3(256), 0, s, a);
+  else if (a.k <= 8)
+    hipLaunchKernelGGL(combine_bf16_kernel<8>, dim3(a.T), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_bf16_kernel<kMaxK>, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
