@@ -159,6 +159,9 @@ int route_splits(const moe_desc* d) {
   const int64_t kmax = d->d / 64;
   int64_t want = (1024 + tiles - 1) / tiles;
   want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
+  // at most 16 ranges: more only multiplies the partial sums the selection
+  // reads (DeepSeek-V3-shaped decode: 56 ranges 34.6 us, 16 ranges 26.6 us)
+  want = std::min<int64_t>(want, 16);
   int s = 1;
   for (int64_t c = 1; c <= std::min(want, kmax); ++c)
     if (kmax % c == 0) s = int(c);
