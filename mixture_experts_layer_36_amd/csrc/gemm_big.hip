@@ -46,6 +46,8 @@
 //     uniform (readfirstlane): otherwise the compiler cannot prove a base
 //     computed on the vector unit uniform and wraps each load through it in a
 //     loop over distinct lane values.
+#include <atomic>
+
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -939,17 +941,19 @@ __global__ __launch_bounds__(256) void gemm_big_fixup_kernel(GemmArgs a, int n_t
   }
 }
 
-// Compute units of the current device (the split plan fills one wave of them).
+// Compute units of the current device (the split plan fills one wave of them),
+// cached per device.  Calls from several threads may race to fill an entry;
+// each stores the same value, and the entries are atomic, so that is benign.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 template <int BN, int EPI, int WDT, bool FP8ACT = false, int WN = MOE_BIG_WN>
