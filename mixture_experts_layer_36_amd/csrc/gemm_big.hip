@@ -870,15 +870,24 @@ __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& t
   constexpr int UNITS = NT * TWO * C::TA * 4;
   constexpr size_t SLOT4 = kPartialSlotBytes / 16;
   const float4* P = (const float4*)a.partial + (size_t)first_slot * SLOT4;
+  // pieces in order; their loads four at a time, so several are in flight
   auto sum = [&](int e) {
     float4 x = P[e];
-    for (int p = 1; p < s; ++p) {
-      const float4 y = P[(size_t)p * SLOT4 + e];
+    auto add = [&](const float4& y) {
       x.x += y.x;
       x.y += y.y;
       x.z += y.z;
       x.w += y.w;
+    };
+    int p = 1;
+    for (; p + 4 <= s; p += 4) {
+      float4 y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = P[(size_t)(p + q) * SLOT4 + e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add(y[q]);
     }
+    for (; p < s; ++p) add(P[(size_t)p * SLOT4 + e]);
     return x;
   };
   for (int u = blockIdx.y * blockDim.x + threadIdx.x; u < UNITS; u += gridDim.y * blockDim.x) {
