@@ -7,7 +7,8 @@
 // Figure 3); counts[e] are the per-expert token counts that page's checklist
 // asks to export (section "Trade-offs, Gotchas, and What Goes Wrong").
 //
-// Three index kernels, all deterministic (no result depends on atomic order):
+// Three index kernels, all deterministic (no result depends on atomic order)
+// (up to 4096 assignments, one block does all three: dispatch_small_kernel):
 //   1. histogram: one wavefront per chunk of a.chunk assignments,
 //      LDS-privatised bins -> chunk_cnt[chunk][e];
 //   2. scan (one block): per-expert running sums over chunks give each
@@ -127,6 +128,86 @@ __global__ __launch_bounds__(64) void scatter_kernel(DispatchArgs a, int32_t* ra
     } else if (valid) {
       if (rel < a.cap) {  // a free slot of its expert
         const int row = a.offsets[e] + rel;
+        a.inv_pos[i] = row;
+        a.perm_token[row] = i / a.k;
+      } else {
+        a.inv_pos[i] = -1;  // the expert is full: dropped
+      }
+    }
+  }
+}
+
+// Small problems (at most kSmallDispatch assignments): histogram, scan and
+// scatter in one block of 8 wavefronts, the arithmetic of the three kernels
+// above with one chunk per wavefront.  The expert ids are staged in LDS
+// once; each wave bins its chunk (LDS atomics: integer, order-free); thread e
+// turns the 8 chunk counts of expert e into chunk bases and the scan over
+// experts gives the offsets; then every wave walks its own chunk in order, 64
+// at a time, ranking each lane among earlier lanes with the same expert by
+// ballots.  One launch instead of three, which is most of the cost at decode
+// sizes.
+constexpr int kSmallDispatch = 4096, kSmallWaves = kMaxE / 64;
+__global__ __launch_bounds__(kMaxE) void dispatch_small_kernel(DispatchArgs a) {
+  __shared__ int keys[kSmallDispatch];
+  __shared__ int cnt[kSmallWaves][kMaxE];  // per chunk: counts, then its next row per expert
+  __shared__ int tot[kMaxE];
+  __shared__ int base[kMaxE];              // first row of each expert
+  const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
+  for (int i = e; i < a.n_assign; i += kMaxE) keys[i] = a.topk_idx[i];
+  for (int w = 0; w < kSmallWaves; ++w) cnt[w][e] = 0;
+  __syncthreads();
+  // chunk w: assignments [w * C, min((w + 1) * C, n)), C a multiple of 64
+  const int C = ((a.n_assign + kSmallWaves * 64 - 1) / (kSmallWaves * 64)) * 64;
+  const int lo = min(wave * C, a.n_assign), hi = min(lo + C, a.n_assign);
+  for (int i = lo + lane; i < hi; i += 64) {
+    const int x = keys[i];
+    if (x >= 0) atomicAdd(&cnt[wave][x], 1);
+  }
+  __syncthreads();
+  int run = 0;
+  if (e < a.E) {
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int v = cnt[w][e];
+      cnt[w][e] = run;  // rows of e before chunk w (relative)
+      run += v;
+    }
+    a.counts[e] = run;  // the demand; the rows kept are min(run, cap)
+  }
+  const int kept = (e < a.E) ? min(run, a.cap) : 0;
+  tot[e] = kept;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    const int v = (e >= off) ? tot[e - off] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  base[e] = tot[e] - kept;
+  if (e < a.E) a.offsets[e] = tot[e] - kept;
+  if (e == a.E - 1) a.offsets[a.E] = tot[e];
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int* next_row = cnt[wave];
+  for (int s0 = lo; s0 < hi; s0 += 64) {
+    const int i = s0 + lane;
+    const bool valid = i < hi;
+    const int x = valid ? keys[i] : kMaxE;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) {
+      const bool bit = (x >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
+    const int rel = valid ? next_row[x] + rank : 0;  // earlier assignments to x
+    __builtin_amdgcn_wave_barrier();  // every lane has read next_row before any update
+    const bool last = (same >> lane) == 1ull;  // highest lane of its group
+    if (valid && last) next_row[x] = rel + 1;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      if (rel < a.cap) {  // a free slot of its expert
+        const int row = base[x] + rel;
         a.inv_pos[i] = row;
         a.perm_token[row] = i / a.k;
       } else {
@@ -285,6 +366,10 @@ hipError_t launch_dispatch_index(const DispatchArgs& a_in, hipStream_t s) {
   a.chunk = dispatch_chunk(a.n_assign);
   if (a.n_assign == 0) {  // a fill kernel, not a memset node (graph-safe)
     hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kMaxE + 64), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.n_assign <= kSmallDispatch) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kMaxE), 0, s, a);
     return hipGetLastError();
   }
   const int n_chunks = (a.n_assign + a.chunk - 1) / a.chunk;
