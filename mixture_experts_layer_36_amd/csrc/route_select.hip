@@ -204,8 +204,9 @@ __global__ __launch_bounds__(kWaves * 64) void route_select_kernel(RouteSelectAr
 // (lane-strided), loading each chunk for the E router rows and the TB tokens
 // and accumulating the E x TB dot products with the packed bf16 dot
 // instruction (fp32 accumulate).  The 4 x 64 partial sums of each product go
-// through LDS and wavefront 0's lane l = tb * EM + e adds them in a fixed
-// order (identical router rows give identical logits), so token tb's logits
+// through LDS; each wavefront adds a quarter of them and wavefront 0's lane
+// l = tb * EM + e adds the four quarters, a fixed order for every product
+// (identical router rows give identical logits), so token tb's logits
 // sit in lanes [tb * EM, tb * EM + EM).  Scores, top-k and gates follow in
 // those lane groups with shuffles that stay inside the group.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -240,29 +241,42 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterFusedArgs a) {
   const u32x4* wr = (const u32x4*)a.w_router;
   const u32x4* x = (const u32x4*)a.x;
   for (int c = c_lo + lane; c < c_hi; c += 64) {
-    u32x4 xv[TB];
+    // every load unconditional (rows past E or T clamped, their products
+    // unused), so a lane's 2 * TB loads are in flight together
+    u32x4 xv[TB], wv[EM];
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       const int t = min(t0 + j, a.T - 1);
       xv[j] = x[(size_t)t * nch + c];
     }
 #pragma unroll
-    for (int e = 0; e < EM; ++e) {
-      if (e >= a.E) break;
-      const u32x4 wv = wr[(size_t)e * nch + c];
+    for (int e = 0; e < EM; ++e) wv[e] = wr[(size_t)min(e, a.E - 1) * nch + c];
 #pragma unroll
-      for (int j = 0; j < TB; ++j) acc[e][j] = dot8(wv, xv[j], acc[e][j]);
-    }
+    for (int e = 0; e < EM; ++e)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) acc[e][j] = dot8(wv[e], xv[j], acc[e][j]);
   }
 #pragma unroll
   for (int e = 0; e < EM; ++e)
 #pragma unroll
     for (int j = 0; j < TB; ++j) s_part[wave][lane][j * EM + e] = acc[e][j];
   __syncthreads();
+  // entry i = threadIdx.x % 64 summed by all four waves: wave q adds lanes
+  // [16q, 16q + 16) of every wave's range, then wave 0 adds the four sums
+  // (a fixed order for every entry)
+  {
+    const int q = wave, i = lane;
+    float p = 0.f;
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int l = 0; l < 16; ++l) p += s_part[w][16 * q + l][i];
+    __syncthreads();  // every read of s_part is done before the slots are reused
+    s_part[0][q][i] = p;
+  }
+  __syncthreads();
   if (wave != 0) return;
-  float z = 0.f;  // entry `lane` summed over the waves' ranges, then lanes
-  for (int w = 0; w < 4; ++w)
-    for (int l = 0; l < 64; ++l) z += s_part[w][l][lane];
+  float z = 0.f;  // entry `lane` summed over the four quarters
+  for (int q = 0; q < 4; ++q) z += s_part[0][q][lane];
   const int e = lane % EM, tb = lane / EM, t = t0 + tb;
   const bool real = e < a.E;
   if (real && a.bias) z += a.bias[e];
