@@ -99,6 +99,10 @@ CASES = {
     "dsv3_big_shared": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384),
     "dsv3_big_shared_f8d": DSV3_PREFILL_SKEW.scaled(T=1100, d=384, f=256, E=16, k=4, f_shared=384,
                                                     dispatch_fp8=True),
+    # router tiles ending in a quarter-height tail (1050 = 4 * 256 + 26 rows;
+    # 1040: 16 rows, with the group limit and a shared expert)
+    "router_big_e256_qtail": QWEN_FP8_SKEW.scaled(T=1050, d=512, f=128, E=256, k=4),
+    "router_big_dsv3_qtail": DSV3_PREFILL_SKEW.scaled(T=1040, d=512, f=128, E=256, f_shared=128),
 }
 
 _CACHE = {}
