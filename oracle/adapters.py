@@ -49,18 +49,19 @@ def decoded_shared(L):
     return decode(sh.w1, a), decode(sh.w3, a), decode(sh.w2, a)
 
 
-def margin_acceptor(margin: float = 1e-3, rank_margin: float = 2e-5):
-    """Row-acceptance callback for synth.LayerInputs(accept=...).  A workload
-    that reroutes capacity overflow also needs the order of its reroute
-    candidates (ranks k .. 2k) decided the same way by a float32 router:
-    adjacent scores there are kept ``rank_margin`` apart, twenty times the
-    float32 router's score error (~1e-6)."""
+def margin_acceptor(margin: float = 1e-3, order_margin: float = 2e-5):
+    """Row-acceptance callback for synth.LayerInputs(accept=...).  The chosen
+    set is kept ``margin`` from the next expert (and the kept groups from the
+    next group); the order of the k outputs, and for a workload that reroutes
+    capacity overflow the order of its reroute candidates (ranks k .. 2k), is
+    kept by ``order_margin`` between adjacent scores, twenty times the float32
+    router's score error (~1e-6)."""
 
     def accept(L, rows, x_rows):
         wr, bias = decoded_router(L)
         w = L.w
         rr = getattr(w, "overflow", "drop") == "reroute" and getattr(w, "capacity_factor", 0) > 0
         return selection_margin_ok(decode(x_rows, w.act), wr, bias, workload_spec(w), margin,
-                                   ranks=2 * w.k if rr else 0, rank_margin=rank_margin)
+                                   ranks=2 * w.k if rr else 0, order_margin=order_margin)
 
     return accept

@@ -273,24 +273,25 @@ def route(x, w_router, bias, spec: RouteSpec):
 
 
 def selection_margin_ok(x, w_router, bias, spec: RouteSpec, margin: float = 1e-3,
-                        ranks: int = 0, rank_margin: Optional[float] = None) -> np.ndarray:
-    """Rows whose routing decisions are separated by at least ``margin``:
-    the k-th vs (k+1)-th eligible expert score and, with a group limit, the
-    topk_group-th vs next group score.  With ranks > k (reroute candidates),
-    also every adjacent pair of eligible scores from rank k to rank ranks,
-    by ``rank_margin`` (default ``margin``).  Used to redraw synthetic token
-    rows so that a float32 router must reach the same decisions as this one."""
+                        ranks: int = 0, order_margin: float = 2e-5) -> np.ndarray:
+    """Rows whose routing decisions are separated, so that a float32 router
+    must reach the same decisions as this one (used to redraw synthetic token
+    rows).  Over the eligible scores sorted descending, s_0 >= s_1 >= ...:
+      * the k-th vs (k+1)-th score (in or out) by at least ``margin``;
+      * with a group limit, the topk_group-th vs next group score by ``margin``;
+      * every other adjacent pair (s_i, s_i+1) for i < max(k, ranks) by at
+        least ``order_margin``: i < k-1 fixes the order of the k outputs,
+        k <= i < ranks the order of reroute candidates (ranks = 2k).
+    A pair whose lower score is not eligible (-inf) always passes."""
     s = expert_scores(router_logits(x, w_router, bias), spec.score)
     T, E = s.shape
     ok = np.ones(T, dtype=bool)
     masked = np.where(eligible(s, spec), s, -np.inf)
     srt = -np.sort(-masked, axis=1)
-    if spec.k < E and np.isfinite(srt[:, spec.k]).all():
-        ok &= (srt[:, spec.k - 1] - srt[:, spec.k]) >= margin
-    rm = margin if rank_margin is None else rank_margin
-    for i in range(spec.k, min(ranks, E - 1)):
+    for i in range(min(max(spec.k, ranks), E - 1)):
+        need = margin if i == spec.k - 1 else order_margin
         hi, lo = srt[:, i], srt[:, i + 1]
-        ok &= ~np.isfinite(lo) | ((hi - lo) >= rm)
+        ok &= ~np.isfinite(lo) | ((hi - lo) >= need)
     if spec.n_group and spec.topk_group < spec.n_group:
         g = -np.sort(-group_scores(s, spec.n_group), axis=1)
         ok &= (g[:, spec.topk_group - 1] - g[:, spec.topk_group]) >= margin

@@ -15,8 +15,6 @@ REL_TOL = {"bf16": 2e-2, "e4m3": 6e-2}
 ABS_TOL_F32 = 1e-4
 # Gates are fp32 in every dtype; logits differ from float64 by ~1e-6.
 GATE_TOL = 2e-5
-# Adjacent chosen scores closer than this may come out in either order.
-ORDER_TIE = 2e-5
 
 
 def from_torch(t: torch.Tensor, dtype: str) -> np.ndarray:
@@ -67,41 +65,41 @@ def assert_values(got: np.ndarray, ref: np.ndarray, w, what: str) -> float:
     return err
 
 
-def assert_routing(idx: np.ndarray, gw: np.ndarray, ref: O.LayerResult, scores: np.ndarray):
-    """Selected expert sets bit-exact; order exact except between adjacent
-    chosen experts whose oracle scores are within ORDER_TIE; gates within
-    GATE_TOL (compared per expert id)."""
+def assert_rows(got: np.ndarray, ref: np.ndarray, w, what: str) -> float:
+    """assert_values row by row: each token's output against the largest
+    magnitude of its own oracle row (so a wrong low-magnitude row cannot hide
+    behind the tensor's maximum).  Returns the largest row error."""
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    if w.act == "f32":
+        return assert_values(got, ref, w, what)
+    tol = REL_TOL[w.wdt if w.wdt == "e4m3" else "bf16"]
+    scale = np.max(np.abs(ref), axis=1)
+    diff = np.max(np.abs(got - ref), axis=1)
+    err = np.where(scale > 0, diff / np.where(scale > 0, scale, 1.0), diff)
+    t = int(np.argmax(err))
+    assert err[t] <= tol, f"{what}: row {t} rel err {err[t]:.3g} > {tol}"
+    return float(err[t])
+
+
+def assert_routing(idx: np.ndarray, gw: np.ndarray, ref: O.LayerResult):
+    """Routing indices bit-exact, position by position (the inputs keep every
+    adjacent pair of chosen scores apart, so the order is decided); gates
+    within GATE_TOL at each position."""
     T, k = ref.topk_idx.shape
     assert idx.shape == (T, k)
-    for t in range(T):
-        r, g = ref.topk_idx[t], idx[t]
-        assert sorted(r) == sorted(g), f"token {t}: experts {g} vs oracle {r}"
-        if not np.array_equal(r, g):
-            s = scores[t, r.astype(np.int64)]
-            for j in range(k):
-                if g[j] != r[j]:
-                    # the swapped entries must be oracle near-ties
-                    jj = int(np.nonzero(r == g[j])[0][0])
-                    lo, hi = min(j, jj), max(j, jj)
-                    assert np.all(np.abs(np.diff(s[lo:hi + 1])) < ORDER_TIE), \
-                        f"token {t}: order {g} vs {r} (scores {s})"
-        ref_by_e = dict(zip(r.tolist(), ref.topk_w[t].tolist()))
-        for j in range(k):
-            assert abs(gw[t, j] - ref_by_e[int(g[j])]) <= GATE_TOL, \
-                f"token {t}: gate {gw[t, j]} vs {ref_by_e[int(g[j])]}"
+    bad = np.nonzero((idx != ref.topk_idx).any(axis=1))[0]
+    assert bad.size == 0, [(int(t), idx[t].tolist(), ref.topk_idx[t].tolist()) for t in bad[:5]]
+    err = np.abs(gw.astype(np.float64) - ref.topk_w)
+    assert err.max(initial=0.0) <= GATE_TOL, f"gate err {err.max():.3g} at token {np.argmax(err) // k}"
 
 
 def assert_dispatch(idx, counts, offsets, perm_token, inv_pos, ref: O.LayerResult):
-    """Bit-exact dispatch.  Given the same expert sets, counts, offsets and
-    perm_token are unique; inv_pos is compared per (token, expert) pair so a
-    tolerated order swap within a token's k experts maps consistently."""
+    """Bit-exact dispatch: counts, offsets, perm_token and inv_pos (the
+    routing indices are already exact)."""
     assert np.array_equal(counts, ref.counts), "counts"
     assert np.array_equal(offsets, ref.offsets), "offsets"
     n = len(ref.perm_token)  # rows kept (all T*k when dropless)
     assert np.array_equal(perm_token[:n], ref.perm_token), "perm_token"
-    T, k = ref.topk_idx.shape
-    got = inv_pos.reshape(T, k)
-    want = ref.inv_pos.reshape(T, k)
-    og = np.argsort(idx, axis=1, kind="stable")
-    orf = np.argsort(ref.topk_idx, axis=1, kind="stable")
-    assert np.array_equal(np.take_along_axis(got, og, 1), np.take_along_axis(want, orf, 1)), "inv_pos"
+    assert np.array_equal(inv_pos, ref.inv_pos), "inv_pos"

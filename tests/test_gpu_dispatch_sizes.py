@@ -1,8 +1,9 @@
 """Dispatch around its size switch.
 
 Up to 4096 assignments the index work (histogram, scan, stable scatter) runs
-in one single-block kernel; above that, as three kernels over chunks.  Both
-must give the oracle's layout exactly.  Expert ids are drawn per token
+in one single-block kernel; above that, as three kernels over chunks of 256
+assignments, of 512 above 16384 and of 1024 above 32768 (up to 128 chunks at
+131072).  All must give the oracle's layout exactly.  Expert ids are drawn per token
 without replacement from a skewed distribution (Gumbel top-k), so some
 experts overflow a capacity; the cases sit on both sides of the switch and
 at the small edges, dropless and with a capacity.  The gathered rows are
@@ -21,7 +22,9 @@ from synth.workloads import MIXTRAL_PREFILL
 pytestmark = pytest.mark.gpu
 
 E, D = 64, 256
-SIZES = [(1, 1), (32, 2), (4095, 1), (512, 8), (4097, 1), (1024, 8), (700, 6)]  # (T, k): T*k assignments
+# (T, k): T*k assignments
+SIZES = [(1, 1), (32, 2), (4095, 1), (512, 8), (4097, 1), (1024, 8), (700, 6), (2500, 8), (5000, 8),
+         (9001, 8), (16384, 8)]
 
 
 def _topk(T, k, seed):

@@ -374,19 +374,57 @@ def check_locality():
     assert np.array_equal(idx2, idx[S]) and np.array_equal(w2, w[S])
 
 
+def _margin_row(E, p, gap, rng):
+    """Router inputs for one token whose sorted sigmoid scores are 0.05 apart
+    except the pair at ranks (p, p+1), which is ``gap`` apart; the scores go
+    to a random permutation of the expert ids."""
+    gaps = np.full(E - 1, 0.05)
+    gaps[p] = gap
+    srt = 0.9 - np.concatenate([[0.0], np.cumsum(gaps)])
+    s = np.empty(E)
+    s[rng.permutation(E)] = srt
+    b = np.log(s / (1.0 - s))  # logits whose sigmoid is s
+    return np.zeros((1, E)), np.zeros((E, E)), b
+
+
 def check_margin_rule():
-    # constructed logits: top-2 of 4 with a known gap between 2nd and 3rd score
-    spec = O.RouteSpec(k=2, score="sigmoid")
-    x = np.eye(4)
-    for gap, want in ((0.0, False), (2e-3, True)):
-        b = np.array([0.5, 0.2, 0.2 - 4 * gap, -1.0])  # sigmoid slope ~0.245 near 0.2
-        ok = O.selection_margin_ok(np.zeros((1, 4)), np.zeros((4, 4)), b, spec)
-        assert ok[0] == want
+    # every adjacent pair of sorted scores: below the pair's margin the row is
+    # rejected, above it accepted; pairs past max(k, ranks) are not checked.
+    # k-th vs (k+1)-th by `margin`, every other checked pair by `order_margin`.
+    rng = np.random.default_rng(23)
+    E, k, margin, om = 10, 3, 1e-3, 2e-5
+    spec = O.RouteSpec(k=k, score="sigmoid")
+    for ranks in (0, 2 * k):
+        top = max(k, ranks)
+        for p in range(E - 1):
+            need = margin if p == k - 1 else om
+            lo = O.selection_margin_ok(*_margin_row(E, p, 0.9 * need, rng), spec, margin, ranks=ranks,
+                                       order_margin=om)[0]
+            hi = O.selection_margin_ok(*_margin_row(E, p, 1.1 * need, rng), spec, margin, ranks=ranks,
+                                       order_margin=om)[0]
+            tie = O.selection_margin_ok(*_margin_row(E, p, 0.0, rng), spec, margin, ranks=ranks,
+                                        order_margin=om)[0]
+            assert hi, (ranks, p)
+            assert lo == (p >= top) and tie == (p >= top), (ranks, p, lo, tie)
+    # k = E: no k+1-th expert, the chosen order is still checked
+    spec = O.RouteSpec(k=4, score="sigmoid")
+    assert O.selection_margin_ok(*_margin_row(4, 2, 1.1 * om, rng), spec)[0]
+    assert not O.selection_margin_ok(*_margin_row(4, 2, 0.9 * om, rng), spec)[0]
     # group rule: 4 groups of 2, keep 2; groups 1 and 2 tie exactly
     spec = O.RouteSpec(k=2, score="sigmoid", n_group=4, topk_group=2)
-    b = np.array([3.0, 3.0, 1.0, 0.0, 1.0, 0.0, -2.0, -2.0])
+    b = np.array([3.0, 3.1, 1.0, 0.0, 1.0, 0.0, -2.0, -2.5])
     assert not O.selection_margin_ok(np.zeros((1, 8)), np.zeros((8, 8)), b, spec)[0]
-    del x
+    b[2] = 1.2  # group 1 now ahead of group 2 by more than the margin
+    assert O.selection_margin_ok(np.zeros((1, 8)), np.zeros((8, 8)), b, spec)[0]
+    # with a group limit the ranks are those of the eligible experts only:
+    # expert 4 (group 2, not kept) scores 1e-5 below the best expert, which
+    # does not matter; the same gap between the two chosen experts does
+    b = np.array([3.0, 3.1, 1.0, 0.0, 0.0, -9.0, -2.0, -2.5])
+    s1 = 1.0 / (1.0 + np.exp(-3.1))
+    b[4] = np.log((s1 - 1e-5) / (1.0 - (s1 - 1e-5)))
+    assert O.selection_margin_ok(np.zeros((1, 8)), np.zeros((8, 8)), b, spec)[0]
+    b[0], b[4] = b[4], 0.0
+    assert not O.selection_margin_ok(np.zeros((1, 8)), np.zeros((8, 8)), b, spec)[0]
 
 
 def check_capacity():
@@ -759,6 +797,45 @@ def _m_round_truncate(a):
     return np.ldexp(np.trunc(np.ldexp(a, 8 - e)), e - 8)
 
 
+def _margin_variant(shift=0, unmasked=False, big_at=-1):
+    """selection_margin_ok with one planted change: the checked pairs end
+    `shift` ranks late (or early), masked experts are ranked too, or the
+    k-th/(k+1)-th margin goes to the pair `big_at` ranks away."""
+
+    def bad(x, w_router, bias, spec, margin=1e-3, ranks=0, order_margin=2e-5):
+        s = M.expert_scores(M.router_logits(x, w_router, bias), spec.score)
+        T, E = s.shape
+        ok = np.ones(T, dtype=bool)
+        masked = s if unmasked else np.where(M.eligible(s, spec), s, -np.inf)
+        srt = -np.sort(-masked, axis=1)
+        for i in range(max(0, min(max(spec.k, ranks) + shift, E - 1))):
+            need = margin if i == spec.k - 1 + (big_at + 1) else order_margin
+            hi, lo = srt[:, i], srt[:, i + 1]
+            ok &= ~np.isfinite(lo) | ((hi - lo) >= need)
+        if spec.n_group and spec.topk_group < spec.n_group:
+            g = -np.sort(-M.group_scores(s, spec.n_group), axis=1)
+            ok &= (g[:, spec.topk_group - 1] - g[:, spec.topk_group]) >= margin
+        return ok
+
+    return bad
+
+
+def _m_margin_short(*a, **kw):
+    return _margin_variant(shift=-1)(*a, **kw)
+
+
+def _m_margin_long(*a, **kw):
+    return _margin_variant(shift=1)(*a, **kw)
+
+
+def _m_margin_unmasked(*a, **kw):
+    return _margin_variant(unmasked=True)(*a, **kw)
+
+
+def _m_margin_wrong_pair(*a, **kw):
+    return _margin_variant(big_at=0)(*a, **kw)
+
+
 MUTATIONS = [
     ("silu", _m_silu_dropped),
     ("expert_scores", _m_softmax_sign),
@@ -777,6 +854,10 @@ MUTATIONS = [
     ("reroute_candidates", _m_candidates_skip_one),
     ("dispatch_reroute", _m_reroute_ignores_pass1),
     ("dispatch_reroute", _m_reroute_keeps_gate),
+    ("selection_margin_ok", _m_margin_short),
+    ("selection_margin_ok", _m_margin_long),
+    ("selection_margin_ok", _m_margin_unmasked),
+    ("selection_margin_ok", _m_margin_wrong_pair),
 ]
 
 
