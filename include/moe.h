@@ -86,10 +86,11 @@ typedef struct {
   int32_t act;        /* moe_dtype of activations: MOE_F32 or MOE_BF16            */
   int32_t wdtype;     /* moe_dtype of routed weights: act, or MOE_FP8_E4M3 when
                          act is MOE_BF16 (per-output-channel fp32 scales)         */
-  int32_t capacity;   /* 0 = dropless; else slots per expert (>= 1): the page's
-                         capacity_factor * T * k / E, rounded up by the caller.
-                         Assignments claim slots in increasing a = t*k + j; one
-                         that finds its expert full is dropped (contributes 0) */
+  int32_t capacity;   /* 0 = dropless; else slots per expert (>= 1), e.g. from
+                         moe_capacity_slots (capacity_factor * T * k / E,
+                         rounded up).  Assignments claim slots in increasing
+                         a = t*k + j; one that finds its expert full is dropped
+                         (contributes 0)                                     */
   int32_t overflow;   /* with a capacity: MOE_OVERFLOW_DROP (0) drops an
                          assignment that finds its expert full;
                          MOE_OVERFLOW_REROUTE (1) first offers it the token's
@@ -163,6 +164,17 @@ const char* moe_status_str(moe_status s);
 
 /* Validates `desc` (host) without touching the GPU.  MOE_OK if supported. */
 moe_status moe_validate(const moe_desc* desc);
+
+/* Expert capacity in slots: a capacity factor times the average load T*k/E,
+ * rounded up to whole slots, the static per-expert buffer size of "Expert-
+ * Parallel MoE Inference" (section "Capacity factor and token dropping").
+ * The factor is the exact ratio factor_num / factor_den (1.25 is 5/4):
+ *   *slots (host) = ceil(factor_num * T * k / (factor_den * E)),
+ * computed exactly in integers; 0 (dropless, no limit) when factor_num <= 0.
+ * Host only, touches no GPU.  MOE_ERR_INVALID when slots is NULL,
+ * factor_den <= 0, T < 0, k < 1, E < 1 or the result exceeds INT32_MAX. */
+moe_status moe_capacity_slots(int64_t factor_num, int64_t factor_den, int32_t T, int32_t k, int32_t E,
+                              int32_t* slots);
 
 /* Workspace bytes needed by moe_route, moe_dispatch, moe_grouped_ffn or
  * moe_layer_forward for `desc`; written to *bytes (host). */
@@ -240,6 +252,15 @@ moe_status moe_dispatch_reroute(const moe_desc* desc, const int32_t* topk_idx, c
                                 int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, float* gates,
                                 void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* Row-major [mats][rows][cols] -> K-blocked [mats][cols/32][rows][32]
+ * (MOE_W_KBLOCKED with N = rows, K = cols), elem_bytes 1 (E4M3) or 2 (bf16).
+ * src and dst: device, 16-byte aligned, not overlapping; cols a multiple of
+ * 32; mats * rows * cols * elem_bytes at most 2^40.  One kernel on `stream`.
+ * MOE_ERR_INVALID for bad arguments.  A storage layout of the same values
+ * (see "Weight layout"), not a step of the method: no page defines it. */
+moe_status moe_pack_weights(const void* src, int64_t mats, int32_t rows, int32_t cols, int32_t elem_bytes,
+                            void* dst, void* stream);
+
 /* Grouped expert FFN over the expert-contiguous rows.  Expert e transforms
  * rows [offsets[e], offsets[e+1]) of x_perm (act dtype [T*k][d], or with
  * dispatch_fp8 the payload of T*k rows as moe_dispatch writes it):
@@ -252,15 +273,13 @@ moe_status moe_dispatch_reroute(const moe_desc* desc, const int32_t* topk_idx, c
  *   w1, w3   [E][f][d], w2 [E][d][f] in wdtype, laid out per w_layout
  *   s1, s3   [E][f], s2 [E][d] fp32 per-output-channel scales when wdtype is
  *            MOE_FP8_E4M3, else NULL
- *   h, y_perm outputs; ws: moe_workspace_size(MOE_STAGE_FFN) bytes. */
-/* Row-major [mats][rows][cols] -> K-blocked [mats][cols/32][rows][32]
- * (MOE_W_KBLOCKED with N = rows, K = cols), elem_bytes 1 (E4M3) or 2 (bf16).
- * src and dst: device, 16-byte aligned, not overlapping; cols a multiple of
- * 32; mats * rows * cols * elem_bytes at most 2^40.  One kernel on `stream`.
- * MOE_ERR_INVALID for bad arguments. */
-moe_status moe_pack_weights(const void* src, int64_t mats, int32_t rows, int32_t cols, int32_t elem_bytes,
-                            void* dst, void* stream);
-
+ *   h, y_perm outputs; ws: moe_workspace_size(MOE_STAGE_FFN) bytes.
+ * Each expert transforms only the rows routed to it; all experts' segments
+ * run as one grouped GEMM ("Tensor vs Expert vs Data Parallelism for MoE
+ * Serving", section "Deeper Analysis", Figure 2; the expert's FFN step of the
+ * per-token path in "Expert-Parallel MoE Inference", section "Deeper
+ * Analysis", Figure 2).  The SwiGLU form and the fp8 weights with per-channel
+ * scales are this layer's definition; the pages name neither. */
 moe_status moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32_t* offsets,
                            const void* w1, const void* w3, const void* w2,
                            const float* s1, const float* s3, const float* s2,
@@ -270,7 +289,14 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const void* x_perm, const int32
  *                       (+ shared_y[t][:]), fp32 accumulation in that order,
  * stored in the act dtype; terms with inv_pos = -1 (dropped) are skipped.
  * No atomics: each token reads its own k rows.
- *   shared_y [T][d] act dtype, nullable. */
+ *   shared_y [T][d] act dtype, nullable.
+ * The expert outputs come back to their tokens' original order and are
+ * summed weighted by the gates ("Expert-Parallel MoE Inference", section
+ * "Deeper Analysis", Figure 2, and the combine step of section "The all-to-
+ * all dispatch and combine, step by step", Figure 3; the weighted-sum combine
+ * of "Tensor vs Expert vs Data Parallelism", section "Deeper Analysis",
+ * Figure 2).  The always-on shared expert is added with coefficient 1
+ * (DeepSeek-V3's shared expert, same page, section "Context and Background"). */
 moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* inv_pos,
                        const float* topk_w, const void* shared_y, void* out, void* stream);
 
@@ -285,7 +311,12 @@ moe_status moe_combine(const moe_desc* desc, const void* y_perm, const int32_t* 
  *   trace: NULL, or MOE_TRACE_EVENTS hipEvent_t (host array of handles)
  *          recorded on `stream` before the router and after the router,
  *          dispatch (with the GEMM tile table), routed gate-up GEMM, routed
- *          down GEMM, shared expert and combine, for per-stage timing. */
+ *          down GEMM, shared expert and combine, for per-stage timing.
+ * The chain router -> top-k -> dispatch -> expert FFN -> combine -> original
+ * token order of "MoE Expert Parallelism in Practice" (section "Core
+ * Principles", item 1) and of the per-token path in "Expert-Parallel MoE
+ * Inference", section "Deeper Analysis", Figure 2, on one GPU: the
+ * expert-contiguous rows the dispatch exchange would ship stay local. */
 moe_status moe_layer_forward(const moe_desc* desc, const void* x, const void* w_router,
                              const float* bias, const void* w1, const void* w3, const void* w2,
                              const float* s1, const float* s3, const float* s2,

@@ -27,7 +27,7 @@ TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "
 # the exported symbols include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows", "moe_pack_weights",
-           "moe_route_candidates", "moe_dispatch_reroute")
+           "moe_route_candidates", "moe_dispatch_reroute", "moe_capacity_slots")
 
 _DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
 OVERFLOW_DROP, OVERFLOW_REROUTE = 0, 1
@@ -44,15 +44,15 @@ class MoeError(RuntimeError):
 
 
 def capacity_slots(capacity_factor, T: int, k: int, E: int) -> int:
-    """Slots per expert for moe_desc.capacity: capacity_factor * T * k / E
-    rounded up, computed exactly from the decimal factor (1.1 is 11/10); 0
-    (dropless) for factors <= 0."""
-    cf = Fraction(str(capacity_factor))
-    if cf <= 0:
-        return 0
-    num = cf.numerator * T * k
-    den = cf.denominator * E
-    return -(-num // den)
+    """Slots per expert for moe_desc.capacity, from moe_capacity_slots: the
+    factor goes to the library as the exact ratio of its decimal form (1.1 is
+    11/10); factors <= 0 give 0 (dropless)."""
+    cf = capacity_factor if isinstance(capacity_factor, Fraction) else Fraction(str(capacity_factor))
+    out = ctypes.c_int32()
+    st = _lib().moe_capacity_slots(cf.numerator, cf.denominator, T, k, E, ctypes.byref(out))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_capacity_slots")
+    return out.value
 
 
 class Desc(ctypes.Structure):
@@ -117,6 +117,8 @@ def _lib() -> ctypes.CDLL:
         lib.moe_status_str.restype = ctypes.c_char_p
         lib.moe_status_str.argtypes = [ctypes.c_int]
         lib.moe_validate.argtypes = [D]
+        lib.moe_capacity_slots.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.moe_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_route.argtypes = [D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         lib.moe_dispatch.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]

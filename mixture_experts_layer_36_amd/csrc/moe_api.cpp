@@ -521,6 +521,22 @@ const char* moe_status_str(moe_status s) {
 
 moe_status moe_validate(const moe_desc* desc) { return check_desc(desc); }
 
+moe_status moe_capacity_slots(int64_t factor_num, int64_t factor_den, int32_t T, int32_t k, int32_t E,
+                              int32_t* slots) {
+  if (slots == nullptr || factor_den <= 0 || T < 0 || k < 1 || E < 1) return MOE_ERR_INVALID;
+  if (factor_num <= 0) {
+    *slots = 0;
+    return MOE_OK;
+  }
+  // ceil(num * T * k / (den * E)), exact in 128 bits: num < 2^63, T, k < 2^31
+  const unsigned __int128 num = (unsigned __int128)uint64_t(factor_num) * uint32_t(T) * uint32_t(k);
+  const unsigned __int128 den = (unsigned __int128)uint64_t(factor_den) * uint32_t(E);
+  const unsigned __int128 q = (num + den - 1) / den;
+  if (q > (unsigned __int128)INT32_MAX) return MOE_ERR_INVALID;
+  *slots = int32_t(q);
+  return MOE_OK;
+}
+
 moe_status moe_pack_weights(const void* src, int64_t mats, int32_t rows, int32_t cols, int32_t elem_bytes,
                             void* dst, void* stream) {
   if (mats < 0 || rows < 0 || cols < 0 || cols % 32 != 0 || (elem_bytes != 1 && elem_bytes != 2))

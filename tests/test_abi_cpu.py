@@ -204,9 +204,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def test_capacity_slots_match_the_oracle():
-    """The binding's slot count (host logic of the product) against the
-    oracle's own rounding of capacity_factor * T * k / E."""
+    """moe_capacity_slots (the library's slot count, through the binding)
+    against the oracle's own rounding of capacity_factor * T * k / E."""
     import oracle as O
     for cf, T, k, E in ((1.0, 512, 8, 256), (1.25, 512, 8, 256), (1.1, 512, 8, 256), (0.1, 10, 1, 1),
-                        (1.3, 4096, 2, 8), (0, 100, 2, 4), (-2, 100, 2, 4), (2, 7, 3, 5)):
+                        (1.3, 4096, 2, 8), (0, 100, 2, 4), (-2, 100, 2, 4), (2, 7, 3, 5), (1.0, 0, 2, 8),
+                        (1.25, 16384, 8, 256), (0.333, 1000, 3, 7)):
         assert moe.capacity_slots(cf, T, k, E) == O.expert_capacity(cf, T, k, E), (cf, T, k, E)
+
+
+def test_capacity_slots_c_abi():
+    """The C entry point directly: exact integer rounding up, and the
+    documented MOE_ERR_INVALID cases."""
+    lib = _lib._lib()
+    out = ctypes.c_int32(-9)
+    assert lib.moe_capacity_slots(5, 4, 512, 8, 256, ctypes.byref(out)) == moe.MOE_OK and out.value == 20
+    assert lib.moe_capacity_slots(11, 10, 512, 8, 256, ctypes.byref(out)) == moe.MOE_OK and out.value == 18
+    assert lib.moe_capacity_slots(1, 1, 7, 1, 7, ctypes.byref(out)) == moe.MOE_OK and out.value == 1
+    assert lib.moe_capacity_slots(0, 1, 7, 1, 7, ctypes.byref(out)) == moe.MOE_OK and out.value == 0
+    assert lib.moe_capacity_slots(-3, 2, 7, 1, 7, ctypes.byref(out)) == moe.MOE_OK and out.value == 0
+    big = (1 << 62) + 1  # 128-bit intermediate: (2^62 + 1) * 3 / (2^62 * 3) -> 2
+    assert lib.moe_capacity_slots(big, 1 << 62, 3, 1, 3, ctypes.byref(out)) == moe.MOE_OK and out.value == 2
+    for args in ((1, 0, 8, 2, 4), (1, -1, 8, 2, 4), (1, 1, -1, 2, 4), (1, 1, 8, 0, 4), (1, 1, 8, 2, 0),
+                 (1 << 40, 1, 1 << 20, 16, 1)):  # the last exceeds INT32_MAX slots
+        assert lib.moe_capacity_slots(*args, ctypes.byref(out)) == moe.MOE_ERR_INVALID, args
+    assert lib.moe_capacity_slots(1, 1, 8, 2, 4, None) == moe.MOE_ERR_INVALID
