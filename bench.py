@@ -3,15 +3,24 @@
 
 One step = one moe_layer_forward (router, dispatch, grouped SwiGLU FFN, shared
 expert when present, combine) over one batch of seeded synthetic tokens, with
-inputs already resident in HBM.  Prints one JSON line:
+inputs already resident in HBM.  The default workload is the DeepSeek-V3-shaped
+prefill layer with skewed routing (T=16384, the largest single-GPU
+configuration); the same line carries a `decode` record for the
+DeepSeek-V3-shaped decode layer (T=256), which is bound by HBM bandwidth.
+Prints one JSON line:
 
   value       tokens/s = T * steps / wall time of the timed steps
-  roofline    the routed gate-up GEMM (+SwiGLU) kernel against the bf16 MFMA
-              peak, or, for decode-shaped layers, the whole layer's
-              algorithmic bytes against HBM bandwidth; its duration comes from
-              HIP events the library records around each stage inside the
-              timed steps, on the stream the kernels run on
-  cpu_baseline the float64 oracle on a bounded token sample, host cores
+  roofline    the gate-up GEMM (+SwiGLU) launch against the peak of the MFMA
+              type it runs (its flops include the shared expert's when the
+              shared expert runs as a segment of the same launch), or, for
+              decode-shaped layers, the whole layer's algorithmic bytes against
+              HBM bandwidth; durations come from HIP events the library
+              records around each stage inside the timed steps, on the stream
+              the kernels run on
+  ceilings    measured in this run: a register-only bf16 and fp8 MFMA loop and
+              a streaming read (calib/ceilings.hip)
+  cpu_baseline the float64 oracle's forward of a bounded token sample on the
+              host cores (the fp64 decode of the expert weights timed apart)
   stages_gbps achieved GB/s of the route, dispatch and combine stages
               (algorithmic bytes over the stage's event time)
   cold_cache  after the timed steps, as many more steps each preceded by a
@@ -19,10 +28,15 @@ inputs already resident in HBM.  Prints one JSON line:
               each timed by its own events: medians of the step and stages
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --calibrate-mfma | --calibrate-stream | --calibrate-copy
+    python bench.py --summarize-trace DIR --warmup W --steps K
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
+import glob
 import hashlib
 import json
 import os
@@ -39,8 +53,15 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-DEFAULT_WORKLOAD = "mixtral8x7b_prefill_bf16"
+CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_36_amd", "lib", "libmoe_calib.so")
+DEFAULT_WORKLOAD = "dsv3_prefill_skew_bf16"
+DECODE_WORKLOAD = "dsv3_decode_bf16"
 DECODE_WORKLOADS = {"dsv3_decode_bf16"}
+EVICT_BYTES = 512 << 20
+# oracle tokens timed per workload: about 10 s of float64 compute on a
+# 16-core host (the whole batch where it is small enough)
+CPU_SAMPLE = {"tiny_f32": 64, "mixtral8x7b_prefill_bf16": 4096, "dsv3_decode_bf16": 256,
+              "dsv3_prefill_skew_bf16": 4096, "qwen_moe_fp8_skew": 8192, "dsv3_ep8_shard_bf16": 2048}
 
 
 def parse():
@@ -52,6 +73,8 @@ def parse():
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=None, help="tokens for the oracle timing")
+    p.add_argument("--no-decode-leg", action="store_true",
+                   help=f"skip the {DECODE_WORKLOAD} record the default workload's line carries")
     p.add_argument("--capacity-factor", type=float, default=0.0,
                    help="expert capacity = factor * T * k / E slots (0: dropless); overflow is dropped")
     p.add_argument("--overflow", choices=("drop", "reroute"), default="drop",
@@ -63,11 +86,18 @@ def parse():
                    help="time replays of one HIP graph of the layer forward (captured once); the per-stage "
                         "times then come from a separate traced eager pass")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache repetitions")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the in-run MFMA / stream ceiling probes")
     p.add_argument("--w-layout", choices=("auto", "rowmajor", "kblocked"), default="auto",
                    help="routed expert weight layout; auto: kblocked for bf16 / fp8 weights (packed "
                         "once after upload, before any timing), rowmajor for fp32")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--calibrate-mfma", action="store_true", help="only run the bf16 and fp8 MFMA-loop probes")
+    p.add_argument("--calibrate-stream", action="store_true", help="only run the streaming-read probe")
+    p.add_argument("--summarize-trace", metavar="DIR", default=None,
+                   help="summarise a rocprofv3 --kernel-trace CSV under DIR (no GPU): per-kernel calls and "
+                        "average, and the steady-state average over the timed steps given by --warmup and "
+                        "--steps")
     return p.parse_args()
 
 
@@ -83,6 +113,8 @@ def kernel_source_hash() -> str:
         h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
+
+# ------------------------------------------------------------ algorithmic work
 
 def layer_bytes(w, counts) -> float:
     """Algorithmic HBM bytes of one layer forward: x, router weight and bias,
@@ -104,6 +136,12 @@ def fp8_gate_up(w) -> bool:
     rows = w.T * w.k
     return (w.dispatch_fp8 and w.wdt == "e4m3" and rows >= 1024 and rows // w.E >= 128
             and w.d % 64 == 0)
+
+
+def shared_fused(w) -> bool:
+    """Whether the shared expert runs as one more segment of the routed GEMM
+    launches (the library does so when its weights share the routed dtype)."""
+    return w.f_shared > 0 and w.wdt == w.act
 
 
 def gathers_blocked(w) -> bool:
@@ -136,14 +174,71 @@ def stage_bytes(w, has_bias: bool, kept: int) -> dict:
     return {"route": float(route), "dispatch": float(dispatch), "combine": float(combine)}
 
 
-# Ceilings measured on MI355X by separate probes (not in this run): a
-# register-only loop of 32x32x16 bf16 MFMAs on every SIMD, the same with the
-# block-scaled fp8 32x32x64 MFMA, and a streaming read of 8 GiB with 16-byte
-# loads.
-MFMA_LOOP_TFLOPS = 1785.0
-MFMA_LOOP_TFLOPS_FP8 = 4614.0
-STREAM_READ_GBS = 6300.0
-EVICT_BYTES = 512 << 20
+# ------------------------------------------------------------------ ceilings
+
+def _calib_lib():
+    if not os.path.exists(CALIB_LIB):
+        raise ImportError(f"{CALIB_LIB} is missing: build with `python -m mixture_experts_layer_36_amd.build`")
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.moe_calib_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_calib_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p]
+    return lib
+
+
+def _timed(launch, reps):
+    """Median ms of `reps` launches, each bracketed by events on the current
+    stream (the one the probe is launched on), after one untimed launch."""
+    import torch
+    launch()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def ceilings(which=("mfma", "stream")) -> dict:
+    """MFMA-loop and streaming-read rates measured now, on this GPU."""
+    import torch
+    lib = _calib_lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"compute_units": cus}
+    if "mfma" in which:
+        blocks = 2 * cus  # two blocks of four wavefronts per CU: two per SIMD
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        for name, fn, iters, flop in (("mfma_bf16_loop_tflops", lib.moe_calib_mfma_bf16, 20000, 32 * 32 * 16 * 2),
+                                      ("mfma_fp8_loop_tflops", lib.moe_calib_mfma_fp8, 20000, 32 * 32 * 64 * 2)):
+            def launch(fn=fn, iters=iters):
+                rc = fn(blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"calibration launch failed: hipError {rc}")
+            ms = _timed(launch, 5)
+            out[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
+        out["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts, 4 independent 32x32 accumulator chains each, "
+                             "register operands (calib/ceilings.hip)")
+    if "stream" in which:
+        nbytes = 4 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+        blocks = 4096
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        read = ctypes.c_longlong(0)
+
+        def launch():
+            rc = lib.moe_calib_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, blocks,
+                                           ctypes.c_void_p(sink.data_ptr()), ctypes.byref(read), stream)
+            if rc != 0:
+                raise RuntimeError(f"calibration launch failed: hipError {rc}")
+        ms = _timed(launch, 5)
+        out["stream_read_gbs"] = round(read.value / (ms * 1e-3) / 1e9, 1)
+        out["stream_probe"] = (f"{read.value >> 20} MiB read by {blocks} blocks, one contiguous chunk each, "
+                               "16-byte loads, 8 in flight per thread (calib/ceilings.hip)")
+        del src
+    return out
 
 
 def calibrate_copy():
@@ -157,31 +252,77 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
+# ------------------------------------------------------------ rocprofv3 trace
+
+def summarize_trace(d: str, warmup: int, steps: int):
+    """Per-kernel table of a rocprofv3 --kernel-trace CSV: calls, average,
+    min and max over all launches, and the steady-state average over the
+    launches of the timed steps (a kernel launched c times per step in W
+    warm-up and K timed steps: its last c*K launches)."""
+    files = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    durs = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                name = row["Kernel_Name"]
+                durs.setdefault(name, []).append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    total = sum(e - s for v in durs.values() for s, e in v)
+    rows = []
+    for name, v in durs.items():
+        v.sort()
+        us = np.array([(e - s) / 1e3 for s, e in v])
+        steady = None
+        if len(v) % (warmup + steps) == 0:
+            per = len(v) // (warmup + steps)
+            steady = float(us[per * warmup:].mean())
+        rows.append((float(us.sum()), name, len(v), float(us.mean()), float(us.min()), float(us.max()), steady))
+    rows.sort(reverse=True)
+    print(f"| kernel | calls | avg µs | min µs | max µs | steady-state avg µs (last {steps} of {warmup + steps} "
+          f"steps) | % of GPU time |")
+    print("|---|---|---|---|---|---|---|")
+    for tot, name, n, avg, lo, hi, st in rows:
+        short = name if len(name) < 120 else name[:117] + "..."
+        sts = f"{st:.1f}" if st is not None else "—"
+        print(f"| `{short}` | {n} | {avg:.1f} | {lo:.1f} | {hi:.1f} | {sts} | {100 * tot / total:.2f} |")
+
+
+# ------------------------------------------------------------- CPU baseline
+
 def cpu_baseline(w, L, host_experts, sample):
-    """The float64 oracle on the first `sample` tokens (the layer is
-    token-wise, so this is exactly those tokens' forward)."""
+    """The float64 oracle on the first `sample` tokens (without a capacity the
+    layer is token-wise, so this is exactly those tokens' forward).  The
+    expert weights' decode to float64 is timed apart and not counted: it is
+    a property of the storage format, done once per weight load."""
     import oracle as O
     from threadpoolctl import threadpool_info
 
     x, wr, b = O.decoded_inputs(L)
     xs = x[:sample]
+    in_forward = [0.0]  # decode time spent inside the timed forward
 
     def expert(e):
+        t0 = time.perf_counter()
         ew = host_experts[e]
         w1, w3, w2 = O.decode(ew.w1, w.wdt), O.decode(ew.w3, w.wdt), O.decode(ew.w2, w.wdt)
         if w.wdt == "e4m3":
             w1 = w1 * ew.s1.astype(np.float64)[:, None]
             w3 = w3 * ew.s3.astype(np.float64)[:, None]
             w2 = w2 * ew.s2.astype(np.float64)[:, None]
+        in_forward[0] += time.perf_counter() - t0
         return w1, w3, w2
 
+    t0 = time.perf_counter()
     shared = O.adapters.decoded_shared(L)
+    shared_s = time.perf_counter() - t0
     # with a capacity factor the sample gets its own slots (factor * sample * k / E)
     cap = O.expert_capacity(getattr(w, "capacity_factor", 0), sample, w.k, w.E)
     t0 = time.perf_counter()
     O.layer_forward(xs, wr, b, O.workload_spec(w), w.E, expert, w.act, shared, capacity=cap,
                     fp8_dispatch=w.dispatch_fp8, overflow=w.overflow)
-    dt = time.perf_counter() - t0
+    dt = time.perf_counter() - t0 - in_forward[0]
+    decode_s = [shared_s + in_forward[0]]
     pools = threadpool_info()
     threads = max([p.get("num_threads", 1) for p in pools] or [1])
     blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools if p.get("user_api") == "blas"})
@@ -192,44 +333,33 @@ def cpu_baseline(w, L, host_experts, sample):
     except OSError:
         pass
     return {"value": round(sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "cpu_model": cpu_model, "blas": blas,
-            "kind": "oracle",
-            "sample": f"first {sample} of {w.T} tokens, full layer forward in float64 "
-                      f"(routing, dispatch, experts, combine), {dt:.2f} s"}
+            "cpu_model": cpu_model, "blas": blas, "kind": "oracle",
+            "sample": f"first {sample} of {w.T} tokens, full layer forward in float64 (routing, dispatch, "
+                      f"experts, combine): {dt:.2f} s of compute; the float64 decode of the stored expert "
+                      f"weights ({decode_s[0]:.2f} s) is excluded",
+            "compute_s": round(dt, 3), "weight_decode_s": round(decode_s[0], 3)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------------------------ one layer
+
+def measure(w, seed, args, keep_host=False, steps=None, warmup=None, cold=True):
+    """Times `steps` layer forwards of workload w after `warmup` untimed ones.
+    Returns (record fields, LayerInputs, host expert bytes or None)."""
     import torch
 
     import mixture_experts_layer_36_amd as moe
-    from synth import DEFAULT_SEED, BY_NAME, LayerInputs
+    from synth import LayerInputs
     from synth.device import DeviceLayer
 
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    w = BY_NAME[args.workload]
-    seed = DEFAULT_SEED[w.name] if args.seed is None else args.seed
-    if args.capacity_factor > 0:
-        w = w.scaled(capacity_factor=args.capacity_factor)
-    if args.dispatch_fp8:
-        w = w.scaled(dispatch_fp8=True)
-    if args.overflow != "drop":
-        w = w.scaled(overflow=args.overflow)
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     L = LayerInputs(w, seed)
-    host_experts = {}
-
-    # upload expert by expert, keeping host copies for the CPU baseline
+    host_experts = {} if keep_host else None
     orig = L.expert
 
     def keep(e):
         ew = orig(e)
-        if not args.no_cpu_baseline:
+        if keep_host:
             host_experts[e] = ew
         return ew
 
@@ -254,11 +384,10 @@ def main():
                           dev.s3, dev.s2, dev.sw1, dev.sw3, dev.sw2, out, idx, gw, counts, ws,
                           trace=trace)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    traces = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)]
-              for _ in range(args.steps)]
+    traces = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)] for _ in range(steps)]
     for tr in traces:  # create the HIP events before the timed region
         for ev in tr:
             ev.record()
@@ -267,7 +396,7 @@ def main():
     if args.graph:
         # per-stage times from a traced eager pass; the timed steps replay
         # one captured graph of the forward
-        for i in range(args.steps):
+        for i in range(steps):
             step(traces[i])
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
@@ -282,45 +411,41 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             graph.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     else:
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(traces[i])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
-    cold = None
-    if not args.no_cold:
+    cold_rec = None
+    if cold and not args.no_cold:
         # cold-cache repetitions, outside the timed region: the eviction
         # write runs between a step's events, never inside them
         evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
-        cold_tr = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)]
-                   for _ in range(args.steps)]
+        cold_tr = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.TRACE_EVENTS)] for _ in range(steps)]
         for tr in cold_tr:
             for ev in tr:
                 ev.record()
         torch.cuda.synchronize()
-        for i in range(args.steps):
+        for i in range(steps):
             evict.fill_(i & 0xff)
             step(cold_tr[i])
         torch.cuda.synchronize()
-        cms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
-                        for tr in cold_tr])
+        cms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)] for tr in cold_tr])
         cstep = float(np.median([tr[0].elapsed_time(tr[-1]) for tr in cold_tr]))
-        cold = {"evict_bytes": EVICT_BYTES, "reps": args.steps, "step_ms_median": round(cstep, 4),
-                "tokens_per_s": round(w.T / (cstep * 1e-3), 1),
-                "stages_us_median": {name: round(float(np.median(cms[:, j])) * 1e3, 2)
-                                     for j, name in enumerate(moe.TRACE_STAGES)}}
+        cold_rec = {"evict_bytes": EVICT_BYTES, "reps": steps, "step_ms_median": round(cstep, 4),
+                    "tokens_per_s": round(w.T / (cstep * 1e-3), 1),
+                    "stages_us_median": {name: round(float(np.median(cms[:, j])) * 1e3, 2)
+                                         for j, name in enumerate(moe.TRACE_STAGES)}}
         del evict
 
-    stage_ms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)]
-                         for tr in traces])
-    stage_us = {name: round(float(stage_ms[:, j].mean()) * 1e3, 2)
-                for j, name in enumerate(moe.TRACE_STAGES)}
+    stage_ms = np.array([[tr[j].elapsed_time(tr[j + 1]) for j in range(moe.TRACE_EVENTS - 1)] for tr in traces])
+    stage_us = {name: round(float(stage_ms[:, j].mean()) * 1e3, 2) for j, name in enumerate(moe.TRACE_STAGES)}
     step_events = [tr[0].elapsed_time(tr[-1]) for tr in traces]
     step_event_ms = float(np.mean(step_events))
     c = counts.cpu().numpy()
@@ -332,31 +457,32 @@ def main():
     n_assign = int(kept.sum())  # rows the experts process (dropped ones removed, rerouted ones added)
     own_kept = int(np.minimum(c, cap).sum()) if cap > 0 else n_assign
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = w.T * args.steps / elapsed
+    ms_per_step = elapsed * 1e3 / steps
+    value = w.T * steps / elapsed
     gemm1_s = stage_ms[:, 2].mean() * 1e-3
-    flops_gemm1 = 4.0 * w.d * w.f * n_assign
+    fused_sh = shared_fused(w)
+    flops_gemm1 = 4.0 * w.d * w.f * n_assign + (4.0 * w.d * w.f_shared * w.T if fused_sh else 0.0)
     flops_all = 6.0 * w.d * w.f * n_assign + 6.0 * w.d * w.f_shared * w.T
     if w.name in DECODE_WORKLOADS:
         layer_s = step_event_ms * 1e-3
         achieved = layer_bytes(w, c) / layer_s / 1e9
-        roof = {"bound": "hbm", "kernel": "whole layer (all kernels)", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "algorithmic_bytes": layer_bytes(w, c),
-                "frac_of_measured_read_ceiling": round(achieved / STREAM_READ_GBS, 4)}
+        roof = {"bound": "hbm", "kernel": "whole layer (all kernels of one moe_layer_forward)",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "algorithmic_bytes": layer_bytes(w, c),
+                "avg_launch_us": round(layer_s * 1e6, 2)}
     else:
         achieved = flops_gemm1 / gemm1_s / 1e12
         f8 = fp8_gate_up(w)
         peak = PEAK_FP8_TFLOPS if f8 else PEAK_BF16_TFLOPS
         kern = ("gemm_big_fp8_kernel: fp8 x fp8 block-scaled MFMA" if f8 else
-                "gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU")
-        roof = {"bound": "mfma", "kernel": f"routed gate-up GEMM + SwiGLU ({kern})",
+                "gemm_big_kernel / gemm_mfma_kernel, EPI_SWIGLU, with its split-tile fixup")
+        roof = {"bound": "mfma",
+                "kernel": f"gate-up GEMM + SwiGLU ({kern})" + (", routed and shared segments" if fused_sh else ""),
                 "mfma_dtype": "fp8" if f8 else "bf16",
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "algorithmic_flops": flops_gemm1,
+                "flops_formula": "4*d*f*rows" + (" + 4*d*f_shared*T" if fused_sh else ""),
                 "avg_launch_us": round(gemm1_s * 1e6, 2)}
-        roof["frac_of_measured_mfma_ceiling"] = round(achieved / (MFMA_LOOP_TFLOPS_FP8 if f8 else MFMA_LOOP_TFLOPS),
-                                                      4)
     # HBM bytes per launch of that kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE passes, valid only while the kernels are unchanged
     roof["traffic"] = None
@@ -367,12 +493,9 @@ def main():
         if ent and ent.get("source_hash") == kernel_source_hash():
             roof["traffic"] = ent.get("bytes_per_launch")
 
+    ffn_s = float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16, fp8 gate-up" if fp8_gate_up(w) else "bf16") if w.act == "bf16" else "f32",
-        "data": "synthetic",
+        "value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "E": w.E, "k": w.k,
                    "score": w.score, "n_group": w.n_group, "topk_group": w.topk_group,
                    "f_shared": w.f_shared, "act": w.act, "weights": w.wdt, "seed": seed,
@@ -381,9 +504,8 @@ def main():
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": roof,
         # all expert GEMMs (routed gate-up and down, shared expert) over their stages
-        "ffn_tflops": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12, 1),
-        "ffn_frac_of_bf16_peak": round(flops_all / (float(stage_ms[:, 2:5].sum(axis=1).mean()) * 1e-3) / 1e12
-                                       / PEAK_BF16_TFLOPS, 4),
+        "ffn_tflops": round(flops_all / ffn_s / 1e12, 1),
+        "ffn_frac_of_bf16_peak": round(flops_all / ffn_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages_us": stage_us,
         "stages_gbps": {k: round(v / (stage_us[k] * 1e-6) / 1e9, 1)
                         for k, v in stage_bytes(w, dev.bias is not None, n_assign).items()},
@@ -394,13 +516,85 @@ def main():
         "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,
                      "overflow": w.overflow, "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5),
                      "rerouted_fraction": round((n_assign - own_kept) / (w.T * w.k), 5)},
-        "cold_cache": cold,
-        "cpu_baseline": None,
+        "cold_cache": cold_rec,
     }
+    del dev, out, idx, gw, counts, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, L, host_experts
+
+
+def main():
+    args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.warmup, args.steps)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch  # noqa: F401
+
+    import mixture_experts_layer_36_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
+    from synth import BY_NAME, DEFAULT_SEED
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.calibrate_mfma or args.calibrate_stream:
+        which = (("mfma",) if args.calibrate_mfma else ()) + (("stream",) if args.calibrate_stream else ())
+        print(json.dumps({"calibration": "ceilings", **ceilings(which)}))
+        return
+    w = BY_NAME[args.workload]
+    seed = DEFAULT_SEED[w.name] if args.seed is None else args.seed
+    if args.capacity_factor > 0:
+        w = w.scaled(capacity_factor=args.capacity_factor)
+    if args.dispatch_fp8:
+        w = w.scaled(dispatch_fp8=True)
+    if args.overflow != "drop":
+        w = w.scaled(overflow=args.overflow)
+
+    rec, L, host_experts = measure(w, seed, args, keep_host=not args.no_cpu_baseline)
+    line = {
+        "metric": METRIC, "value": rec.pop("value"), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ("bf16, fp8 gate-up" if fp8_gate_up(w) else "bf16") if w.act == "bf16" else "f32",
+        "data": "synthetic",
+    }
+    line.update(rec)
+    ceil = None
+    if not args.no_ceilings:
+        ceil = ceilings()
+        r = line["roofline"]
+        if r["bound"] == "mfma":
+            key = "mfma_fp8_loop_tflops" if r["mfma_dtype"] == "fp8" else "mfma_bf16_loop_tflops"
+            r["frac_of_measured_mfma_ceiling"] = round(r["achieved"] / ceil[key], 4)
+        else:
+            r["frac_of_measured_read_ceiling"] = round(r["achieved"] / ceil["stream_read_gbs"], 4)
+    line["ceilings"] = ceil
+    line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or {"mixtral8x7b_prefill_bf16": 4096, "tiny_f32": 64}.get(w.name, 16)
-        rec["cpu_baseline"] = cpu_baseline(w, L, host_experts, min(sample, w.T))
-    print(json.dumps(rec))
+        sample = args.cpu_sample or CPU_SAMPLE.get(w.name, 256)
+        line["cpu_baseline"] = cpu_baseline(w, L, host_experts, min(sample, w.T))
+    del host_experts, L
+
+    line["decode"] = None
+    if w.name == DEFAULT_WORKLOAD and not args.no_decode_leg and args.workload == DEFAULT_WORKLOAD:
+        # the decode-shaped layer, bound by HBM bandwidth: its own steps
+        # (more of them: a step is ~4 ms), no cold repetitions
+        wd = BY_NAME[DECODE_WORKLOAD]
+        d_rec, _, _ = measure(wd, DEFAULT_SEED[wd.name], args, steps=4 * args.steps, warmup=args.warmup,
+                              cold=False)
+        r = d_rec["roofline"]
+        if ceil:
+            r["frac_of_measured_read_ceiling"] = round(r["achieved"] / ceil["stream_read_gbs"], 4)
+        line["decode"] = {"metric": "MoE-layer tokens/s per MI355X; decode % HBM BW",
+                          "value": d_rec["value"], "unit": "tokens/s", "steps": 4 * args.steps,
+                          "ms_per_step": d_rec["ms_per_step"], "config": d_rec["config"], "roofline": r,
+                          "stages_us": d_rec["stages_us"], "stages_gbps": d_rec["stages_gbps"],
+                          "load": d_rec["load"]}
+    print(json.dumps(line))
 
 
 if __name__ == "__main__":

@@ -1,4 +1,6 @@
-"""Builds libmoe.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Builds libmoe.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree,
+and libmoe_calib.so (the bench's ceiling probes, calib/), which the layer
+library does not contain or load.
 
     python -m mixture_experts_layer_36_amd.build
 """
@@ -16,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libmoe.so")
+CALIB_SRC = os.path.join(PKG, "calib", "ceilings.hip")
+CALIB_LIB = os.path.join(LIB_DIR, "libmoe_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -39,20 +43,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as pool:
-        objs = list(pool.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-o", tmp, "--offload-arch=gfx950", "-fPIC"] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as pool:
+        calib = pool.submit(_compile, CALIB_SRC)
+        objs = list(pool.map(_compile, srcs))
+        calib_obj = calib.result()
+    _link(objs, LIB)
+    _link([calib_obj], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

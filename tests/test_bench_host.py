@@ -1,0 +1,60 @@
+"""bench.py's host logic, without a GPU: the one-GPU refusal, the rocprofv3
+trace summary (steady-state averages over the timed steps) and the
+algorithmic-work formulas the roofline divides by."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from synth import BY_NAME
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_summarize_trace_steady_state(tmp_path, capsys):
+    # kernel A: once per step, 2 warm-up steps of 100 us then 3 of 10 us;
+    # kernel B: twice per step, always 5 us
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for step in range(5):
+        dur = 100_000 if step < 2 else 10_000
+        rows.append(f"A,{t},{t + dur}")
+        t += dur + 1000
+        for _ in range(2):
+            rows.append(f"B,{t},{t + 5000}")
+            t += 6000
+    sub = tmp_path / "host"
+    sub.mkdir()
+    (sub / "123_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_trace(str(tmp_path), warmup=2, steps=3)
+    out = capsys.readouterr().out.splitlines()
+    a = next(ln for ln in out if ln.startswith("| `A`"))
+    b = next(ln for ln in out if ln.startswith("| `B`"))
+    cols = [c.strip() for c in a.split("|")]
+    assert cols[2] == "5" and cols[3] == "46.0" and cols[6] == "10.0"  # all-launch avg vs steady state
+    cols = [c.strip() for c in b.split("|")]
+    assert cols[2] == "10" and cols[6] == "5.0"
+
+
+def test_gate_up_flops_count_the_fused_shared_expert():
+    w4 = BY_NAME["dsv3_prefill_skew_bf16"]
+    assert bench.shared_fused(w4)  # bf16 shared weights beside bf16 routed weights: one launch
+    assert not bench.shared_fused(BY_NAME["qwen_moe_fp8_skew"])  # no shared expert
+    assert not bench.shared_fused(BY_NAME["mixtral8x7b_prefill_bf16"])
+
+
+def test_layer_bytes_counts_touched_experts_only():
+    w = BY_NAME["dsv3_decode_bf16"]
+    c = np.zeros(w.E, dtype=np.int64)
+    c[:10] = 1
+    b10 = bench.layer_bytes(w, c)
+    c[:11] = 1
+    assert bench.layer_bytes(w, c) - b10 == 3 * w.d * w.f * 2
