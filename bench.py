@@ -58,6 +58,7 @@ DEFAULT_WORKLOAD = "dsv3_prefill_skew_bf16"
 DECODE_WORKLOAD = "dsv3_decode_bf16"
 DECODE_WORKLOADS = {"dsv3_decode_bf16"}
 EVICT_BYTES = 512 << 20
+XCDS = 8  # MI355X: 8 XCDs of 32 compute units
 # oracle tokens timed per workload: about 10 s of float64 compute on a
 # 16-core host (the whole batch where it is small enough)
 CPU_SAMPLE = {"tiny_f32": 64, "mixtral8x7b_prefill_bf16": 4096, "dsv3_decode_bf16": 256,
@@ -94,6 +95,9 @@ def parse():
                    help="only run a plain 1 GiB device copy (counter calibration)")
     p.add_argument("--calibrate-mfma", action="store_true", help="only run the bf16 and fp8 MFMA-loop probes")
     p.add_argument("--calibrate-stream", action="store_true", help="only run the streaming-read probe")
+    p.add_argument("--summarize-counters", metavar="DIR", default=None,
+                   help="summarise rocprofv3 --pmc counter CSVs under DIR (no GPU): per kernel, the mean of "
+                        "each counter over the dispatches of the timed steps (--warmup / --steps as above)")
     p.add_argument("--summarize-trace", metavar="DIR", default=None,
                    help="summarise a rocprofv3 --kernel-trace CSV under DIR (no GPU): per-kernel calls and "
                         "average, and the steady-state average over the timed steps given by --warmup and "
@@ -112,6 +116,11 @@ def kernel_source_hash() -> str:
             code = [ln.split("//", 1)[0].rstrip() for ln in fh]
         h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
+
+
+def progress(msg: str):
+    """A progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 # ------------------------------------------------------------ algorithmic work
@@ -288,6 +297,69 @@ def summarize_trace(d: str, warmup: int, steps: int):
         print(f"| `{short}` | {n} | {avg:.1f} | {lo:.1f} | {hi:.1f} | {sts} | {100 * tot / total:.2f} |")
 
 
+def summarize_counters(d: str, warmup: int, steps: int):
+    """Per kernel and counter of rocprofv3 --pmc CSVs: the mean value per
+    dispatch over the timed steps (a kernel dispatched c times per step in W
+    warm-up and K timed steps: its last c*K dispatches), and derived ratios
+    where their inputs are present: MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES per
+    SIMD over the kernel's cycles), TA and TD busy per CU, and L1 stalls.
+    GRBM_GUI_ACTIVE comes summed over the 8 XCDs (8x the cycles of the
+    kernel's span at the clock: checked against its duration), so one XCD's
+    count, GRBM_GUI_ACTIVE / 8, is the kernel's cycles."""
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    vals = {}  # (kernel, counter) -> {dispatch: value}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                key = (row["Kernel_Name"], row["Counter_Name"])
+                did = (f, int(row["Dispatch_Id"]))
+                vals.setdefault(key, {})
+                vals[key][did] = vals[key].get(did, 0.0) + float(row["Counter_Value"])
+    kernels = sorted({k for k, _ in vals})
+    for kern in kernels:
+        ctrs = sorted(c for k, c in vals if k == kern)
+        mean = {}
+        n_disp = 0
+        for c in ctrs:
+            per = [v for _, v in sorted(vals[(kern, c)].items())]
+            n_disp = len(per)
+            if len(per) % (warmup + steps) == 0:
+                per = per[len(per) // (warmup + steps) * warmup:]
+            mean[c] = float(np.mean(per))
+        print(f"### `{kern}` ({n_disp} dispatches)\n")
+        print("| counter | mean per dispatch (timed steps) |\n|---|---|")
+        for c in ctrs:
+            print(f"| {c} | {mean[c]:.6g} |")
+        g = mean.get("GRBM_GUI_ACTIVE")
+        g = g / XCDS if g else g
+        derived = []
+        if g:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                derived.append(("MFMA busy, % of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x "
+                                "1024 SIMDs))", 100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024)))
+            for c, what in (("TA_TA_BUSY", "TA busy"), ("TD_TD_BUSY", "TD busy"),
+                            ("TA_ADDR_STALLED_BY_TC_CYCLES", "TA address stalled by the L1 (TC)"),
+                            ("TD_TC_STALL", "TD stalled by the L1 (TC)"),
+                            ("TCP_TCR_TCP_STALL_CYCLES", "L1 stalled by the L2 request path (TCR)"),
+                            ("TCP_PENDING_STALL_CYCLES", "L1 stalled on pending misses"),
+                            ("SQ_BUSY_CU_CYCLES", "CU busy (SQ_BUSY_CU_CYCLES)")):
+                if c in mean:
+                    derived.append((f"{what}, % of cycles per CU ({c} / (GRBM_GUI_ACTIVE / 8 x 256 CUs))",
+                                    100 * mean[c] / (g * 256)))
+        if "SQ_INSTS_MFMA" in mean and "SQ_INSTS_VALU" in mean:
+            derived.append(("non-MFMA VALU instructions per MFMA", (mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"])
+                            / max(mean["SQ_INSTS_MFMA"], 1.0)))
+        if "SQ_INSTS_LDS" in mean and "SQ_INSTS_MFMA" in mean:
+            derived.append(("LDS instructions per MFMA", mean["SQ_INSTS_LDS"] / max(mean["SQ_INSTS_MFMA"], 1.0)))
+        if derived:
+            print("\n| derived | value |\n|---|---|")
+            for what, v in derived:
+                print(f"| {what} | {v:.4g} |")
+        print()
+
+
 # ------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, L, host_experts, sample):
@@ -353,6 +425,7 @@ def measure(w, seed, args, keep_host=False, steps=None, warmup=None, cold=True):
 
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
+    progress(f"{w.name}: generating and uploading inputs (seed {seed})")
     L = LayerInputs(w, seed)
     host_experts = {} if keep_host else None
     orig = L.expert
@@ -384,6 +457,7 @@ def measure(w, seed, args, keep_host=False, steps=None, warmup=None, cold=True):
                           dev.s3, dev.s2, dev.sw1, dev.sw3, dev.sw2, out, idx, gw, counts, ws,
                           trace=trace)
 
+    progress(f"{w.name}: {warmup} warm-up and {steps} timed steps")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -529,6 +603,9 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.warmup, args.steps)
         return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.warmup, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -565,6 +642,7 @@ def main():
     line.update(rec)
     ceil = None
     if not args.no_ceilings:
+        progress("ceiling probes")
         ceil = ceilings()
         r = line["roofline"]
         if r["bound"] == "mfma":
@@ -576,6 +654,7 @@ def main():
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or CPU_SAMPLE.get(w.name, 256)
+        progress(f"oracle on {min(sample, w.T)} tokens")
         line["cpu_baseline"] = cpu_baseline(w, L, host_experts, min(sample, w.T))
     del host_experts, L
 

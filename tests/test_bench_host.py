@@ -58,3 +58,18 @@ def test_layer_bytes_counts_touched_experts_only():
     b10 = bench.layer_bytes(w, c)
     c[:11] = 1
     assert bench.layer_bytes(w, c) - b10 == 3 * w.d * w.f * 2
+
+
+def test_summarize_counters_timed_dispatches(tmp_path, capsys):
+    # one kernel, 1 warm-up + 2 timed steps; the warm-up dispatch is excluded
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    for disp, (mfma, gui) in enumerate(((900.0, 1000.0), (512.0, 1000.0), (256.0, 1000.0))):
+        rows.append(f"{disp},K,SQ_VALU_MFMA_BUSY_CYCLES,{mfma * 1024}")
+        rows.append(f"{disp},K,GRBM_GUI_ACTIVE,{gui * 8}")  # summed over the 8 XCDs
+        rows.append(f"{disp},K,TA_TA_BUSY,{250.0 * 256}")
+    (tmp_path / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_counters(str(tmp_path), warmup=1, steps=2)
+    out = capsys.readouterr().out
+    assert "| SQ_VALU_MFMA_BUSY_CYCLES | 393216 |" in out  # mean of 512 and 256 (x1024)
+    assert "MFMA busy" in out and "| 38.4 |" in out
+    assert "TA busy" in out and "| 25 |" in out
