@@ -237,6 +237,27 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, const voi
                         int32_t* inv_pos, void* x_perm, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* moe_dispatch with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (less ws, ws_bytes) and the same
+ * outputs as moe_dispatch, bit for bit; allocates nothing and calls no
+ * allocating routine.
+ * Its scratch (the per-chunk expert counts) is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library, one copy per GPU, held until the
+ * process ends.  A desc whose dispatch workspace (moe_workspace_size with
+ * MOE_STAGE_DISPATCH: ceil(T*k/256) * E * 4 bytes) exceeds it gives
+ * MOE_ERR_WORKSPACE: T*k up to 2^28 / E assignments fit (2^20 at E = 256).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Nothing in the array needs clearing: each call writes every entry it reads.
+ * The buffers and the stream must belong to the current device; the first
+ * call on a device looks up its copy of the array (MOE_ERR_DEVICE if that
+ * fails).  overflow = MOE_OVERFLOW_REROUTE gives MOE_ERR_UNSUPPORTED. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+moe_status moe_dispatch_noalloc(const moe_desc* desc, const int32_t* topk_idx, const void* x, int32_t* counts,
+                                int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
+                                void* stream);
+
 /* Dispatch with capacity overflow rerouted (desc: capacity > 0 and overflow =
  * MOE_OVERFLOW_REROUTE, else MOE_ERR_INVALID): the two passes of "Capacity
  * overflow" above, from moe_route_candidates' outputs.  Outputs as

@@ -27,7 +27,8 @@ TRACE_STAGES = ("route", "dispatch", "gemm1_swiglu", "gemm2", "shared_expert", "
 # the exported symbols include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_layer_rows", "moe_pack_weights",
-           "moe_route_candidates", "moe_dispatch_reroute", "moe_capacity_slots")
+           "moe_route_candidates", "moe_dispatch_reroute", "moe_capacity_slots",
+           "moe_dispatch_noalloc")
 
 _DTYPES = {"f32": F32, "bf16": BF16, "e4m3": FP8_E4M3}
 OVERFLOW_DROP, OVERFLOW_REROUTE = 0, 1
@@ -122,6 +123,7 @@ def _lib() -> ctypes.CDLL:
         lib.moe_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_route.argtypes = [D, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         lib.moe_dispatch.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.moe_dispatch_noalloc.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P]
         lib.moe_grouped_ffn.argtypes = [D] + [_P] * 11 + [ctypes.c_size_t, _P]
         lib.moe_combine.argtypes = [D, _P, _P, _P, _P, _P, _P]
         lib.moe_layer_forward.argtypes = [D] + [_P] * 17 + [ctypes.c_size_t, _P, _P]
@@ -200,6 +202,16 @@ def dispatch(desc, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, ws
     _check(_lib().moe_dispatch(ctypes.byref(desc), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
                                _ptr(perm_token), _ptr(inv_pos), _ptr(x_perm), _ptr(ws),
                                ws.numel() if ws is not None else 0, _stream(stream)), "moe_dispatch")
+
+
+def dispatch_noalloc(desc, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, stream=None):
+    """moe_dispatch_noalloc: moe_dispatch with the library's static scratch."""
+    _check(_lib().moe_dispatch_noalloc(ctypes.byref(desc), _ptr(topk_idx), _ptr(x), _ptr(counts), _ptr(offsets),
+                                       _ptr(perm_token), _ptr(inv_pos), _ptr(x_perm), _stream(stream)),
+           "moe_dispatch_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 def grouped_ffn(desc, x_perm, offsets, w1, w3, w2, s1, s3, s2, h, y_perm, ws, stream=None):

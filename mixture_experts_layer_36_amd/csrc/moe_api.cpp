@@ -7,10 +7,20 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
+#include <mutex>
 
 #include "moe_internal.hpp"
 
 using namespace moe;
+
+// Scratch of moe_dispatch_noalloc: the per-chunk expert counts of the
+// dispatch index kernels, in a static device array (one copy per GPU, held
+// until the process ends) instead of a caller workspace.  Host code never
+// uses the symbol itself as an address: each device's copy is looked up once
+// with hipGetSymbolAddress (scratch_on_current_device) and that pointer is
+// what the kernels get.
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
 
 namespace {
 
@@ -499,6 +509,40 @@ bool scales_ok(const moe_desc* d, const float* s1, const float* s3, const float*
   return s1 == nullptr && s3 == nullptr && s2 == nullptr;
 }
 
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (with the device current) and kept: MOE_ERR_DEVICE if the
+// lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::array<void*, kMaxDevices> g_scratch_ptr{};
+moe_status scratch_on_current_device(void** out) {
+  int dev_id = -1;
+  if (hipGetDevice(&dev_id) != hipSuccess) return MOE_ERR_DEVICE;
+  if (dev_id < 0 || dev_id >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev_id] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_DEVICE;
+    g_scratch_ptr[dev_id] = p;
+  }
+  *out = g_scratch_ptr[dev_id];
+  return MOE_OK;
+}
+
+// moe_dispatch after validation, on a workspace of at least
+// stage_bytes(d, MOE_STAGE_DISPATCH) bytes.
+moe_status dispatch_on(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm, void* ws,
+                       hipStream_t s) {
+  Carve c(ws);
+  const DispatchWs w = carve_dispatch(c, d, false);
+  if (!d->dispatch_fp8)
+    return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w, s);
+  MOE_TRY(run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, nullptr, w, s));
+  if (d->T == 0) return MOE_OK;
+  return run_payload(d, x, perm_token, int(n_assign(d)), offsets + d->E, false, x_perm, s);
+}
+
 moe_status record(void* const* trace, int i, hipStream_t s) {
   if (trace == nullptr) return MOE_OK;
   return dev(hipEventRecord(static_cast<hipEvent_t>(trace[i]), s));
@@ -622,14 +666,23 @@ moe_status moe_dispatch(const moe_desc* d, const int32_t* topk_idx, const void* 
                    !need(x_perm) || !need(ws)))
     return MOE_ERR_INVALID;
   if (d->T > 0 && ws_bytes < stage_bytes(d, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
-  Carve c(ws);
-  const DispatchWs w = carve_dispatch(c, d, false);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!d->dispatch_fp8)
-    return run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, w, s);
-  MOE_TRY(run_dispatch(d, topk_idx, x, counts, offsets, perm_token, inv_pos, nullptr, w, s));
-  if (d->T == 0) return MOE_OK;
-  return run_payload(d, x, perm_token, int(n_assign(d)), offsets + d->E, false, x_perm, s);
+  return dispatch_on(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_dispatch_noalloc(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t* counts,
+                                int32_t* offsets, int32_t* perm_token, int32_t* inv_pos, void* x_perm,
+                                void* stream) {
+  MOE_TRY(check_desc(d));
+  if (reroute(d)) return MOE_ERR_UNSUPPORTED;  // as moe_dispatch
+  if (!need(counts) || !need(offsets)) return MOE_ERR_INVALID;
+  if (d->T > 0 && (!need(topk_idx) || !need(x) || !need(perm_token) || !need(inv_pos) || !need(x_perm)))
+    return MOE_ERR_INVALID;
+  if (stage_bytes(d, MOE_STAGE_DISPATCH) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MOE_TRY(scratch_on_current_device(&ws));
+  return dispatch_on(d, topk_idx, x, counts, offsets, perm_token, inv_pos, x_perm, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets,

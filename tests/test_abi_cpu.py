@@ -229,3 +229,22 @@ def test_capacity_slots_c_abi():
                  (1 << 40, 1, 1 << 20, 16, 1)):  # the last exceeds INT32_MAX slots
         assert lib.moe_capacity_slots(*args, ctypes.byref(out)) == moe.MOE_ERR_INVALID, args
     assert lib.moe_capacity_slots(1, 1, 8, 2, 4, None) == moe.MOE_ERR_INVALID
+
+
+def test_noalloc_dispatch_validates_before_touching_a_gpu():
+    """moe_dispatch_noalloc rejects a desc whose chunk counts exceed its
+    static scratch, and rerouting, before it looks up the scratch on a
+    device (no GPU here)."""
+    lib = _lib._lib()
+    ok = ctypes.c_void_p(16)
+    null = ctypes.c_void_p(0)
+    big = _good(T=(1 << 20) // 8 + 256, d=128, f=128, E=256, k=8, act="bf16", wdtype="bf16")
+    assert moe.workspace_size(big, moe.STAGE_DISPATCH) > moe.NOALLOC_SCRATCH_BYTES
+    D = ctypes.byref(big)
+    assert lib.moe_dispatch_noalloc(D, ok, ok, ok, ok, ok, ok, ok, null) == moe.MOE_ERR_WORKSPACE
+    fits = _good(T=(1 << 20) // 8, d=128, f=128, E=256, k=8, act="bf16", wdtype="bf16")
+    assert moe.workspace_size(fits, moe.STAGE_DISPATCH) <= moe.NOALLOC_SCRATCH_BYTES
+    rr = _good(capacity=5, overflow="reroute")
+    assert lib.moe_dispatch_noalloc(ctypes.byref(rr), ok, ok, ok, ok, ok, ok, ok, null) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_dispatch_noalloc(ctypes.byref(_good()), ok, ok, null, ok, ok, ok, ok, null) == \
+        moe.MOE_ERR_INVALID
