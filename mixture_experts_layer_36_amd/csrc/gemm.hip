@@ -17,6 +17,7 @@
 //     4 consecutive output columns of one activation row, which become 8-byte
 //     (bf16) or 16-byte (fp32) stores;
 //   * fp8 (OCP E4M3) weights are widened to bf16 exactly while being staged
+//     (gfx950's packed scaled conversion, two codes per instruction)
 //     into LDS; the per-output-channel scale multiplies the fp32 accumulator
 //     in the epilogue, so y = s_n * sum_k x_k q_nk exactly as dequantised;
 //   * SwiGLU: each wavefront's weight rows are half W1 rows and half W3 rows
@@ -131,9 +132,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a, int n_slots,
         u32x4 lo, hi;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t v = rb[j][w];
-          const uint32_t p0 = e4m3_to_bf16(v & 0xff) | (e4m3_to_bf16((v >> 8) & 0xff) << 16);
-          const uint32_t p1 = e4m3_to_bf16((v >> 16) & 0xff) | (e4m3_to_bf16(v >> 24) << 16);
+          const u32x2 pp = e4m3x4_to_bf16_bits(rb[j][w]);
+          const uint32_t p0 = pp[0], p1 = pp[1];
           if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
         }
         const int off = b_dst[j] - BM * C::BK;

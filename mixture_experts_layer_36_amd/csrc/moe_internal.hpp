@@ -9,6 +9,8 @@ namespace moe {
 
 // ---------------------------------------------------------------- device utils
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +52,17 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b) {
     mag = __float_as_uint((float)em * 0.001953125f) >> 16;  // m * 2^-9, exact
   }
   return sign | mag;
+}
+
+// Four OCP E4M3 codes (bytes 0..3 of w) -> their bf16 bits, two per word
+// (bytes 0, 1 in word 0), exactly: gfx950's packed scaled conversion with a
+// scale of 1.0.  Whole pairs are bit-cast: clang miscompiles a bit cast of
+// one component of such a vector (it takes the first component).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16_bits(uint32_t w) {
+  u32x2 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return o;
 }
 
 // ------------------------------------------------------------------ launchers
