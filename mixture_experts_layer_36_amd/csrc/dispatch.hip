@@ -332,9 +332,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
   }
 }
 
-// The same rows into K/32 planes of [rows][32] bf16: thread g moves the 16
-// bytes at g, so a wave stores one contiguous kilobyte (16 rows x 64 bytes of
-// one plane) and loads 16 row runs of 64 bytes.
+// The same rows into K/32 planes of [rows][32] bf16 (perm NULL: x's rows in
+// order): thread g moves the 16 bytes at g, so a wave stores one contiguous
+// kilobyte (16 rows x 64 bytes of one plane) and loads 16 row runs of 64
+// bytes.
 __global__ __launch_bounds__(256) void gather_blocked_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ perm, int rows,
                                                              const int32_t* __restrict__ rows_dev, int d,
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void gather_blocked_kernel(const u32x4* __rest
   const int p = (int)(g / per_plane), rem = (int)(g % per_plane), r = rem >> 2, q = rem & 3;
   const int n = rows_dev ? min(*rows_dev, rows) : rows;
   if (r >= n) return;
-  out[g] = x[((size_t)perm[r] * d + p * 32 + q * 8) / 8];
+  out[g] = x[((size_t)(perm ? perm[r] : r) * d + p * 32 + q * 8) / 8];
 }
 
 __global__ __launch_bounds__(256) void segment_rows_kernel(const int32_t* offsets, int E, int32_t* rows) {

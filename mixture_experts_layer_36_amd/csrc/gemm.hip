@@ -404,7 +404,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if ((a.a_blk || a.sh_a_blk || a.c_blk) &&
       !(a.act != GD_F32 && !use_decode(a) && use_big(a) && a.epi != EPI_BIAS_F32 &&
-        (!a.c_blk || a.epi == EPI_SWIGLU) && (!a.a_blk || (a.act == GD_BF16 && a.a_map == nullptr)) &&
+        (!a.c_blk || a.epi == EPI_SWIGLU) && (!a.a_blk || a.act == GD_BF16) &&
         (!a.sh_a_blk || a.act == GD_BF16)))
     return hipErrorInvalidValue;
   if (a.act == GD_F32) {

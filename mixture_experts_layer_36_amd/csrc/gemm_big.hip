@@ -402,7 +402,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     const int r = s / CH, c = (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
     if (a_plane) {
-      a_off[j] = (uint32_t)((ti.row0 + rr) * BK + c * 8) * 2u;
+      const int ar = sg.amap ? sg.amap[ti.row0 + rr] : ti.row0 + rr;
+      a_off[j] = (uint32_t)(ar * BK + c * 8) * 2u;
     } else {
       const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
       a_off[j] = (uint32_t)(ar * K + c * 8) * 2u;

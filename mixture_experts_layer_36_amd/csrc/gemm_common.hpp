@@ -82,7 +82,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.N = a.N;
   sg.K = a.K;
   sg.amap = a.a_map;
-  sg.a_prows = a.a_blk ? a.rows : 0;
+  sg.a_prows = a.a_blk ? (a.a_map ? a.a_map_rows : a.rows) : 0;
   sg.c_prows = a.c_blk ? a.rows : 0;
   sg.b_blk = a.b_blk;
   return ti.nrows > 0;

@@ -143,7 +143,7 @@ hipError_t launch_segment_rows(const int32_t* offsets, int E, int32_t* rows, hip
 hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
                               int row_bytes, void* x_perm, hipStream_t s);
 // The same rows into the K-blocked planes of GemmArgs::a_blk (P = rows): bf16,
-// d a multiple of 32.
+// d a multiple of 32; perm_token NULL copies x's rows in order.
 hipError_t launch_gather_rows_blocked(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
                                       int d, void* x_perm, hipStream_t s);
 
@@ -234,10 +234,11 @@ struct GemmArgs {
   // Prefill kernel only, bf16: K-blocked operands.  A K-blocked matrix of P
   // rows and K columns is K/32 planes of [P][32] elements, element (r, k) at
   // (k / 32) * P * 32 + r * 32 + k % 32, so the 32-column slice of a tile's
-  // rows is one contiguous run.  a_blk (no row map): A in this layout with
-  // P = rows; sh_a_blk: the extra segment's shA with P = sh_rows.  c_blk
-  // (SwiGLU only): C with P = rows and shC with P = sh_rows.  Each matrix
-  // must stay under 2^31 bytes.
+  // rows is one contiguous run.  a_blk: A in this layout with P = rows, or,
+  // with a row map, P = a_map_rows (the map indexes the planes' rows);
+  // sh_a_blk: the extra segment's shA with P = sh_rows.  c_blk (SwiGLU
+  // only): C with P = rows and shC with P = sh_rows.  Each matrix must stay
+  // under 2^31 bytes.
   int a_blk;
   int sh_a_blk;
   int c_blk;
