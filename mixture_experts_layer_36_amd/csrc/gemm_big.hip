@@ -201,9 +201,10 @@ struct Work {
   int mt, nt, k0num, slot, s;
 };
 // Blocks are dealt round-robin to the 8 XCDs (block b on XCD b % 8).  Whole
-// tiles come first, an equal contiguous share per XCD (grouped order, so the
-// blocks an XCD runs at once share operands in its L2); the split pieces
-// follow, again an equal share per XCD, so they all run in the last wave.
+// tiles come first, an equal share per XCD (xcd_tile: whole groups in turn,
+// so the blocks an XCD runs at once share operands in its L2); the split
+// pieces follow, again an equal share per XCD, so they all run in the last
+// wave.
 [[maybe_unused]] __device__ __forceinline__ bool big_work(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu,
                                          int BMv, Work& w) {
   const int m_real = real_mtiles(a, BMv);
@@ -217,7 +218,7 @@ struct Work {
   if (p.rem > 0) {
     const int f8 = p.full >> 3, Q = p.rem * p.s, q = (Q + 7) >> 3;
     if (i < f8) {
-      L = x * f8 + i;
+      if (!xcd_tile(x, i, p.full, n_tiles, L)) return false;
     } else {
       const int j = i - f8, pi = x * q + j;
       if (j >= q || pi >= Q) return false;
@@ -227,9 +228,7 @@ struct Work {
       w.s = p.s;
     }
   } else {
-    const int share = (R + 7) >> 3;
-    L = x * share + i;
-    if (i >= share || L >= R) return false;
+    if (!xcd_tile(x, i, R, n_tiles, L)) return false;
   }
   tile_coords(L, m_real, n_tiles, w.mt, w.nt);
   return true;

@@ -107,6 +107,23 @@ __device__ __forceinline__ void tile_coords(int L, int m_real, int n_tiles, int&
   mt = g * kGroupM + within % gm;
   nt = within / gm;
 }
+// Block (XCD x, index i on it) of an equal per-XCD share of the first Rw
+// tiles of the grouped order -> its tile L.  Whole groups go to the XCDs in
+// turn (super-groups of 8 groups: XCD x takes the x-th), so the 8 blocks of
+// one dispatch round sit at the same place in 8 neighbouring groups --
+// usually tiles of the same expert and kind, of equal duration -- while the
+// blocks an XCD runs at once still share operands in its L2; tiles past the
+// last whole super-group are dealt in turn one by one.  False past Rw.
+__device__ __forceinline__ bool xcd_tile(int x, int i, int Rw, int n_tiles, int& L) {
+  const int G = kGroupM * n_tiles, SG = 8 * G;
+  const int ns = Rw / SG;
+  if (i < ns * G) {
+    L = (i / G) * SG + x * G + i % G;
+    return true;
+  }
+  L = ns * SG + (i - ns * G) * 8 + x;
+  return L < Rw;
+}
 __device__ __forceinline__ void block_coords(int m_real, int n_tiles, int& mt, int& nt) {
   const int per_xcd = (gridDim.x >> 3);
   const int R = m_real * n_tiles;
