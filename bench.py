@@ -277,7 +277,7 @@ def summarize_trace(d: str, warmup: int, steps: int):
             for row in csv.DictReader(fh):
                 name = row["Kernel_Name"]
                 durs.setdefault(name, []).append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
-    total = sum(e - s for v in durs.values() for s, e in v)
+    total = sum(e - s for v in durs.values() for s, e in v) / 1e3  # us
     rows = []
     for name, v in durs.items():
         v.sort()
