@@ -17,8 +17,12 @@ Prints one JSON line:
               HBM bandwidth; durations come from HIP events the library
               records around each stage inside the timed steps, on the stream
               the kernels run on
-  ceilings    measured in this run: a register-only bf16 and fp8 MFMA loop and
-              a streaming read (calib/ceilings.hip)
+  ceilings    measured in this run: the GEMM's MFMA pattern alone (bf16 and fp8,
+              random and constant operands, each sustained ~1 s, with the
+              socket power and graphics clock read meanwhile) and a streaming
+              read (calib/ceilings.hip)
+  sustained   the same step repeated for ~2 s after the timed steps, with the
+              socket power and graphics clock read meanwhile (amdsmi)
   cpu_baseline the float64 oracle's forward of a bounded token sample on the
               host cores (the fp64 decode of the expert weights timed apart)
   stages_gbps achieved GB/s of the route, dispatch and combine stages
@@ -88,6 +92,8 @@ def parse():
                         "times then come from a separate traced eager pass")
     p.add_argument("--no-cold", action="store_true", help="skip the cold-cache repetitions")
     p.add_argument("--no-ceilings", action="store_true", help="skip the in-run MFMA / stream ceiling probes")
+    p.add_argument("--sustain-seconds", type=float, default=2.0,
+                   help="after the timed steps, repeat the step this long with power sampling (0: skip)")
     p.add_argument("--w-layout", choices=("auto", "rowmajor", "kblocked"), default="auto",
                    help="routed expert weight layout; auto: kblocked for bf16 / fp8 weights (packed "
                         "once after upload, before any timing), rowmajor for fp32")
@@ -189,8 +195,8 @@ def _calib_lib():
     if not os.path.exists(CALIB_LIB):
         raise ImportError(f"{CALIB_LIB} is missing: build with `python -m mixture_experts_layer_36_amd.build`")
     lib = ctypes.CDLL(CALIB_LIB)
-    lib.moe_calib_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.moe_calib_mfma_fp8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for fn in (lib.moe_calib_mfma_bf16_gemm, lib.moe_calib_mfma_fp8_gemm):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p]
     return lib
@@ -210,26 +216,119 @@ def _timed(launch, reps):
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+class PowerSampler:
+    """Socket power and graphics clock, read from the GPU's metrics table
+    (amdsmi, read-only) every few ms on a thread while a sustained run goes on.
+    Without amdsmi, or on any error from it, the summary is None."""
+
+    SETTLE_S = 0.25  # samples in the first 0.25 s of a window are dropped
+
+    def __init__(self):
+        import threading
+        self.samples, self.h, self.cap_w = [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_cap_info(self.h).get("power_cap")
+            self.cap_w = round(cap / 1e6, 1) if isinstance(cap, (int, float)) and cap > 0 else None
+        except Exception:
+            self.h = None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self.h)
+                self.samples.append((time.perf_counter(), m.get("current_socket_power"), m.get("current_gfxclk")))
+            except Exception:
+                pass
+            time.sleep(0.004)
+
+    def start(self):
+        import threading
+        if self.h is None:
+            return
+        self.samples = []
+        self._stop.clear()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self, t0: float, t1: float):
+        """Medians over [t0 + SETTLE_S, t1], or None."""
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        self._thread = None
+        return self.summarize(self.samples, t0 + self.SETTLE_S, t1, self.cap_w)
+
+    @staticmethod
+    def summarize(samples, t0: float, t1: float, cap_w=None):
+        """Medians of (time, socket W, gfx MHz) samples taken in [t0, t1];
+        readings the table marks unavailable (0, 0xffff) are skipped."""
+        win = [x for x in samples if t0 <= x[0] <= t1]
+
+        def med(i):
+            v = [x[i] for x in win if isinstance(x[i], (int, float)) and 0 < x[i] < 0xffff]
+            return round(float(np.median(v)), 1) if v else None
+        if not win:
+            return None
+        return {"socket_power_w_median": med(1), "gfxclk_mhz_median": med(2), "power_cap_w": cap_w,
+                "samples": len(win)}
+
+
+def _sustained(launch, seconds: float, sampler=None):
+    """Launch repeatedly, in batches, until `seconds` have passed; returns
+    (launches, wall seconds, power summary or None)."""
+    import torch
+    launch()
+    torch.cuda.synchronize()
+    if sampler:
+        sampler.start()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            launch()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    t1 = time.perf_counter()
+    return n, t1 - t0, (sampler.stop(t0, t1) if sampler else None)
+
+
 def ceilings(which=("mfma", "stream")) -> dict:
-    """MFMA-loop and streaming-read rates measured now, on this GPU."""
+    """MFMA and streaming-read rates measured now, on this GPU."""
     import torch
     lib = _calib_lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = {"compute_units": cus}
     if "mfma" in which:
-        blocks = 2 * cus  # two blocks of four wavefronts per CU: two per SIMD
+        # the GEMM's k16-step MFMA pattern, one wavefront per SIMD, each probe
+        # sustained for about a second (long enough for the clock to settle)
+        sampler = PowerSampler()
+        blocks = cus
         sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-        for name, fn, iters, flop in (("mfma_bf16_loop_tflops", lib.moe_calib_mfma_bf16, 20000, 32 * 32 * 16 * 2),
-                                      ("mfma_fp8_loop_tflops", lib.moe_calib_mfma_fp8, 20000, 32 * 32 * 64 * 2)):
-            def launch(fn=fn, iters=iters):
-                rc = fn(blocks, iters, ctypes.c_void_p(sink.data_ptr()), stream)
-                if rc != 0:
-                    raise RuntimeError(f"calibration launch failed: hipError {rc}")
-            ms = _timed(launch, 5)
-            out[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
-        out["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts, 4 independent 32x32 accumulator chains each, "
-                             "register operands (calib/ceilings.hip)")
+        power = {}
+        for name, fn, iters, flop in (("bf16", lib.moe_calib_mfma_bf16_gemm, 3000, 32 * 32 * 16 * 2),
+                                      ("fp8", lib.moe_calib_mfma_fp8_gemm, 1500, 32 * 32 * 64 * 2)):
+            for const in (0, 1):
+                def launch(fn=fn, iters=iters, const=const):
+                    rc = fn(blocks, iters, const, ctypes.c_void_p(sink.data_ptr()), stream)
+                    if rc != 0:
+                        raise RuntimeError(f"calibration launch failed: hipError {rc}")
+                n, secs, pw = _sustained(launch, 1.0, sampler)
+                key = f"mfma_{name}_{'constant' if const else 'random'}_tflops"
+                out[key] = round(n * blocks * 4 * iters * 32 * flop / secs / 1e12, 1)
+                power[key] = pw
+        out["mfma_power"] = power
+        out["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts (one per SIMD), a 4 x 4 grid of 32x32 accumulators "
+                             "fed from two alternating register sets, random or constant operands, each sustained "
+                             "~1 s (calib/ceilings.hip)")
     if "stream" in which:
         nbytes = 4 << 30
         src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
@@ -244,6 +343,9 @@ def ceilings(which=("mfma", "stream")) -> dict:
                 raise RuntimeError(f"calibration launch failed: hipError {rc}")
         ms = _timed(launch, 5)
         out["stream_read_gbs"] = round(read.value / (ms * 1e-3) / 1e9, 1)
+        n, secs, pw = _sustained(launch, 1.0, PowerSampler())
+        out["stream_read_sustained_gbs"] = round(n * read.value / secs / 1e9, 1)
+        out["stream_power"] = pw
         out["stream_probe"] = (f"{read.value >> 20} MiB read by {blocks} blocks, one contiguous chunk each, "
                                "16-byte loads, 8 in flight per thread (calib/ceilings.hip)")
         del src
@@ -496,6 +598,15 @@ def measure(w, seed, args, keep_host=False, steps=None, warmup=None, cold=True):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
 
+    sustained = None
+    if args.sustain_seconds > 0:
+        # the step over and over for a few seconds, outside the timed region:
+        # the rate once power management has settled, with the socket power
+        # and graphics clock meanwhile
+        n, secs, pw = _sustained(step, args.sustain_seconds, PowerSampler())
+        sustained = {"steps": n, "seconds": round(secs, 3), "ms_per_step": round(secs * 1e3 / n, 4),
+                     "tokens_per_s": round(w.T * n / secs, 1), "power": pw}
+
     cold_rec = None
     if cold and not args.no_cold:
         # cold-cache repetitions, outside the timed region: the eviction
@@ -590,6 +701,7 @@ def measure(w, seed, args, keep_host=False, steps=None, warmup=None, cold=True):
         "capacity": {"factor": w.capacity_factor, "slots_per_expert": cap,
                      "overflow": w.overflow, "dropped_fraction": round(1.0 - n_assign / (w.T * w.k), 5),
                      "rerouted_fraction": round((n_assign - own_kept) / (w.T * w.k), 5)},
+        "sustained": sustained,
         "cold_cache": cold_rec,
     }
     del dev, out, idx, gw, counts, ws
@@ -646,7 +758,7 @@ def main():
         ceil = ceilings()
         r = line["roofline"]
         if r["bound"] == "mfma":
-            key = "mfma_fp8_loop_tflops" if r["mfma_dtype"] == "fp8" else "mfma_bf16_loop_tflops"
+            key = f"mfma_{r['mfma_dtype']}_random_tflops"  # random operands, like the layer's data
             r["frac_of_measured_mfma_ceiling"] = round(r["achieved"] / ceil[key], 4)
         else:
             r["frac_of_measured_read_ceiling"] = round(r["achieved"] / ceil["stream_read_gbs"], 4)
@@ -672,7 +784,7 @@ def main():
                           "value": d_rec["value"], "unit": "tokens/s", "steps": 4 * args.steps,
                           "ms_per_step": d_rec["ms_per_step"], "config": d_rec["config"], "roofline": r,
                           "stages_us": d_rec["stages_us"], "stages_gbps": d_rec["stages_gbps"],
-                          "load": d_rec["load"]}
+                          "load": d_rec["load"], "sustained": d_rec["sustained"]}
     print(json.dumps(line))
 
 

@@ -1,10 +1,14 @@
 // Ceiling probes for the bench's roofline figures, kept apart from the layer
 // library (libmoe_calib.so, loaded only by bench.py).  Each measures what one
 // gfx950 unit sustains with nothing else in the way:
-//   * a register-only loop of bf16 MFMAs (v_mfma_f32_32x32x16_bf16), four
-//     independent accumulator chains per wavefront, four wavefronts per block;
-//   * the same with the block-scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4,
-//     E4M3 operands, unit scales);
+//   * the MFMA pattern of the prefill GEMM's k16 step on its own: one
+//     wavefront per SIMD (one block of four per CU), a 4 x 4 grid of 32x32
+//     accumulators, operands from two alternating register sets of 4 weight and
+//     4 activation fragments, in bf16 (v_mfma_f32_32x32x16_bf16) or fp8
+//     (v_mfma_scale_f32_32x32x64_f8f6f4); with random operand values (the
+//     MFMA's power, and so the clock the chip holds, depends on how the
+//     operand bits toggle: a loop on constant operands runs at full clock,
+//     one on random data does not) or constant ones;
 //   * a streaming read: each block reads one contiguous chunk with 16-byte
 //     loads, consecutive lanes on consecutive 16-byte pieces.
 // Results are folded into one value per thread and stored only if it equals
@@ -21,47 +25,86 @@ typedef uint32_t c_u32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChains = 4;
 
-__global__ __launch_bounds__(kThreads) void mfma_bf16_loop(int iters, float* sink) {
-  const int t = threadIdx.x;
-  c_bf16x8 a, b;
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(1.0f + 0.001f * float((t + i) & 15));
-    b[i] = (__bf16)(0.5f - 0.001f * float((t * 3 + i) & 15));
-  }
-  c_f32x16 acc[kChains];
-  for (int c = 0; c < kChains; ++c)
-    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
-  }
-  float s = 0.0f;
-  for (int c = 0; c < kChains; ++c)
-    for (int i = 0; i < 16; ++i) s += acc[c][i];
-  if (s == -1.2345e-30f) sink[blockIdx.x * kThreads + t] = s;
+// A 32-bit mix of the thread and register index (the "lowbias32" integer
+// hash): the operand values of the GEMM-shaped probes.
+__device__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
 }
 
-__global__ __launch_bounds__(kThreads) void mfma_fp8_loop(int iters, float* sink) {
-  const int t = threadIdx.x;
-  c_i32x8 a, b;
-  for (int i = 0; i < 8; ++i) {  // E4M3 bytes of moderate normal values
-    a[i] = int(0x38383838u + uint32_t((t + i) & 3));
-    b[i] = int(0x30303030u + uint32_t((t * 5 + i) & 3));
-  }
-  c_f32x16 acc[kChains];
-  for (int c = 0; c < kChains; ++c)
-    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+// bf16 operands: random values in [-2, 2) unless `constant`.
+__global__ __launch_bounds__(kThreads, 1) void mfma_bf16_gemm_shape(int iters, int constant, float* sink) {
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  c_bf16x8 w[2][4], x[2][4];
+  for (int s = 0; s < 2; ++s)
+    for (int q = 0; q < 4; ++q)
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t r = mix32(t * 977u + s * 131u + q * 17u + i + 1u);
+        w[s][q][i] = (__bf16)(constant ? 1.0f : float(int(r & 0xffff) - 32768) / 16384.0f);
+        x[s][q][i] = (__bf16)(constant ? 0.5f : float(int(r >> 16) - 32768) / 16384.0f);
+      }
+  c_f32x16 acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[s][i], x[s][j], acc[i][j], 0, 0, 0);
   }
-  float s = 0.0f;
-  for (int c = 0; c < kChains; ++c)
-    for (int i = 0; i < 16; ++i) s += acc[c][i];
-  if (s == -1.2345e-30f) sink[blockIdx.x * kThreads + t] = s;
+  float v = 0.0f;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) v += acc[i][j][q];
+  if (v == -1.2345e-30f) sink[t] = v;
+}
+
+// fp8 operands: random finite E4M3 codes (a NaN code 0x7f / 0xff becomes
+// 0x7e / 0xfe) unless `constant`; unit block scales.
+__global__ __launch_bounds__(kThreads, 1) void mfma_fp8_gemm_shape(int iters, int constant, float* sink) {
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  c_i32x8 w[2][4], x[2][4];
+  auto code4 = [&](uint32_t r) {
+    uint32_t o = 0;
+    for (int b = 0; b < 4; ++b) {
+      uint32_t c = (r >> (8 * b)) & 0xffu;
+      if ((c & 0x7fu) == 0x7fu) c ^= 1u;
+      o |= c << (8 * b);
+    }
+    return int(o);
+  };
+  for (int s = 0; s < 2; ++s)
+    for (int q = 0; q < 4; ++q)
+      for (int i = 0; i < 8; ++i) {
+        w[s][q][i] = constant ? int(0x38383838u) : code4(mix32(t * 977u + s * 131u + q * 17u + i + 1u));
+        x[s][q][i] = constant ? int(0x30303030u) : code4(mix32(t * 1009u + s * 137u + q * 19u + i + 7u));
+      }
+  c_f32x16 acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[s][i], x[s][j], acc[i][j], 0, 0, 0, 127, 0, 127);
+  }
+  float v = 0.0f;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) v += acc[i][j][q];
+  if (v == -1.2345e-30f) sink[t] = v;
 }
 
 // Block b reads bytes [b * chunk, (b + 1) * chunk); chunk is a multiple of
@@ -86,21 +129,19 @@ __global__ __launch_bounds__(kThreads) void stream_read(const c_u32x4* src, long
 
 extern "C" {
 
-// flop of one launch: blocks * 4 wavefronts * iters * 4 chains * 32*32*16*2.
-// sink: device, blocks * 256 floats (written only in the impossible case).
-// 0 on success, else the hipError_t of the launch.
-int moe_calib_mfma_bf16(int blocks, int iters, float* sink, void* stream) {
+// GEMM-shaped probes.  flop of one launch: blocks * 4 wavefronts * iters *
+// 32 MFMAs * (32*32*16*2 for bf16, 32*32*64*2 for fp8); constant != 0 runs
+// constant operands, else random ones.  sink: device, blocks * 256 floats.
+int moe_calib_mfma_bf16_gemm(int blocks, int iters, int constant, float* sink, void* stream) {
   if (blocks <= 0 || iters <= 0 || sink == nullptr) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL(mfma_bf16_loop, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), iters,
-                     sink);
+  hipLaunchKernelGGL(mfma_bf16_gemm_shape, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), iters,
+                     constant, sink);
   return int(hipGetLastError());
 }
-
-// flop of one launch: blocks * 4 wavefronts * iters * 4 chains * 32*32*64*2.
-int moe_calib_mfma_fp8(int blocks, int iters, float* sink, void* stream) {
+int moe_calib_mfma_fp8_gemm(int blocks, int iters, int constant, float* sink, void* stream) {
   if (blocks <= 0 || iters <= 0 || sink == nullptr) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL(mfma_fp8_loop, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), iters,
-                     sink);
+  hipLaunchKernelGGL(mfma_fp8_gemm_shape, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), iters,
+                     constant, sink);
   return int(hipGetLastError());
 }
 

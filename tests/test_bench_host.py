@@ -73,3 +73,11 @@ def test_summarize_counters_timed_dispatches(tmp_path, capsys):
     assert "| SQ_VALU_MFMA_BUSY_CYCLES | 393216 |" in out  # mean of 512 and 256 (x1024)
     assert "MFMA busy" in out and "| 38.4 |" in out
     assert "TA busy" in out and "| 25 |" in out
+
+
+def test_power_summary_window_and_unavailable_readings():
+    # (time s, socket W, gfx MHz); 0xffff marks a reading the metrics table lacks
+    samples = [(0.0, 900, 2400), (1.0, 1390, 1700), (1.5, 1400, 1600), (2.0, 0xffff, 1650), (3.5, 500, 2400)]
+    r = bench.PowerSampler.summarize(samples, 0.5, 3.0, cap_w=1400.0)
+    assert r == {"socket_power_w_median": 1395.0, "gfxclk_mhz_median": 1650.0, "power_cap_w": 1400.0, "samples": 3}
+    assert bench.PowerSampler.summarize(samples, 5.0, 6.0) is None
