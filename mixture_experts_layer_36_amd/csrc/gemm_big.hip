@@ -272,11 +272,13 @@ struct OutTile {
 //     dead by then: every wave has read its last fragments.
 //   * A piece stores its raw accumulators to its partial slot, register-major
 //     so that each 16-byte store of a wave is contiguous.
-// Both are handled block by block in one pass.
+// Both are handled block by block in one pass.  lds_sc: the tile's fp8
+// channel scales, staged in LDS by the prologue (stage_scales): BN of them
+// (SwiGLU: BN/2 of W1, then BN/2 of W3).
 template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
                                             f32x16 (&acc)[BigCfg<BN, WN, LAY>::TW][BigCfg<BN, WN, LAY>::TA],
-                                            int ncol0, char* lds, int slot) {
+                                            int ncol0, char* lds, int slot, const float* lds_sc) {
   using C = BigCfg<BN, WN, LAY>;
   using O = OutTile<BN, EPI>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -308,8 +310,8 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
       const int lcol = wcol + i * 32 + g * 8 + (lane >> 5) * 4;
       float4 su = make_float4(1.f, 1.f, 1.f, 1.f), sv = su;
       if (scaled) {
-        su = *(const float4*)(sg.s0 + ncol0 + lcol);
-        if (EPI == EPI_SWIGLU) sv = *(const float4*)(sg.s1 + ncol0 + lcol);
+        su = *(const float4*)(lds_sc + lcol);
+        if (EPI == EPI_SWIGLU) sv = *(const float4*)(lds_sc + BN / 2 + lcol);
       }
       const float s4u[4] = {su.x, su.y, su.z, su.w}, s4v[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
@@ -344,12 +346,16 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
   const int rows = ti.nrows;
   if (sg.c_prows) {
     // K-blocked C: the tile's 32-column planes in turn, each a contiguous run
-    // of rows x 64 bytes (4 chunks per row)
-    for (int u = tid; u < rows * O::CPR; u += C::NTHR) {
-      const int p = u / (rows * 4), rem = u % (rows * 4), r = rem >> 2, ch = p * 4 + (rem & 3);
-      const u32x4 v = *(const u32x4*)(lds + r * O::ROW_BYTES + ((ch ^ (r & 15)) << 4));
-      if (ncol0 + p * 32 < sg.N)
-        *(u32x4*)((uint16_t*)sg.C + ((size_t)(ncol0 / 32 + p) * sg.c_prows + ti.row0 + r) * 32 + (rem & 3) * 8) = v;
+    // of rows x 64 bytes (4 chunks per row): chunk q of a plane's run is row
+    // q / 4, chunk q % 4, at element 8 q of the run
+#pragma unroll
+    for (int p = 0; p < O::CPR / 4; ++p) {
+      if (ncol0 + p * 32 >= sg.N) break;
+      uint16_t* run = (uint16_t*)sg.C + ((size_t)(ncol0 / 32 + p) * sg.c_prows + ti.row0) * 32;
+      for (int q = tid; q < rows * 4; q += C::NTHR) {
+        const int r = q >> 2, ch = p * 4 + (q & 3);
+        *(u32x4*)(run + q * 8) = *(const u32x4*)(lds + r * O::ROW_BYTES + ((ch ^ (r & 15)) << 4));
+      }
     }
     return;
   }
@@ -360,10 +366,28 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
   }
 }
 
+// The fp8 channel scales of a whole tile's columns into LDS (lds_sc, BN
+// floats; SwiGLU: BN/2 of W1 then BN/2 of W3), one dword direct load per
+// lane, issued before the tile's first stage so the prologue's wait for
+// stage 0 covers it; columns past N read 0 (the descriptor's bound).  The
+// epilogue then reads them from LDS instead of waiting on global loads.
+template <int BN, int EPI, int NTHR>
+__device__ __forceinline__ void stage_scales(const Seg& sg, int ncol0, float* lds_sc, int wave) {
+  constexpr int HALF = BN / 2;
+  if (wave * 64 >= BN) return;
+  const bool w3 = EPI == EPI_SWIGLU && wave * 64 >= HALF;
+  const float* src = (w3 ? sg.s1 : sg.s0) + ncol0;
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(src, (sg.N - ncol0) * 4);
+  const int c0 = (EPI == EPI_SWIGLU && w3) ? wave * 64 - HALF : wave * 64;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds_sc + wave * 64), 4,
+                                           (uint32_t)((c0 + (int)(threadIdx.x & 63)) * 4), 0, 0, 0);
+  static_assert(BN <= NTHR, "one scale per thread");
+}
+
 // One tile (or K-piece of a tile) in the full, half or quarter layout.
 template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
-                                         int ncol0, char* lds) {
+                                         int ncol0, char* lds, float* lds_sc) {
   using C = BigCfg<BN, WN, LAY>;
   using M = BigMem<BN, WN, LAY, WDT>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -562,6 +586,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     });
   };
   constexpr int NG = NDS;  // groups per step
+  const bool scaled = WDT == GD_FP8 && EPI != EPI_BIAS_F32 && sg.s0 != nullptr && wk.slot < 0;
+  if (scaled) stage_scales<BN, EPI, C::NTHR>(sg, ncol0, lds_sc, wave);
   issue_part(0, 0, 0); issue_part(0, 0, 1);
   issue_part(1, 1, 0); issue_part(1, 1, 1);
   issue_part(2, 2, 0); issue_part(2, 2, 1);
@@ -616,7 +642,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   if constexpr (EPI == EPI_BIAS_F32)  // router logits: never split (K ranges go to blockIdx.y)
     store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, LAY, EPI>(wave), lane);
   else
-    finish_tile<BN, WN, EPI, LAY, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot);
+    finish_tile<BN, WN, EPI, LAY, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
 }
 #endif
 
@@ -627,7 +653,10 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int RING = STAGES * BigMem<BN, WN, 0, WDT>::STAGE_BYTES;
   constexpr int OUT = (EPI == EPI_BIAS_F32) ? 0 : OutTile<BN, EPI>::BYTES;
-  __shared__ __attribute__((aligned(1024))) char lds[RING > OUT ? RING : OUT];
+  constexpr int MAIN = RING > OUT ? RING : OUT;
+  constexpr int SC = (WDT == GD_FP8 && EPI != EPI_BIAS_F32) ? BN * 4 : 0;  // the tile's channel scales
+  __shared__ __attribute__((aligned(1024))) char lds[MAIN + SC];
+  float* lds_sc = (float*)(lds + MAIN);
   Work wk;
   if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
@@ -636,9 +665,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
   switch (tile_layout(ti.nrows)) {
-    case 2: big_tile<BN, WN, EPI, 2, WDT>(a, ti, sg, wk, ncol0, lds); break;
-    case 1: big_tile<BN, WN, EPI, 1, WDT>(a, ti, sg, wk, ncol0, lds); break;
-    default: big_tile<BN, WN, EPI, 0, WDT>(a, ti, sg, wk, ncol0, lds);
+    case 2: big_tile<BN, WN, EPI, 2, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    case 1: big_tile<BN, WN, EPI, 1, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    default: big_tile<BN, WN, EPI, 0, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc);
   }
 #endif
 }
@@ -660,40 +689,26 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
 // refilled once per 8 stages; K-pieces of split tiles start on chunk
 // boundaries.
 //
-// A stage's 4 x 4 grid of 32x32 blocks runs in four quarters (weight half,
-// activation half): (lo, lo), (lo, hi), (hi, hi), (hi, lo).  The fragments
-// of the first quarter are in registers when the stage starts; the other
-// halves of this stage are read during the first two quarters, then every
-// wave passes the barrier (all of this stage read, the next stage landed)
-// and the next stage's lo halves are read during the last two, so LDS reads
-// stay spread over the MFMAs.
+// A stage (k = 64) is one step of TW x TA block-scaled MFMAs, laid out like
+// a k16 step of the bf16 pipeline: groups of MFMAs, each followed by its
+// share of the direct loads and of the next stage's fragment reads (full
+// fragment sets double-buffered in registers).  The first groups issue the B
+// refill, then the barrier, then the A refill and the reads (Qwen-shaped
+// fp8 x fp8 gate-up 918 -> 904 us against a schedule of four quarters with
+// the loads issued four at a time).
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BK8 = 64;            // k per stage of the fp8 x fp8 path
 [[maybe_unused]] constexpr int SC_STAGES = 8;       // stages per 16-byte chunk of scales
 [[maybe_unused]] constexpr int SC_BYTES = BM * 16;  // one chunk for every row of a tile
 
-// Spread ND LDS reads and NV direct loads over the NM MFMAs of a quarter.
-template <int NM, int ND, int NV>
-__device__ __forceinline__ void sched_quarter() {
-  constexpr int dpm = (ND + NM - 1) / NM, vpm = (NV + NM - 1) / NM;
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (dpm > 0) __builtin_amdgcn_sched_group_barrier(0x100, dpm, 0);
-    if (vpm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vpm, 0);
-  }
-}
-
 #if defined(__HIP_DEVICE_COMPILE__)
 template <int BN, int WN, int EPI, int LAY>
 __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
-                                             int ncol0, char* lds) {
+                                             int ncol0, char* lds, float* lds_sc) {
   using C = BigCfg<BN, WN, LAY>;
   using M = BigMem<BN, WN, LAY, GD_BF16>;  // 64-byte rows on both operands: the bf16 stage geometry
   static_assert(C::NTHR == BM, "one scale row per thread");
-  constexpr int TW2 = C::TW / 2, TA2 = C::TA / 2;
-  static_assert(TW2 >= 1 && TA2 >= 1, "quarters");
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = sg.K;  // bytes per row of either operand
@@ -807,8 +822,53 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, x, acc[i][j], 0, 0, 0, 127, 0, sb);
   };
 
-  i32x8 WL[2][TW2], XL[2][TA2], WH[TW2], XH[TA2];
-  // prologue: scale chunk 0, stages 0..2 and the A part of stage 3
+  // Fragments of one stage (k = 64): the wave's weight and activation
+  // blocks, 32 bytes of a row per lane.  F[st & 1] holds stage st's.
+  struct Frags8 {
+    i32x8 w[C::TW], x[C::TA];
+  };
+  constexpr int NMF = C::TW * C::TA, NDS = C::TW + C::TA;  // MFMAs and fragments per stage
+  constexpr int NG = NDS;                                  // groups per stage
+  constexpr int BG = 2;                                    // groups before the barrier
+  static_assert(BG >= 1 && BG < NG, "barrier group");
+  // fragment q of a stage in the order the MFMAs (i-major) consume them:
+  // w0, every x, then w1 ..
+  auto read_one = [&](Frags8& F, const char* L, auto IDX) {
+    constexpr int qq = decltype(IDX)::value;
+    constexpr int q = qq == 0 ? 0 : qq <= C::TA ? C::TW + qq - 1 : qq - C::TA;
+    if constexpr (q < C::TW) F.w[q] = wfrag(L, q);
+    else F.x[q - C::TW] = xfrag(L, q - C::TW);
+  };
+  auto load_one = [&](int kt, int buf, int part, auto JDX) {
+    constexpr int jj = decltype(JDX)::value;
+    char* st = lds + buf * M::STAGE_BYTES;
+    const int ks = kt0 + min(kt, KT - 1);
+    if (part == 0) {
+      if constexpr (jj < M::A_LOADS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + jj) * 1024), 16, a_off[jj], ks * BK8, 0, 0);
+    } else {
+      if constexpr (jj < M::B_LOADS) {
+        const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + jj) * 1024);
+        if (b_w3[jj])
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[jj], ks * b_step, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[jj], ks * b_step, 0, 0);
+      }
+    }
+  };
+  auto mfma_range = [&](const Frags8& F, const int (&sb)[C::TA], auto LO, auto HI) {
+    static_for<decltype(LO)::value, decltype(HI)::value>([&](auto MI) {
+      constexpr int m = decltype(MI)::value;
+      constexpr int i = m / C::TA, j = m % C::TA;
+      mf(i, j, F.w[i], F.x[j], sb[j]);
+    });
+  };
+
+  // prologue: the channel scales, scale chunk 0, stages 0..2 and the A part
+  // of stage 3
+  const bool scaled = sg.s0 != nullptr && wk.slot < 0;
+  if (scaled) stage_scales<BN, EPI, C::NTHR>(sg, ncol0, lds_sc, wave);
   issue_scales(0);
   issue_part(0, 0, 0); issue_part(0, 0, 1);
   issue_part(1, 1, 0); issue_part(1, 1, 1);
@@ -817,76 +877,55 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
   wait_vmcnt<2 * M::LOADS + M::A_LOADS>();  // scale chunk 0 and stage 0 done
   barrier_only();
   read_scales(0);
-#pragma unroll
-  for (int i = 0; i < TW2; ++i) WL[0][i] = wfrag(lds, i);
-#pragma unroll
-  for (int j = 0; j < TA2; ++j) XL[0][j] = xfrag(lds, j);
+  Frags8 F[2];
+  static_for<0, NDS>([&](auto Q) { read_one(F[0], lds, Q); });
 
   // Stage kt is in ring buffer kt % 4 = st % 4 (chunks are 8 stages), so
-  // every LDS address below is a constant offset.  Waits and refills are
-  // those of the bf16 pipeline; a scale chunk load adds one more load to
-  // some waits' windows, which only makes them wait a little longer.
+  // every LDS address is a constant.  A stage is laid out as NG groups, each
+  // fenced so the compiler keeps the order: a group's MFMAs on F[st & 1],
+  // then its share of the direct loads and of the next stage's fragment
+  // reads.  The first BG groups issue the B part of stage kt+3 (into buffer
+  // (kt+3) % 4, whose stage every wave had read before the previous barrier);
+  // then this wave's loads of stage kt+1 have landed and a barrier (every wave
+  // holds this stage's fragments, so buffer kt % 4 is free); the remaining
+  // groups issue the A part of stage kt+4 into buffer kt % 4 and read stage
+  // kt+1's fragments into F[(st + 1) & 1].  Waits are those of the bf16
+  // pipeline; a scale chunk load adds one more load to some waits' windows,
+  // which only makes them wait a little longer.
   for (int c = 0; c < NC; ++c) {
     static_for<0, SC_STAGES>([&](auto ST) {
       constexpr int st = decltype(ST)::value, p = st & 1;
       const int kt = c * SC_STAGES + st;
       if (kt >= KT) return;
-      const char* L = lds + (st % STAGES) * M::STAGE_BYTES;
       const char* Ln = lds + ((st + 1) % STAGES) * M::STAGE_BYTES;
+      constexpr int bb = (st + 3) % STAGES, ba = st % STAGES;
       int sb[C::TA];
 #pragma unroll
       for (int j = 0; j < C::TA; ++j) sb[j] = (int)((SC[j][st >> 1] >> (16 * (st & 1) + 8 * h)) & 0xffu);
       if (st == 0) issue_scales(c + 1);
-      // (lo, lo): read this stage's activation hi half; B part of stage kt+3
-      issue_part(kt + 3, (st + 3) % STAGES, 1);
-#pragma unroll
-      for (int j = 0; j < TA2; ++j) XH[j] = xfrag(L, TA2 + j);
-#pragma unroll
-      for (int i = 0; i < TW2; ++i)
-#pragma unroll
-        for (int j = 0; j < TA2; ++j) mf(i, j, WL[p][i], XL[p][j], sb[j]);
-      sched_quarter<TW2 * TA2, 2 * TA2, M::B_LOADS>();
       __builtin_amdgcn_sched_barrier(0);
-      // (lo, hi): read this stage's weight hi half
-#pragma unroll
-      for (int i = 0; i < TW2; ++i) WH[i] = wfrag(L, TW2 + i);
-#pragma unroll
-      for (int i = 0; i < TW2; ++i)
-#pragma unroll
-        for (int j = 0; j < TA2; ++j) mf(i, TA2 + j, WL[p][i], XH[j], sb[TA2 + j]);
-      sched_quarter<TW2 * TA2, 2 * TW2, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      // this stage read everywhere, stage kt+1 resident: A part of stage
-      // kt+4 into this buffer
+      static_for<0, BG>([&](auto G) {
+        constexpr int g = decltype(G)::value;
+        mfma_range(F[p], sb, IC<g * NMF / NG>{}, IC<(g + 1) * NMF / NG>{});
+        static_for<g * M::B_LOADS / BG, (g + 1) * M::B_LOADS / BG>([&](auto J) { load_one(kt + 3, bb, 1, J); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       wait_vmcnt<2 * M::LOADS>();
       barrier_only();
       __builtin_amdgcn_sched_barrier(0);
-      issue_part(kt + 4, st % STAGES, 0);
-      // (hi, hi): next stage's weight lo half
-#pragma unroll
-      for (int i = 0; i < TW2; ++i) WL[p ^ 1][i] = wfrag(Ln, i);
-#pragma unroll
-      for (int i = 0; i < TW2; ++i)
-#pragma unroll
-        for (int j = 0; j < TA2; ++j) mf(TW2 + i, TA2 + j, WH[i], XH[j], sb[TA2 + j]);
-      sched_quarter<TW2 * TA2, 2 * TW2, M::A_LOADS>();
-      __builtin_amdgcn_sched_barrier(0);
-      // (hi, lo): next stage's activation lo half (and, at a chunk's end,
-      // the next chunk's scales)
-#pragma unroll
-      for (int j = 0; j < TA2; ++j) XL[p ^ 1][j] = xfrag(Ln, j);
-      if (st == SC_STAGES - 1) read_scales(c + 1);
-#pragma unroll
-      for (int i = 0; i < TW2; ++i)
-#pragma unroll
-        for (int j = 0; j < TA2; ++j) mf(TW2 + i, j, WH[i], XL[p][j], sb[j]);
-      sched_quarter<TW2 * TA2, 2 * TA2 + (st == SC_STAGES - 1 ? C::TA : 0), 0>();
-      __builtin_amdgcn_sched_barrier(0);
+      static_for<BG, NG>([&](auto G) {
+        constexpr int g = decltype(G)::value, q0 = g - BG, NP = NG - BG;
+        mfma_range(F[p], sb, IC<g * NMF / NG>{}, IC<(g + 1) * NMF / NG>{});
+        static_for<q0 * M::A_LOADS / NP, (q0 + 1) * M::A_LOADS / NP>([&](auto J) { load_one(kt + 4, ba, 0, J); });
+        static_for<q0 * NDS / NP, (q0 + 1) * NDS / NP>([&](auto R) { read_one(F[p ^ 1], Ln, R); });
+        if constexpr (g == NG - 1 && st == SC_STAGES - 1) read_scales(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
-  finish_tile<BN, WN, EPI, LAY, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot);
+  finish_tile<BN, WN, EPI, LAY, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
 }
 #endif
 
@@ -895,8 +934,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
                                                                     int n_cu) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(OutTile<BN, EPI>::BYTES <= STAGES * BigMem<BN, WN, 0, GD_BF16>::STAGE_BYTES, "LDS");
-  __shared__ __attribute__((aligned(1024))) char lds[STAGES * BigMem<BN, WN, 0, GD_BF16>::STAGE_BYTES +
-                                                     2 * SC_BYTES];
+  constexpr int MAIN = STAGES * BigMem<BN, WN, 0, GD_BF16>::STAGE_BYTES + 2 * SC_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[MAIN + BN * 4];  // + the tile's channel scales
+  float* lds_sc = (float*)(lds + MAIN);
   Work wk;
   if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
@@ -905,9 +945,9 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
   switch (tile_layout(ti.nrows)) {
-    case 2: big_tile_fp8<BN, WN, EPI, 2>(a, ti, sg, wk, ncol0, lds); break;
-    case 1: big_tile_fp8<BN, WN, EPI, 1>(a, ti, sg, wk, ncol0, lds); break;
-    default: big_tile_fp8<BN, WN, EPI, 0>(a, ti, sg, wk, ncol0, lds);
+    case 2: big_tile_fp8<BN, WN, EPI, 2>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    case 1: big_tile_fp8<BN, WN, EPI, 1>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    default: big_tile_fp8<BN, WN, EPI, 0>(a, ti, sg, wk, ncol0, lds, lds_sc);
   }
 #endif
 }
