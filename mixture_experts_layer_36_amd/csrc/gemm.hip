@@ -269,30 +269,70 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a, int n_slots, 
 }
 
 // ============================================================== tile tables
+// Inclusive prefix sum over the 512 threads of v, through LDS.
+__device__ __forceinline__ int block_scan512(int* buf, int v) {
+  const int e = threadIdx.x;
+  buf[e] = v;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    const int u = (e >= off) ? buf[e - off] : 0;
+    __syncthreads();
+    buf[e] += u;
+    __syncthreads();
+  }
+  const int r = buf[e];
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(512) void tile_table_kernel(TileTableArgs t) {
-  __shared__ int pre[2][512];
+  __shared__ int pre[512];
+  __shared__ int tot[3];
   const int e = threadIdx.x;
   const int cnt = (e < t.E) ? t.offsets[e + 1] - t.offsets[e] : 0;
   for (int w = 0; w < 2; ++w) {
     const int bm = w == 0 ? t.bm0 : t.bm1;
     if (bm == 0) break;
-    const int tiles = (cnt + bm - 1) / bm;
-    pre[w][e] = tiles;
-    __syncthreads();
-    for (int off = 1; off < 512; off <<= 1) {
-      const int v = (e >= off) ? pre[w][e - off] : 0;
-      __syncthreads();
-      pre[w][e] += v;
-      __syncthreads();
-    }
-    const int incl = pre[w][e], total = pre[w][511];
     int32_t* table = w == 0 ? t.table0 : t.table1;
     const int n_slots = w == 0 ? t.n_slots0 : t.n_slots1;
-    for (int i = 0; i < tiles; ++i) table[incl - tiles + i] = (e << kTableExpertShift) | i;
-    const int sh_tiles = (t.sh_rows + bm - 1) / bm;  // the extra segment E, after the experts
-    for (int i = e; i < sh_tiles; i += 512) table[total + i] = (t.E << kTableExpertShift) | i;
-    for (int s = total + sh_tiles + e; s < n_slots; s += 512) table[s] = -1;
-    if (e == 0) table[n_slots] = total + sh_tiles;  // real m-tiles, read by every GEMM block
+    const int sh_tiles = (t.sh_rows + bm - 1) / bm;  // the extra segment E
+    int total;
+    if (bm == 256) {
+      // Tiles by cost, so the launch ends on its cheapest tiles and the
+      // XCDs are dealt tiles of like cost together: every expert's tiles
+      // that run the full layout (more than 128 rows), then the extra
+      // segment's, then the half-height last tiles (65-128 rows), then the
+      // quarter-height ones (1-64 rows); experts in order within each class.
+      // The split plan's K-pieces then come from the cheap tiles at the end.
+      // Same box: Qwen-shaped fp8-weight layer gate-up -5.5%, down -8.1%;
+      // DeepSeek-V3-shaped prefill gate-up -2.9%; Mixtral-shaped unchanged.
+      const int rem = cnt % 256;
+      const int nf = cnt / 256 + (rem > 128 ? 1 : 0);
+      const int nh = (rem > 64 && rem <= 128) ? 1 : 0, nq = (rem > 0 && rem <= 64) ? 1 : 0;
+      // one scan for both one-per-expert classes: each count is at most 512
+      const int pf = block_scan512(pre, nf), phq = block_scan512(pre, nh | (nq << 16));
+      const int ph = phq & 0xffff, pq = phq >> 16;
+      if (e == 511) { tot[0] = pf; tot[1] = ph; tot[2] = pq; }
+      __syncthreads();
+      const int F = tot[0] + sh_tiles, H = tot[1], Q = tot[2];
+      for (int i = 0; i < nf; ++i) table[pf - nf + i] = (e << kTableExpertShift) | i;
+      for (int i = e; i < sh_tiles; i += 512) table[tot[0] + i] = (t.E << kTableExpertShift) | i;
+      if (nh) table[F + ph - 1] = (e << kTableExpertShift) | (cnt / 256);
+      if (nq) table[F + H + pq - 1] = (e << kTableExpertShift) | (cnt / 256);
+      total = F + H + Q;
+      __syncthreads();
+    } else {
+      const int tiles = (cnt + bm - 1) / bm;
+      const int incl = block_scan512(pre, tiles);
+      if (e == 511) tot[0] = incl;
+      __syncthreads();
+      for (int i = 0; i < tiles; ++i) table[incl - tiles + i] = (e << kTableExpertShift) | i;
+      for (int i = e; i < sh_tiles; i += 512) table[tot[0] + i] = (t.E << kTableExpertShift) | i;
+      total = tot[0] + sh_tiles;
+      __syncthreads();
+    }
+    for (int s = total + e; s < n_slots; s += 512) table[s] = -1;
+    if (e == 0) table[n_slots] = total;  // real m-tiles, read by every GEMM block
   }
 }
 
