@@ -198,7 +198,7 @@ def _calib_lib():
     for fn in (lib.moe_calib_mfma_bf16_gemm, lib.moe_calib_mfma_fp8_gemm):
         fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
-                                          ctypes.POINTER(ctypes.c_longlong), ctypes.c_void_p]
+                                          ctypes.POINTER(ctypes.c_longlong), ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -336,18 +336,22 @@ def ceilings(which=("mfma", "stream")) -> dict:
         sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
         read = ctypes.c_longlong(0)
 
-        def launch():
-            rc = lib.moe_calib_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, blocks,
-                                           ctypes.c_void_p(sink.data_ptr()), ctypes.byref(read), stream)
-            if rc != 0:
-                raise RuntimeError(f"calibration launch failed: hipError {rc}")
-        ms = _timed(launch, 5)
-        out["stream_read_gbs"] = round(read.value / (ms * 1e-3) / 1e9, 1)
-        n, secs, pw = _sustained(launch, 1.0, PowerSampler())
-        out["stream_read_sustained_gbs"] = round(n * read.value / secs / 1e9, 1)
-        out["stream_power"] = pw
+        for nt, key in ((0, "stream_read_plain_gbs"), (1, "stream_read_nt_gbs")):
+            def launch(nt=nt):
+                rc = lib.moe_calib_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, blocks,
+                                               ctypes.c_void_p(sink.data_ptr()), ctypes.byref(read), nt, stream)
+                if rc != 0:
+                    raise RuntimeError(f"calibration launch failed: hipError {rc}")
+            ms = _timed(launch, 5)
+            out[key] = round(read.value / (ms * 1e-3) / 1e9, 1)
+            n, secs, pw = _sustained(launch, 1.0, PowerSampler())
+            out[key.replace("_gbs", "_sustained_gbs")] = round(n * read.value / secs / 1e9, 1)
+            out[key.replace("_gbs", "_power")] = pw
+        # the ceiling: the faster of the two access kinds
+        out["stream_read_gbs"] = max(out["stream_read_plain_gbs"], out["stream_read_nt_gbs"])
         out["stream_probe"] = (f"{read.value >> 20} MiB read by {blocks} blocks, one contiguous chunk each, "
-                               "16-byte loads, 8 in flight per thread (calib/ceilings.hip)")
+                               "16-byte loads, 8 in flight per thread, plain and non-temporal "
+                               "(calib/ceilings.hip); stream_read_gbs is the faster")
         del src
     return out
 
