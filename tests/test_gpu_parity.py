@@ -36,6 +36,10 @@ CASES = {
     "dsv3_decode_small": DSV3_DECODE.scaled(T=40, d=512, f=256, E=64, f_shared=256),
     "decode_k128": DSV3_DECODE.scaled(T=24, d=128, f=128, E=16, f_shared=128),
     "decode_shared_wide": DSV3_DECODE.scaled(T=70, d=256, f=128, E=32, f_shared=384),
+    # the down projection's slices go four to a block: three slices (a
+    # partial group), and experts with more than one 32-row token block
+    "decode_d384": DSV3_DECODE.scaled(T=40, d=384, f=256, E=64, f_shared=256),
+    "decode_hot": DSV3_DECODE.scaled(T=200, d=512, f=256, E=64, f_shared=128),
     "dsv3_skew_small": DSV3_PREFILL_SKEW.scaled(T=300, d=384, f=256, E=64, f_shared=128),
     "qwen_fp8_small": QWEN_FP8_SKEW.scaled(T=260, d=256, f=384, E=32),
     # fp8 weights in the 256-row kernel: skewed tails (half tiles), K-split
