@@ -66,13 +66,25 @@ template <int EPI, int SPB>
 __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_slices) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) __bf16 lds[STAGES * STAGE];
-  // the shared segment (all T rows, several token blocks) is dispatched first
-  // so that its longer blocks do not end up in the tail of the launch
+  // the shared segment (all T rows, several token blocks) is dispatched
+  // first, one slice per block, so that its longer blocks neither end up in
+  // the tail of the launch nor grow into its critical path; then the routed
+  // segments, SPB slices per block
   const int has_sh = a.sh_rows > 0 ? 1 : 0;
   const int n_groups = (n_slices + SPB - 1) / SPB;
-  const int s0 = blockIdx.x / n_groups, grp = blockIdx.x % n_groups;
-  if (s0 >= a.E + has_sh) return;
-  const int seg = has_sh ? (s0 == 0 ? a.E : s0 - 1) : s0;
+  const int sh_blocks = has_sh ? n_slices : 0;
+  int seg, first, per;
+  if ((int)blockIdx.x < sh_blocks) {
+    seg = a.E;
+    first = blockIdx.x;
+    per = 1;
+  } else {
+    const int b = blockIdx.x - sh_blocks;
+    seg = b / n_groups;
+    if (seg >= a.E) return;
+    first = (b % n_groups) * SPB;
+    per = SPB;
+  }
 
   // segment operands
   const bool shared = seg == a.E;
@@ -110,9 +122,8 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_decode_kernel(GemmArgs a, int n_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KT = K / BK;
-  // the slices of this block: grp * SPB .. that + nsl - 1 (those inside N)
-  const int first = grp * SPB;
-  const int nsl = min(SPB, (N + ncol - 1) / ncol - first);
+  // the slices of this block: first .. first + nsl - 1 (those inside N)
+  const int nsl = min(per, (N + ncol - 1) / ncol - first);
   if (nsl <= 0) return;
 
   // weight rows of this slice: SwiGLU = 64 W1 rows then the same 64 W3 rows.
@@ -358,7 +369,8 @@ hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((gemm_decode_kernel<EPI_SWIGLU, 1>), dim3(n_seg * n_slices), dim3(NTHR), 0, s, a, n_slices);
   else
     hipLaunchKernelGGL((gemm_decode_kernel<EPI_STORE, kStoreSlices>),
-                       dim3(n_seg * ((n_slices + kStoreSlices - 1) / kStoreSlices)), dim3(NTHR), 0, s, a, n_slices);
+                       dim3((a.sh_rows > 0 ? n_slices : 0) + a.E * ((n_slices + kStoreSlices - 1) / kStoreSlices)),
+                       dim3(NTHR), 0, s, a, n_slices);
   return hipGetLastError();
 }
 
