@@ -8,20 +8,29 @@
 // batch").  This kernel is built for that regime:
 //   * block tile 256 activation rows x BN weight rows (BN = 256 or 128),
 //     BK = 32, four wavefronts in a 2 x 2 grid, so each wavefront owns a
-//     128 x (BN/2) tile: 16 (or 8) v_mfma_f32_32x32x16_bf16 per 8 (or 6)
-//     128-bit LDS fragment reads, with the accumulators in AGPRs;
+//     128 x (BN/2) tile as 16x16 blocks: per stage 64 (or 32)
+//     v_mfma_f32_16x16x32_bf16 on 16 (or 12) 128-bit LDS fragment reads,
+//     with the accumulators in AGPRs.  The 16x16x32 form does the same work
+//     per cycle as 32x32x16 but moves a quarter of the accumulator registers
+//     per MFMA: the GEMM-shaped MFMA loop alone on random bf16 operands
+//     sustains 2086 TFLOP/s against 1842 (MI355X, same power limit);
 //   * global -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a
-//     4-deep ring of 32 KB stages, refilled four stages ahead; each wave
-//     waits only for its own loads of the next stage (vmcnt) and a bare
-//     s_barrier publishes them, so later stages stay in flight;
-//   * the LDS fragments of the next k16 step are read while the current
-//     step's MFMAs run (two fragment sets), across the stage boundary too;
-//     each k16 step is laid out as groups of MFMAs, each followed by at most
-//     one direct load and one fragment read, fenced by sched_barrier so the
-//     compiler keeps that order: left to itself it sank a step's loads past
-//     all of its fragment reads and issued them in a burst beside the
-//     barrier (Mixtral-shaped gate-up 1944 -> 1774 us, down 928 -> 858 us;
-//     DeepSeek-shaped prefill down GEMM -5%);
+//     4-deep ring of 32 KB stages; each wave waits only for its own loads of
+//     the next stage (vmcnt) and a bare s_barrier publishes them, so later
+//     stages stay in flight;
+//   * a stage is one k32 step: its MFMAs run on fragments read during the
+//     previous stage (two fragment sets), laid out as groups of MFMAs, each
+//     followed by at most one direct load and a share of the next stage's
+//     fragment reads, fenced by sched_barrier so the compiler keeps that
+//     order: left to itself it sank a step's loads past all of its fragment
+//     reads and issued them in a burst beside the barrier.  The barrier
+//     comes two groups into the stage, after which the stage's buffer is
+//     free and is refilled with the stage four ahead: three stages of lead
+//     for every load (against the 32x32x16 two-step schedule: Qwen-shaped
+//     fp8-weight layer gate-up 1406 -> 1305 us and down 837 -> 776 us,
+//     Mixtral-shaped gate-up 1608 -> 1526 us and down 782 -> 721 us,
+//     DeepSeek-V3-shaped down 3758 -> 3688 us; its gate-up, at the power
+//     limit and on the load path, unchanged);
 //   * an expert's last tile with at most 128 (64) rows runs a half-height
 //     (quarter-height) layout: all four wavefronts on those rows, each with
 //     half the weight rows, so a short tail loads and multiplies only its
@@ -37,11 +46,13 @@
 //     gate-up GEMM runs both operands in fp8 on the block-scaled MFMA
 //     (big_tile_fp8 below);
 //   * LDS rows of BK elements with 16-byte chunks XOR-swizzled by row
-//     ((r >> 2) & 3 for 64-byte rows, (r ^ (r >> 3)) & 7 for 128-byte rows):
-//     measured on gfx950 (64 banks; a 128-bit read is served 16 lanes at a
-//     time), these make the fragment reads of 32 rows x 1 chunk
-//     conflict-free.  A direct load writes 64 consecutive 16-byte slots, so
-//     each lane fetches the global chunk that belongs in its slot;
+//     ((r >> 2) & 3 for 64-byte rows, (r ^ (r >> 3)) & 7 for 128-byte rows;
+//     fp8 weight rows of 32 bytes: (r >> 3) & 1): a 128-bit read is served
+//     16 lanes at a time on gfx950's 64 banks, and the 16 lanes of one
+//     fragment read take one chunk of 16 consecutive rows, which the
+//     swizzle spreads over all banks.  A direct load writes 64 consecutive
+//     16-byte slots, so each lane fetches the global chunk that belongs in
+//     its slot;
 //   * operands row-major or K-blocked (32-column planes of [rows][32]: the
 //     expert weights when packed, h between the two routed GEMMs, x_perm for
 //     wide experts): K-blocked, a stage's slice of a tile's consecutive rows
@@ -63,7 +74,6 @@ namespace {
 #endif
 constexpr int BM = 256, BK = 32, STAGES = 4;
 constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
-[[maybe_unused]] constexpr int KK = BK / 16;       // k16 MFMA steps per stage
 
 // Tile layouts, LAY = 0, 1, 2.  Full (0): WN wavefronts along the weight
 // rows, 2 along the 256 activation rows, each wave 128 activation rows x RW
@@ -71,14 +81,28 @@ constexpr int CH = BK / 8;        // 16-byte chunks per LDS row
 // the 128 activation rows, each with RW/2 weight rows.  Quarter (2, at most
 // 64 rows): the same weight split over 64 activation rows.  The LDS ring is
 // the same; a shorter layout loads and multiplies only its rows.
-template <int BN, int WN, int LAY>
+// BH: the edge of the MFMA blocks -- 16 for the bf16-operand tiles
+// (16x16x32 MFMAs), 32 for the fp8 x fp8 tiles (32x32x64).
+template <int BN, int WN, int LAY, int BH = 32>
 struct BigCfg {
   static constexpr int NTHR = 128 * WN;
   static constexpr int RW = BN / WN;                 // weight rows per wave column (full layout)
-  static constexpr int TA = LAY == 2 ? 2 : 4;        // 32-row activation blocks per wave
-  static constexpr int TW = LAY ? RW / 64 : RW / 32;
+  static constexpr int TA = (LAY == 2 ? 64 : 128) / BH;  // activation blocks per wave
+  static constexpr int TW = (LAY ? RW / 2 : RW) / BH;    // weight blocks per wave
+  static constexpr int NACC = BH * BH / 64;          // accumulator floats per lane and block
+  static constexpr int RUNS = NACC / 4;              // runs of 4 output columns per lane and block
   static constexpr int A_ROWS = BM >> LAY;           // activation rows loaded
-  static_assert(TW >= 1 && LAY >= 0 && LAY <= 2, "layout");
+  static_assert(TW >= 1 && LAY >= 0 && LAY <= 2 && (BH == 16 || BH == 32), "layout");
+};
+template <int BH>
+struct AccOf;
+template <>
+struct AccOf<16> {
+  using T = f32x4;
+};
+template <>
+struct AccOf<32> {
+  using T = f32x16;
 };
 
 // The layout of a tile with `nrows` rows.
@@ -125,14 +149,14 @@ struct BigMem {
 // tiles hold, per wave column of the full layout, RW/2 rows of W1 followed
 // by the same columns of W3, and a wave's blocks i < TW/2 are W1 (u), the
 // blocks i + TW/2 the matching W3 (v).
-template <int BN, int WN, int LAY, int EPI>
+template <int BN, int WN, int LAY, int EPI, int BH>
 __device__ __forceinline__ int wave_wrow(int wave, int i) {
-  using C = BigCfg<BN, WN, LAY>;
-  if (!LAY) return (wave % WN) * C::RW + i * 32;
-  if (EPI != EPI_SWIGLU) return wave * (C::RW / 2) + i * 32;
+  using C = BigCfg<BN, WN, LAY, BH>;
+  if (!LAY) return (wave % WN) * C::RW + i * BH;
+  if (EPI != EPI_SWIGLU) return wave * (C::RW / 2) + i * BH;
   const int slab = wave >> 1, sub = wave & 1;
-  return i < C::TW / 2 ? slab * C::RW + sub * (C::RW / 4) + i * 32
-                       : slab * C::RW + C::RW / 2 + sub * (C::RW / 4) + (i - C::TW / 2) * 32;
+  return i < C::TW / 2 ? slab * C::RW + sub * (C::RW / 4) + i * BH
+                       : slab * C::RW + C::RW / 2 + sub * (C::RW / 4) + (i - C::TW / 2) * BH;
 }
 template <int BN, int WN, int LAY>
 __device__ __forceinline__ int wave_arow(int wave) {
@@ -262,24 +286,26 @@ struct OutTile {
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // End of a tile with the SwiGLU or plain-store epilogue (bf16 out), or of a
-// K-piece of a split tile.
-//   * A whole tile goes out through LDS: each wave writes its values -- runs
-//     of 4 consecutive columns of one row per lane and 32x32 block -- into a
+// K-piece of a split tile.  In MFMA block (i, j) of edge BH, lane l holds
+// output columns i*BH + g*8 + (l/BH)*4 + q (q = 0..3, run g < BH*BH/256)
+// of activation row j*BH + l % BH: runs of 4 consecutive columns.
+//   * A whole tile goes out through LDS: each wave writes its runs into a
 //     row-major copy of the tile, 16-byte chunk c of row r at c ^ (r & 15)
-//     (the 32 rows one write touches spread over the banks); then the block
+//     (the rows one write touches spread over the banks); then the block
 //     stores whole rows with 16-byte writes, so one wave instruction covers
-//     2-4 full row runs rather than 32 rows x 16 bytes.  The operand ring is
+//     2-4 full row runs rather than one run per lane.  The operand ring is
 //     dead by then: every wave has read its last fragments.
 //   * A piece stores its raw accumulators to its partial slot, register-major
 //     so that each 16-byte store of a wave is contiguous.
 // Both are handled block by block in one pass.  lds_sc: the tile's fp8
 // channel scales, staged in LDS by the prologue (stage_scales): BN of them
 // (SwiGLU: BN/2 of W1, then BN/2 of W3).
-template <int BN, int WN, int EPI, int LAY, int WDT>
-__device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
-                                            f32x16 (&acc)[BigCfg<BN, WN, LAY>::TW][BigCfg<BN, WN, LAY>::TA],
-                                            int ncol0, char* lds, int slot, const float* lds_sc) {
-  using C = BigCfg<BN, WN, LAY>;
+template <int BN, int WN, int EPI, int LAY, int WDT, int BH>
+__device__ __forceinline__ void finish_tile(
+    const GemmArgs& a, const TileInfo& ti, const Seg& sg,
+    typename AccOf<BH>::T (&acc)[BigCfg<BN, WN, LAY, BH>::TW][BigCfg<BN, WN, LAY, BH>::TA], int ncol0,
+    char* lds, int slot, const float* lds_sc) {
+  using C = BigCfg<BN, WN, LAY, BH>;
   using O = OutTile<BN, EPI>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -296,18 +322,18 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
     *(u32x2*)(lds + lrow * O::ROW_BYTES + (((lcol >> 3) ^ (lrow & 15)) << 4) + (lcol & 7) * 2) = o;
   };
   auto raw = [&](int i, int j, int g) {
-    P[((i * C::TA + j) * 4 + g) * C::NTHR + tid] =
+    P[((i * C::TA + j) * C::RUNS + g) * C::NTHR + tid] =
         make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
   };
   constexpr int NB = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
 #pragma unroll
-  // Column group by column group (4 columns of 32 activation rows per lane
-  // and block): only that group's fp8 channel scales stay live, which cuts
-  // the fp8-weight epilogue's register spills by more than half.
+  // Run by run (4 columns of BH activation rows per lane and block): only
+  // that run's fp8 channel scales stay live, which keeps the fp8-weight
+  // epilogue's register spills down.
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int lcol = wcol + i * 32 + g * 8 + (lane >> 5) * 4;
+    for (int g = 0; g < C::RUNS; ++g) {
+      const int lcol = wcol + i * BH + g * 8 + (lane / BH) * 4;
       float4 su = make_float4(1.f, 1.f, 1.f, 1.f), sv = su;
       if (scaled) {
         su = *(const float4*)(lds_sc + lcol);
@@ -322,7 +348,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
         }
         // a piece also fills the LDS copy (never stored): with no second
         // path the compiler keeps the accumulators in AGPRs
-        const int lrow = arow + j * 32 + (lane & 31);
+        const int lrow = arow + j * BH + lane % BH;
         float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -336,7 +362,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, const TileInfo& t
         }
         put(lrow, lcol, o[0], o[1], o[2], o[3]);
       }
-      // one group at a time: the accumulators leave the AGPRs as needed
+      // one run at a time: the accumulators leave the AGPRs as needed
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -384,35 +410,58 @@ __device__ __forceinline__ void stage_scales(const Seg& sg, int ncol0, float* ld
   static_assert(BN <= NTHR, "one scale per thread");
 }
 
-// fp8 weights: the order of the next stage's fragment reads in the second
-// k16 step (position -> fragment; weight blocks 0..TW-1, activation blocks
-// TW..): two weight blocks, then activation and weight blocks alternately.
-template <int TW, int TA>
-constexpr int fp8_raw_order(int pos) {
-  int w = 0, x = 0;
-  for (int p = 0;; ++p) {
-    const bool take_w = w < TW && (p < 2 || x >= TA || (p % 2 == 1));
-    const int q = take_w ? w++ : TW + x++;
-    if (p == pos) return q;
+// Pipeline of the bf16-operand tiles: per stage (32 k values) NG groups,
+// GB of them before the stage's barrier; the reads of the next stage's
+// fragments are spread over groups GB..NG-1.
+#ifndef MOE_BIG_GB
+#define MOE_BIG_GB 2
+#endif
+constexpr int kNG = 16, kGB = MOE_BIG_GB;
+// The order of a stage's fragment reads (position -> fragment; weight blocks
+// 0..TW-1, activation blocks TW..).  bf16: the order the MFMAs (weight-block
+// major) first use them, w0, every x, then w1 ..  fp8 weights (raw bytes,
+// widened groups later): two weight blocks, then activation and weight
+// blocks alternately (w0 w1 x0 w2 x1 w3 ..), so every weight block lands
+// well before its widening.
+template <int TW, int TA, int WDT>
+constexpr int frag_order(int pos) {
+  if (WDT == GD_FP8) {
+    int w = 0, x = 0;
+    for (int p = 0;; ++p) {
+      const bool take_w = w < TW && (p < 2 || x >= TA || (p % 2 == 1));
+      const int q = take_w ? w++ : TW + x++;
+      if (p == pos) return q;
+    }
   }
+  return pos == 0 ? 0 : pos <= TA ? TW + pos - 1 : pos - TA;
 }
-// The group of the second k16 step (2 .. NG-1, NG = TW + TA groups, the
-// reads spread over groups 2..NG-1) that reads weight block i.
-template <int TW, int TA>
-constexpr int fp8_read_group(int i) {
-  constexpr int NG = TW + TA;
+// The first read position of group g (GB <= g <= NG) of NDS reads.
+template <int NDS>
+constexpr int read_pos(int g) {
+  return (g - kGB) * NDS / (kNG - kGB);
+}
+// The group that reads fragment q, and (fp8 weights) the group that widens
+// weight block i: one of the last TW groups, at least two groups after its
+// read; NG or more: after the groups.
+template <int TW, int TA, int WDT>
+constexpr int read_group(int q) {
   int pos = 0;
-  while (fp8_raw_order<TW, TA>(pos) != i) ++pos;
-  for (int g = 2; g < NG; ++g)
-    if ((g - 1) * NG / (NG - 2) > pos) return g;
-  return NG;
+  while (frag_order<TW, TA, WDT>(pos) != q) ++pos;
+  int g = kGB;
+  while (read_pos<TW + TA>(g + 1) <= pos) ++g;
+  return g;
+}
+template <int TW, int TA, int WDT>
+constexpr int widen_group(int i) {
+  const int r = read_group<TW, TA, WDT>(i) + 2, l = kNG - TW + i;
+  return r > l ? r : l;
 }
 
 // One tile (or K-piece of a tile) in the full, half or quarter layout.
 template <int BN, int WN, int EPI, int LAY, int WDT>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
                                          int ncol0, char* lds, float* lds_sc) {
-  using C = BigCfg<BN, WN, LAY>;
+  using C = BigCfg<BN, WN, LAY, 16>;
   using M = BigMem<BN, WN, LAY, WDT>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
@@ -489,210 +538,133 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     b_off[j] = (uint32_t)(n * (sg.b_blk ? BK : K) * M::WB + c * 16);
   }
 
-  // Stages past the end re-load the last stage into a buffer that is never
-  // read again: every iteration then issues the same loads, the vmcnt waits
-  // are constants and the refill can be scheduled between the MFMAs.
-  // part 0 = the A loads of a stage, part 1 = its B loads
-  auto issue_part = [&](int kt, int buf, int part) {
-    char* st = lds + buf * M::STAGE_BYTES;
-    const int ks = kt0 + min(kt, KT - 1);  // the stage's k-slice
-    if (part == 0) {
-#pragma unroll
-      for (int j = 0; j < M::A_LOADS; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * a_step, 0, 0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < M::B_LOADS; ++j) {
-        const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
-        if (b_w3[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
-      }
-    }
-  };
-
-  f32x16 acc[C::TW][C::TA];
+  f32x4 acc[C::TW][C::TA];
 #pragma unroll
   for (int i = 0; i < C::TW; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TA; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    for (int j = 0; j < C::TA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Fragments of one k16 step: the wave's weight blocks and activation blocks.
+  // A stage's fragments: the wave's weight blocks and activation blocks, 16
+  // rows each.  Lane l takes row l % 16 of a block and the stage's k values
+  // 8 (l / 16) .. 8 (l / 16) + 7: 16-byte chunk l / 16 of a bf16 row, bytes
+  // 8 (l / 16) .. of a fp8 row (8 raw codes, widened to bf16 in registers).
   const int arow = wave_arow<BN, WN, LAY>(wave);
+  const int kc = lane >> 4, rl = lane & 15;
   struct Frags {
     bf16x8 w[C::TW], x[C::TA];
   };
-  // A k16 step's k values for lane half h = lane / 32: bf16 weights use the
-  // MFMA's own order (chunk 2 kk + h); fp8 weights use chunk 2 h + kk for both
-  // operands -- the same permutation of k on both sides leaves the dot
-  // products unchanged -- so one 16-byte read of a fp8 weight row holds the
-  // lane's values for both k16 steps of the stage.
-  // fp8: a stage's raw weight bytes (both k16 steps), by stage parity: the
-  // next stage's are read during this one and widened only at its end (and,
-  // for the second step, during the next stage's first), so no widening waits
-  // on an LDS read it has just issued
-  u32x4 w8[2][C::TW];
-  auto read_frags = [&](Frags& F, const char* L, int kk) {
-    const int h = lane >> 5;
-    const int c = (WDT == GD_FP8) ? 2 * h + kk : kk * 2 + h;
-#pragma unroll
-    for (int i = 0; i < C::TW; ++i) {
-      const int wr = wave_wrow<BN, WN, LAY, EPI>(wave, i) + (lane & 31);
-      if (WDT == GD_FP8) {
-        if (kk == 0) w8[0][i] = *(const u32x4*)(L + M::A_BYTES + f8_off(wr, h));
-        F.w[i] = kk == 0 ? e4m3x8_to_bf16(w8[0][i][0], w8[0][i][1]) : e4m3x8_to_bf16(w8[0][i][2], w8[0][i][3]);
-      } else {
-        F.w[i] = *(const bf16x8*)(L + M::A_BYTES + 2 * lds_off(wr, c));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < C::TA; ++j)
-      F.x[j] = *(const bf16x8*)(L + 2 * lds_off(arow + j * 32 + (lane & 31), c));
-  };
-  constexpr int NMF = C::TW * C::TA, NDS = C::TW + C::TA;  // MFMAs and fragment reads per k16 step
-
-  // Pipeline over a ring of STAGES = 4 buffers, stage kt in buffer kt % 4.
-  // Iteration kt computes stage kt in two k16 steps.  Each step is laid out
-  // explicitly as NDS groups, fenced so the compiler keeps the order: a
-  // group's MFMAs, then at most one direct load, then one fragment read of
-  // the next step -- the loads and reads then never bunch up between MFMAs.
-  //   step 0: MFMAs on F[0]; the B half of stage kt+3 (into buffer
-  //     (kt+3) % 4); F[1] of this stage.
-  //   step 1: the first two groups' MFMAs on F[1]; then this wave's loads
-  //     of stage kt+1 landed and a barrier (every wave holds its stage-kt
-  //     fragments, so buffer kt % 4 is free); then the remaining MFMAs with
-  //     the A half of stage kt+4 (into buffer kt % 4) and F[0] of stage kt+1.
-  // Stages past the end re-load the last k-slice into buffers never read
-  // again, so every wait is a constant.
-  static_assert(STAGES == 4 && KK == 2, "pipeline is laid out for 4 stages of two k16 steps");
-  // fragments in the order the MFMAs (i-major) consume them: w0, every x,
-  // then w1 ..
-  // One fragment of a k16 step; par: parity of its stage (the fp8 raw
-  // buffer).  fp8 first-step reads are raw weight bytes, widened groups
-  // later: two weight blocks first, then activation and weight blocks
-  // alternately (w0 w1 x0 w2 x1 w3 x2 x3), so each weight block lands well
-  // before its widening and the first activation blocks early (Qwen-shaped
-  // fp8-weight layer, same box, bit-identical: gate-up 1405 -> 1355 us,
-  // down 823 -> 807 us against reading and widening together).
-  auto read_one = [&](Frags& F, const char* L, auto KKC, auto IDX, auto PAR) {
-    constexpr int kk = decltype(KKC)::value, qq = decltype(IDX)::value, par = decltype(PAR)::value;
-    constexpr int q = (WDT == GD_FP8 && kk == 0) ? fp8_raw_order<C::TW, C::TA>(qq)
-                      : qq == 0 ? 0 : qq <= C::TA ? C::TW + qq - 1 : qq - C::TA;
-    const int h = lane >> 5;
-    const int c = (WDT == GD_FP8) ? 2 * h + kk : kk * 2 + h;
+  u32x2 w8[C::TW];  // fp8: raw weight codes between their read and widening
+  auto read_one = [&](Frags& F, const char* L, auto POS) {
+    constexpr int q = frag_order<C::TW, C::TA, WDT>(decltype(POS)::value);
     if constexpr (q < C::TW) {
-      const int wr = wave_wrow<BN, WN, LAY, EPI>(wave, q) + (lane & 31);
-      if constexpr (WDT == GD_FP8) {
-        if (kk == 0) w8[par][q] = *(const u32x4*)(L + M::A_BYTES + f8_off(wr, h));  // widened at the stage's end
-        else F.w[q] = e4m3x8_to_bf16(w8[par][q][2], w8[par][q][3]);
-      } else {
-        F.w[q] = *(const bf16x8*)(L + M::A_BYTES + 2 * lds_off(wr, c));
-      }
+      const int wr = wave_wrow<BN, WN, LAY, EPI, 16>(wave, q) + rl;
+      if constexpr (WDT == GD_FP8)
+        w8[q] = *(const u32x2*)(L + M::A_BYTES + f8_off(wr, kc >> 1) + (kc & 1) * 8);
+      else
+        F.w[q] = *(const bf16x8*)(L + M::A_BYTES + 2 * lds_off(wr, kc));
     } else {
-      F.x[q - C::TW] = *(const bf16x8*)(L + 2 * lds_off(arow + (q - C::TW) * 32 + (lane & 31), c));
+      F.x[q - C::TW] = *(const bf16x8*)(L + 2 * lds_off(arow + (q - C::TW) * 16 + rl, kc));
     }
   };
-  auto issue_one = [&](int kt, int buf, int part, auto JDX) {
-    constexpr int j = decltype(JDX)::value;
+  auto widen = [&](Frags& F, auto I) {
+    constexpr int i = decltype(I)::value;
+    F.w[i] = e4m3x8_to_bf16(w8[i][0], w8[i][1]);
+  };
+  // load l of a stage: its A loads, then its B loads
+  auto issue_one = [&](int kt, int buf, auto LDX) {
+    constexpr int l = decltype(LDX)::value;
     char* st = lds + buf * M::STAGE_BYTES;
     const int ks = kt0 + min(kt, KT - 1);
-    if (part == 0) {
-      if constexpr (j < M::A_LOADS)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + j) * 1024), 16, a_off[j], ks * a_step, 0, 0);
-    } else {
-      if constexpr (j < M::B_LOADS) {
-        const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
-        if (b_w3[j])
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
-      }
+    if constexpr (l < M::A_LOADS) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rsrc, (lds_ptr_t)(st + (wave * M::A_LOADS + l) * 1024), 16, a_off[l], ks * a_step, 0, 0);
+    } else if constexpr (l < M::LOADS) {
+      constexpr int j = l - M::A_LOADS;
+      const lds_ptr_t dst = (lds_ptr_t)(st + M::A_BYTES + (wave * M::B_LOADS + j) * 1024);
+      if (b_w3[j])
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
     }
   };
+  constexpr int NMF = C::TW * C::TA, NDS = C::TW + C::TA;  // MFMAs and fragment reads per stage
   auto mfma_range = [&](const Frags& F, auto LO, auto HI) {
     static_for<decltype(LO)::value, decltype(HI)::value>([&](auto MI) {
       constexpr int m = decltype(MI)::value;
       constexpr int i = m / C::TA, j = m % C::TA;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.w[i], F.x[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F.w[i], F.x[j], acc[i][j], 0, 0, 0);
     });
   };
-  constexpr int NG = NDS;  // groups per step
+
+  // Pipeline over a ring of STAGES = 4 buffers, stage kt in buffer kt % 4,
+  // its fragments read into registers during stage kt - 1.  Stage kt is one
+  // k32 step of TW x TA MFMAs on those registers, laid out as kNG groups
+  // fenced so the compiler keeps the order:
+  //   groups 0 .. kGB-1: MFMAs only;
+  //   then every wave's reads of stage kt are done (lgkmcnt(0)) and this
+  //     wave's loads of stage kt+1 have landed (vmcnt), and a barrier: stage
+  //     kt+1 is readable and buffer kt % 4 free;
+  //   groups kGB .. kNG-1: MFMAs, one direct load of stage kt+4 into buffer
+  //     kt % 4 and a share of the reads of stage kt+1's fragments (fp8
+  //     weights: raw codes, widened in the last groups).
+  // A stage's loads are issued three stages before the barrier that waits
+  // for them.  Stages past the end re-load the last k-slice into buffers
+  // never read again, so every wait is a constant.
+  static_assert(STAGES == 4, "pipeline is laid out for 4 stages");
+  static_assert(M::LOADS <= kNG - kGB && 3 * M::LOADS < 64, "loads per stage");
 
   const bool scaled = WDT == GD_FP8 && EPI != EPI_BIAS_F32 && sg.s0 != nullptr && wk.slot < 0;
   if (scaled) stage_scales<BN, EPI, C::NTHR>(sg, ncol0, lds_sc, wave);
-  issue_part(0, 0, 0); issue_part(0, 0, 1);
-  issue_part(1, 1, 0); issue_part(1, 1, 1);
-  issue_part(2, 2, 0); issue_part(2, 2, 1);
-  issue_part(3, 3, 0);
-  wait_vmcnt<2 * M::LOADS + M::A_LOADS>();  // stage 0 done
+  static_for<0, STAGES>([&](auto S) {
+    static_for<0, M::LOADS>([&](auto J) { issue_one(decltype(S)::value, decltype(S)::value, J); });
+  });
+  wait_vmcnt<3 * M::LOADS>();  // stage 0 (and the scales) landed
   barrier_only();
 
   Frags F[2];
-  read_frags(F[0], lds, 0);
+  static_for<0, NDS>([&](auto R) { read_one(F[0], lds, R); });
+  if constexpr (WDT == GD_FP8) static_for<0, C::TW>([&](auto I) { widen(F[0], I); });
   // unrolled by the ring depth: stage kt = k4 + u sits in buffer u, so
   // every LDS address is a constant
   for (int k4 = 0; k4 < KT; k4 += STAGES) {
     static_for<0, STAGES>([&](auto U) {
-      constexpr int u = decltype(U)::value;
+      constexpr int u = decltype(U)::value, cur = u & 1;
       const int kt = k4 + u;
       if (kt >= KT) return;
-      const char* L = lds + u * M::STAGE_BYTES;
       const char* Ln = lds + ((u + 1) % STAGES) * M::STAGE_BYTES;
-      constexpr int bb = (u + 3) % STAGES, ba = u;
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int par = u & 1;
-      // step 0
-      static_for<0, NG>([&](auto G) {
+      static_for<0, kGB>([&](auto G) {
         constexpr int g = decltype(G)::value;
-        mfma_range(F[0], IC<g * NMF / NG>{}, IC<(g + 1) * NMF / NG>{});
-        issue_one(kt + 3, bb, 1, G);
-        read_one(F[1], L, IC<1>{}, G, IC<par>{});
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // step 1
-      static_for<0, 2>([&](auto G) {
-        constexpr int g = decltype(G)::value;
-        mfma_range(F[1], IC<g * NMF / NG>{}, IC<(g + 1) * NMF / NG>{});
+        mfma_range(F[cur], IC<g * NMF / kNG>{}, IC<(g + 1) * NMF / kNG>{});
         __builtin_amdgcn_sched_barrier(0);
       });
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       wait_vmcnt<2 * M::LOADS>();
       barrier_only();
       __builtin_amdgcn_sched_barrier(0);
-      static_for<2, NG>([&](auto G) {
+      static_for<kGB, kNG>([&](auto G) {
         constexpr int g = decltype(G)::value;
-        constexpr int r0 = (g - 2) * NDS / (NG - 2), r1 = (g - 1) * NDS / (NG - 2);
-        mfma_range(F[1], IC<g * NMF / NG>{}, IC<(g + 1) * NMF / NG>{});
-        issue_one(kt + 4, ba, 0, IC<g - 2>{});
-        static_for<r0, r1>([&](auto R) { read_one(F[0], Ln, IC<0>{}, R, IC<par ^ 1>{}); });
-        if constexpr (WDT == GD_FP8) {  // widen a weight block read groups ago
-          constexpr int i = g - (NG - C::TW);
-          if constexpr (i >= 0 && fp8_read_group<C::TW, C::TA>(i) < g)
-            F[0].w[i] = e4m3x8_to_bf16(w8[par ^ 1][i][0], w8[par ^ 1][i][1]);
-        }
+        mfma_range(F[cur], IC<g * NMF / kNG>{}, IC<(g + 1) * NMF / kNG>{});
+        issue_one(kt + 4, u, IC<g - kGB>{});
+        static_for<read_pos<NDS>(g), read_pos<NDS>(g + 1)>([&](auto R) { read_one(F[cur ^ 1], Ln, R); });
+        if constexpr (WDT == GD_FP8)
+          static_for<0, C::TW>([&](auto I) {
+            if constexpr (widen_group<C::TW, C::TA, WDT>(decltype(I)::value) == g) widen(F[cur ^ 1], I);
+          });
         __builtin_amdgcn_sched_barrier(0);
       });
-      static_for<NG - 2, M::A_LOADS>([&](auto J) { issue_one(kt + 4, ba, 0, J); });
-      if constexpr (WDT == GD_FP8) {  // the rest of the next stage's first-step weights
+      if constexpr (WDT == GD_FP8)
         static_for<0, C::TW>([&](auto I) {
-          constexpr int i = decltype(I)::value, g = NG - C::TW + i;
-          if constexpr (!(i >= 0 && g >= 2 && fp8_read_group<C::TW, C::TA>(i) < g))
-            F[0].w[i] = e4m3x8_to_bf16(w8[par ^ 1][i][0], w8[par ^ 1][i][1]);
+          if constexpr (widen_group<C::TW, C::TA, WDT>(decltype(I)::value) >= kNG) widen(F[cur ^ 1], I);
         });
-      }
     });
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
 
   if constexpr (EPI == EPI_BIAS_F32)  // router logits: never split (K ranges go to blockIdx.y)
-    store_tile<C::TW, C::TA, WDT, EPI>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, LAY, EPI>(wave), lane);
+    store_tile<C::TW, C::TA, WDT, EPI, 16>(a, ti, sg, acc, arow, ncol0 + wave_col<BN, WN, LAY, EPI>(wave), lane);
   else
-    finish_tile<BN, WN, EPI, LAY, WDT>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
+    finish_tile<BN, WN, EPI, LAY, WDT, 16>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
 }
 #endif
 
@@ -740,7 +712,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
 // boundaries.
 //
 // A stage (k = 64) is one step of TW x TA block-scaled MFMAs, laid out like
-// a k16 step of the bf16 pipeline: groups of MFMAs, each followed by its
+// a stage of the bf16 pipeline: groups of MFMAs, each followed by its
 // share of the direct loads and of the next stage's fragment reads (full
 // fragment sets double-buffered in registers).  The first groups issue the B
 // refill, then the barrier, then the A refill and the reads (Qwen-shaped
@@ -859,7 +831,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     return __builtin_shufflevector(p, q, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto wfrag = [&](const char* L, int i) {
-    return frag(L + M::A_BYTES, wave_wrow<BN, WN, LAY, EPI>(wave, i) + (lane & 31));
+    return frag(L + M::A_BYTES, wave_wrow<BN, WN, LAY, EPI, 32>(wave, i) + (lane & 31));
   };
   auto xfrag = [&](const char* L, int j) { return frag(L, arow + j * 32 + (lane & 31)); };
   u32x4 SC[C::TA];  // this chunk's 16 scale bytes of each activation block's row
@@ -975,7 +947,7 @@ __device__ __forceinline__ void big_tile_fp8(const GemmArgs& a, const TileInfo& 
     });
   }
   wait_vmcnt<0>();  // the re-loads past the end land before the block can exit
-  finish_tile<BN, WN, EPI, LAY, GD_FP8>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
+  finish_tile<BN, WN, EPI, LAY, GD_FP8, 32>(a, ti, sg, acc, ncol0, lds, wk.slot, lds_sc);
 }
 #endif
 
@@ -1003,20 +975,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
 }
 
 // Fixup of the split tiles, one float4 of the pieces' register layout per
-// work unit: unit ((i * TA + j) * 4 + g) * NTHR + t holds accumulator floats
-// 4g..4g+3 of block (i, j) of GEMM thread t, i.e. four consecutive output
-// columns of one row.  The unit's pieces are added in piece order (the same
+// work unit: unit ((i * TA + j) * RUNS + g) * NTHR + t holds accumulator
+// floats 4g..4g+3 of block (i, j) of GEMM thread t, i.e. four consecutive
+// output columns of one row (the block layout of finish_tile, edge BH).  The unit's pieces are added in piece order (the same
 // sum whichever block ran which piece), then the tile's epilogue is applied
 // to those four columns.  SwiGLU units pair block i (u) with block i + TW/2
 // (v).  Spreading units over many blocks keeps the reads in flight.
 constexpr int kFixupChunks = 16;  // blocks per split tile
-template <int BN, int WN, int EPI, int LAY, int WDT>
+template <int BN, int WN, int EPI, int LAY, int WDT, int BH>
 __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& ti, const Seg& sg, int ncol0,
                                             int first_slot, int s) {
-  using C = BigCfg<BN, WN, LAY>;
+  using C = BigCfg<BN, WN, LAY, BH>;
   constexpr int NT = 128 * WN;  // threads of the GEMM block
   constexpr int TWO = (EPI == EPI_SWIGLU) ? C::TW / 2 : C::TW;
-  constexpr int UNITS = NT * TWO * C::TA * 4;
+  constexpr int UNITS = NT * TWO * C::TA * C::RUNS;
   constexpr size_t SLOT4 = kPartialSlotBytes / 16;
   const float4* P = (const float4*)a.partial + (size_t)first_slot * SLOT4;
   // pieces in order; their loads four at a time, so several are in flight
@@ -1041,15 +1013,15 @@ __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& t
   };
   for (int u = blockIdx.y * blockDim.x + threadIdx.x; u < UNITS; u += gridDim.y * blockDim.x) {
     const int t = u % NT, r = u / NT;
-    const int g = r & 3, j = (r >> 2) % C::TA, i = (r >> 2) / C::TA;
+    const int g = r % C::RUNS, j = (r / C::RUNS) % C::TA, i = (r / C::RUNS) / C::TA;
     const int wave = t >> 6, lane = t & 63;
-    const int row = wave_arow<BN, WN, LAY>(wave) + j * 32 + (lane & 31);
+    const int row = wave_arow<BN, WN, LAY>(wave) + j * BH + lane % BH;
     if (row >= ti.nrows) continue;
-    const int n = ncol0 + wave_col<BN, WN, LAY, EPI>(wave) + i * 32 + g * 8 + (lane >> 5) * 4;
+    const int n = ncol0 + wave_col<BN, WN, LAY, EPI>(wave) + i * BH + g * 8 + (lane / BH) * 4;
     float o[4];
-    const float4 x = sum(((i * C::TA + j) * 4 + g) * NT + t);
+    const float4 x = sum(((i * C::TA + j) * C::RUNS + g) * NT + t);
     if (EPI == EPI_SWIGLU) {
-      const float4 y = sum((((i + C::TW / 2) * C::TA + j) * 4 + g) * NT + t);
+      const float4 y = sum((((i + C::TW / 2) * C::TA + j) * C::RUNS + g) * NT + t);
       float4 su = make_float4(1.f, 1.f, 1.f, 1.f), sv = su;
       if (WDT == GD_FP8 && sg.s0) {
         su = *(const float4*)(sg.s0 + n);
@@ -1077,8 +1049,8 @@ __device__ __forceinline__ void fixup_units(const GemmArgs& a, const TileInfo& t
   }
 }
 
-// Blocks (split tile, chunk).
-template <int BN, int WN, int EPI, int WDT>
+// Blocks (split tile, chunk); BH: the MFMA block edge of the GEMM's tiles.
+template <int BN, int WN, int EPI, int WDT, int BH>
 __global__ __launch_bounds__(256) void gemm_big_fixup_kernel(GemmArgs a, int n_tiles, int kt_plan, int n_cu) {
   if constexpr (EPI != EPI_BIAS_F32) {  // router logits never split this way
     const int m_real = real_mtiles(a, BM);
@@ -1092,9 +1064,9 @@ __global__ __launch_bounds__(256) void gemm_big_fixup_kernel(GemmArgs a, int n_t
     const int ncol0 = nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
     if (ncol0 >= sg.N) return;
     switch (tile_layout(ti.nrows)) {
-      case 2: fixup_units<BN, WN, EPI, 2, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
-      case 1: fixup_units<BN, WN, EPI, 1, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
-      default: fixup_units<BN, WN, EPI, 0, WDT>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
+      case 2: fixup_units<BN, WN, EPI, 2, WDT, BH>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
+      case 1: fixup_units<BN, WN, EPI, 1, WDT, BH>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s); break;
+      default: fixup_units<BN, WN, EPI, 0, WDT, BH>(a, ti, sg, ncol0, blockIdx.x * p.s, p.s);
     }
   }
 }
@@ -1139,7 +1111,7 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
     hipLaunchKernelGGL((gemm_big_kernel<BN, WN, EPI, WDT>), dim3(nb, a.ksplit), dim3(128 * WN), 0, s, a,
                        n_tiles, kt_plan, n_cu);
   if (n_cu > 0)
-    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT>), dim3(n_cu / 2, kFixupChunks), dim3(256),
+    hipLaunchKernelGGL((gemm_big_fixup_kernel<BN, WN, EPI, WDT, FP8ACT ? 32 : 16>), dim3(n_cu / 2, kFixupChunks), dim3(256),
                        0, s, a, n_tiles, kt_plan, n_cu);
   return hipGetLastError();
 }

@@ -141,27 +141,28 @@ __device__ __forceinline__ float silu(float u) {
   return u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
 }
 
-// Epilogue of a wave's TW x TA grid of 32x32 MFMA blocks computed as
-// (weight rows) x (activation rows).  In block (i, j), lane l holds weight rows
-// g*8 + (l/32)*4 + q (q = 0..3, group g = 0..3) of activation row l % 32, i.e.
-// runs of 4 consecutive output columns.
+// Epilogue of a wave's TW x TA grid of BHxBH MFMA blocks (BH = 32 or 16)
+// computed as (weight rows) x (activation rows).  In block (i, j), lane l
+// holds weight rows g*8 + (l/BH)*4 + q (q = 0..3, run g < BH*BH/256) of
+// activation row l % BH, i.e. runs of 4 consecutive output columns.
 //   col0: first output column of this wave's weight rows
 //   SwiGLU: blocks i < TW/2 are W1 (u), blocks i + TW/2 the matching W3 (v).
-template <int TW, int TA, int WDT, int EPI>
+template <int TW, int TA, int WDT, int EPI, int BH = 32, class AV = f32x16>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg,
-                                           f32x16 (&acc)[TW][TA], int row_base, int col0,
+                                           AV (&acc)[TW][TA], int row_base, int col0,
                                            int lane) {
-  const int r_in = lane & 31;
+  constexpr int G = BH * BH / 256;  // runs per lane and block
+  const int r_in = lane % BH;
   const bool scaled = WDT == GD_FP8 && sg.s0 != nullptr;
   if (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < TW / 2; ++i) {
       // fp8 per-output-channel scales of this block's columns: one 16-byte
       // load per run of 4 columns, shared by all activation blocks
-      float4 su[4], sv[4];
+      float4 su[G], sv[G];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+      for (int g = 0; g < G; ++g) {
+        const int n = col0 + i * BH + g * 8 + (lane / BH) * 4;
         if (scaled) {
           su[g] = *(const float4*)(sg.s0 + n);
           sv[g] = *(const float4*)(sg.s1 + n);
@@ -169,12 +170,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
       }
 #pragma unroll
       for (int j = 0; j < TA; ++j) {
-        const int lrow = row_base + j * 32 + r_in;
+        const int lrow = row_base + j * BH + r_in;
         if (lrow >= ti.nrows) continue;
         const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+        for (int g = 0; g < G; ++g) {
+          const int n = col0 + i * BH + g * 8 + (lane / BH) * 4;
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -196,18 +197,18 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
   } else if (EPI == EPI_STORE) {
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-      float4 sc[4];
+      float4 sc[G];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        if (scaled) sc[g] = *(const float4*)(sg.s0 + col0 + i * 32 + g * 8 + (lane >> 5) * 4);
+      for (int g = 0; g < G; ++g)
+        if (scaled) sc[g] = *(const float4*)(sg.s0 + col0 + i * BH + g * 8 + (lane / BH) * 4);
 #pragma unroll
       for (int j = 0; j < TA; ++j) {
-        const int lrow = row_base + j * 32 + r_in;
+        const int lrow = row_base + j * BH + r_in;
         if (lrow >= ti.nrows) continue;
         const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+        for (int g = 0; g < G; ++g) {
+          const int n = col0 + i * BH + g * 8 + (lane / BH) * 4;
           float yv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -224,14 +225,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileInfo& ti
   } else {  // EPI_BIAS_F32: router logits (partial sums of one K range)
 #pragma unroll
     for (int j = 0; j < TA; ++j) {
-      const int lrow = row_base + j * 32 + r_in;
+      const int lrow = row_base + j * BH + r_in;
       if (lrow >= ti.nrows) continue;
       const size_t row = (size_t)(ti.row0 + lrow);
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = col0 + i * 32 + g * 8 + (lane >> 5) * 4;
+        for (int g = 0; g < G; ++g) {
+          const int n = col0 + i * BH + g * 8 + (lane / BH) * 4;
           float* zr = (float*)sg.C + ((size_t)blockIdx.y * a.rows + row) * sg.N + n;
           if ((sg.N & 3) == 0 && n + 3 < sg.N) {  // whole run, 16-byte aligned
             float4 z = make_float4(acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
