@@ -107,6 +107,11 @@ CASES = {
     # 1040: 16 rows, with the group limit and a shared expert)
     "router_big_e256_qtail": QWEN_FP8_SKEW.scaled(T=1050, d=512, f=128, E=256, k=4),
     "router_big_dsv3_qtail": DSV3_PREFILL_SKEW.scaled(T=1040, d=512, f=128, E=256, f_shared=128),
+    # group limits in the selection kernel: groups of 64 and of 2 (64 groups)
+    # ranked in registers, groups of 48 (not a power of two) through LDS
+    "group_g64": DSV3_PREFILL_SKEW.scaled(T=64, d=256, f=256, E=256, n_group=4, topk_group=2, f_shared=0),
+    "group_g2": DSV3_PREFILL_SKEW.scaled(T=64, d=256, f=256, E=128, k=4, n_group=64, topk_group=8, f_shared=0),
+    "group_g48": DSV3_PREFILL_SKEW.scaled(T=64, d=256, f=256, E=192, n_group=4, topk_group=2, f_shared=0),
 }
 
 _CACHE = {}
