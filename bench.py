@@ -18,7 +18,7 @@ Prints one JSON line:
               records around each stage inside the timed steps, on the stream
               the kernels run on
   ceilings    measured in this run: the GEMM's MFMA pattern alone (bf16 and fp8,
-              random and constant operands, each sustained ~1 s, with the
+              random and constant operands, each sustained ~1.6 s, with the
               socket power and graphics clock read meanwhile) and a streaming
               read (calib/ceilings.hip)
   sustained   the same step repeated for ~2 s after the timed steps, with the
@@ -221,7 +221,9 @@ class PowerSampler:
     (amdsmi, read-only) every few ms on a thread while a sustained run goes on.
     Without amdsmi, or on any error from it, the summary is None."""
 
-    SETTLE_S = 0.25  # samples in the first 0.25 s of a window are dropped
+    # samples in the first 0.6 s of a window are dropped: the table's power
+    # and clock readings trail the work by a fraction of a second
+    SETTLE_S = 0.6
 
     def __init__(self):
         import threading
@@ -308,27 +310,30 @@ def ceilings(which=("mfma", "stream")) -> dict:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = {"compute_units": cus}
     if "mfma" in which:
-        # the GEMM's k16-step MFMA pattern, one wavefront per SIMD, each probe
-        # sustained for about a second (long enough for the clock to settle)
+        # the MFMA pattern of a GEMM stage (bf16: 16x16x32 as the bf16-operand
+        # tiles; fp8: 32x32x64 as the fp8 x fp8 tiles), one wavefront per
+        # SIMD, each probe sustained for ~1.6 s (long enough for the
+        # clock to settle); both do 32 x 32768 flops per wavefront and iteration
         sampler = PowerSampler()
         blocks = cus
         sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
         power = {}
-        for name, fn, iters, flop in (("bf16", lib.moe_calib_mfma_bf16_gemm, 3000, 32 * 32 * 16 * 2),
+        for name, fn, iters, flop in (("bf16", lib.moe_calib_mfma_bf16_gemm, 3000, 2 * 16 * 16 * 32 * 2),
                                       ("fp8", lib.moe_calib_mfma_fp8_gemm, 1500, 32 * 32 * 64 * 2)):
             for const in (0, 1):
                 def launch(fn=fn, iters=iters, const=const):
                     rc = fn(blocks, iters, const, ctypes.c_void_p(sink.data_ptr()), stream)
                     if rc != 0:
                         raise RuntimeError(f"calibration launch failed: hipError {rc}")
-                n, secs, pw = _sustained(launch, 1.0, sampler)
+                n, secs, pw = _sustained(launch, 1.6, sampler)
                 key = f"mfma_{name}_{'constant' if const else 'random'}_tflops"
                 out[key] = round(n * blocks * 4 * iters * 32 * flop / secs / 1e12, 1)
                 power[key] = pw
         out["mfma_power"] = power
-        out["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts (one per SIMD), a 4 x 4 grid of 32x32 accumulators "
-                             "fed from two alternating register sets, random or constant operands, each sustained "
-                             "~1 s (calib/ceilings.hip)")
+        out["mfma_probe"] = (f"{blocks} blocks x 4 wavefronts (one per SIMD); bf16: 16x16x32 MFMAs on an 8 x 4 "
+                             "grid of 16x16 accumulators, fp8: 32x32x64 block-scaled MFMAs on a 4 x 4 grid of 32x32 "
+                             "accumulators; operands from two alternating register sets, random or constant, each "
+                             "sustained ~1.6 s (calib/ceilings.hip)")
     if "stream" in which:
         nbytes = 4 << 30
         src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
@@ -344,7 +349,7 @@ def ceilings(which=("mfma", "stream")) -> dict:
                     raise RuntimeError(f"calibration launch failed: hipError {rc}")
             ms = _timed(launch, 5)
             out[key] = round(read.value / (ms * 1e-3) / 1e9, 1)
-            n, secs, pw = _sustained(launch, 1.0, PowerSampler())
+            n, secs, pw = _sustained(launch, 1.6, PowerSampler())
             out[key.replace("_gbs", "_sustained_gbs")] = round(n * read.value / secs / 1e9, 1)
             out[key.replace("_gbs", "_power")] = pw
         # the ceiling: the faster of the two access kinds

@@ -1,14 +1,17 @@
 // Ceiling probes for the bench's roofline figures, kept apart from the layer
 // library (libmoe_calib.so, loaded only by bench.py).  Each measures what one
 // gfx950 unit sustains with nothing else in the way:
-//   * the MFMA pattern of the prefill GEMM's k16 step on its own: one
-//     wavefront per SIMD (one block of four per CU), a 4 x 4 grid of 32x32
-//     accumulators, operands from two alternating register sets of 4 weight and
-//     4 activation fragments, in bf16 (v_mfma_f32_32x32x16_bf16) or fp8
-//     (v_mfma_scale_f32_32x32x64_f8f6f4); with random operand values (the
-//     MFMA's power, and so the clock the chip holds, depends on how the
-//     operand bits toggle: a loop on constant operands runs at full clock,
-//     one on random data does not) or constant ones;
+//   * the MFMA pattern of a prefill GEMM stage on its own: one wavefront per
+//     SIMD (one block of four per CU), operands from two alternating
+//     register sets; bf16 as the bf16-operand tiles run it
+//     (v_mfma_f32_16x16x32_bf16 on an 8 x 4 grid of 16x16 accumulators, 8
+//     weight and 4 activation fragments per set), fp8 as the fp8 x fp8
+//     tiles do (v_mfma_scale_f32_32x32x64_f8f6f4 on a 4 x 4 grid of 32x32
+//     accumulators); with random operand values (the MFMA's power, and so
+//     the clock the chip holds, depends on how the operand bits toggle: a
+//     loop on constant operands runs at full clock, one on random data does
+//     not) or constant ones.  Both do 32 x 32768 flops per wavefront and
+//     iteration;
 //   * a streaming read: each block reads one contiguous chunk with 16-byte
 //     loads, consecutive lanes on consecutive 16-byte pieces, with plain or
 //     non-temporal loads.
@@ -20,6 +23,7 @@
 
 typedef __bf16 c_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float c_f32x16 __attribute__((ext_vector_type(16)));
+typedef float c_f32x4 __attribute__((ext_vector_type(4)));
 typedef int c_i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t c_u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,30 +45,30 @@ __device__ uint32_t mix32(uint32_t x) {
 // bf16 operands: random values in [-2, 2) unless `constant`.
 __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_gemm_shape(int iters, int constant, float* sink) {
   const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
-  c_bf16x8 w[2][4], x[2][4];
+  c_bf16x8 w[2][8], x[2][4];
   for (int s = 0; s < 2; ++s)
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 8; ++q)
       for (int i = 0; i < 8; ++i) {
         const uint32_t r = mix32(t * 977u + s * 131u + q * 17u + i + 1u);
         w[s][q][i] = (__bf16)(constant ? 1.0f : float(int(r & 0xffff) - 32768) / 16384.0f);
-        x[s][q][i] = (__bf16)(constant ? 0.5f : float(int(r >> 16) - 32768) / 16384.0f);
+        if (q < 4) x[s][q][i] = (__bf16)(constant ? 0.5f : float(int(r >> 16) - 32768) / 16384.0f);
       }
-  c_f32x16 acc[4][4];
-  for (int i = 0; i < 4; ++i)
+  c_f32x4 acc[8][4];
+  for (int i = 0; i < 8; ++i)
     for (int j = 0; j < 4; ++j)
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+      for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.0f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[s][i], x[s][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[s][i], x[s][j], acc[i][j], 0, 0, 0);
   }
   float v = 0.0f;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
     for (int j = 0; j < 4; ++j)
-      for (int q = 0; q < 16; ++q) v += acc[i][j][q];
+      for (int q = 0; q < 4; ++q) v += acc[i][j][q];
   if (v == -1.2345e-30f) sink[t] = v;
 }
 
