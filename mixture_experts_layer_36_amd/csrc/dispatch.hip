@@ -332,21 +332,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ x
   }
 }
 
-// The same rows into K/32 planes of [rows][32] bf16 (perm NULL: x's rows in
+// The same rows into K/pw planes of [rows][pw] bf16 (perm NULL: x's rows in
 // order): thread g moves the 16 bytes at g, so a wave stores one contiguous
-// kilobyte (16 rows x 64 bytes of one plane) and loads 16 row runs of 64
-// bytes.
+// kilobyte (16 rows x 64 bytes, or 8 rows x 128, of one plane) and loads
+// 16 (8) row runs.
 __global__ __launch_bounds__(256) void gather_blocked_kernel(const u32x4* __restrict__ x,
                                                              const int32_t* __restrict__ perm, int rows,
                                                              const int32_t* __restrict__ rows_dev, int d,
-                                                             u32x4* __restrict__ out) {
+                                                             int pw, u32x4* __restrict__ out) {
   const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t per_plane = (size_t)rows * 4;
-  if (g >= per_plane * (d / 32)) return;
-  const int p = (int)(g / per_plane), rem = (int)(g % per_plane), r = rem >> 2, q = rem & 3;
+  const int cpr = pw / 8;  // 16-byte chunks per row and plane
+  const size_t per_plane = (size_t)rows * cpr;
+  if (g >= per_plane * (d / pw)) return;
+  const int p = (int)(g / per_plane), rem = (int)(g % per_plane), r = rem / cpr, q = rem % cpr;
   const int n = rows_dev ? min(*rows_dev, rows) : rows;
   if (r >= n) return;
-  out[g] = x[((size_t)(perm ? perm[r] : r) * d + p * 32 + q * 8) / 8];
+  out[g] = x[((size_t)(perm ? perm[r] : r) * d + p * pw + q * 8) / 8];
 }
 
 __global__ __launch_bounds__(256) void segment_rows_kernel(const int32_t* offsets, int E, int32_t* rows) {
@@ -411,12 +412,12 @@ hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows
 }
 
 hipError_t launch_gather_rows_blocked(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
-                                      int d, void* x_perm, hipStream_t s) {
+                                      int d, int pw, void* x_perm, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (d % 32 != 0) return hipErrorInvalidValue;
+  if ((pw != 32 && pw != 64) || d % pw != 0) return hipErrorInvalidValue;
   const size_t threads = (size_t)rows * (d / 8);
   hipLaunchKernelGGL(gather_blocked_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     (const u32x4*)x, perm_token, rows, rows_dev, d, (u32x4*)x_perm);
+                     (const u32x4*)x, perm_token, rows, rows_dev, d, pw, (u32x4*)x_perm);
   return hipGetLastError();
 }
 

@@ -447,6 +447,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
         (!a.c_blk || a.epi == EPI_SWIGLU) && (!a.a_blk || a.act == GD_BF16) &&
         (!a.sh_a_blk || a.act == GD_BF16)))
     return hipErrorInvalidValue;
+  // 64-column planes: the SwiGLU GEMM, K (and the extra segment's K) a
+  // multiple of 64
+  if (a.a_blk < 0 || a.a_blk > 2 || a.sh_a_blk < 0 || a.sh_a_blk > 2 ||
+      ((a.a_blk == 2 || a.sh_a_blk == 2) &&
+       (a.epi != EPI_SWIGLU || a.K % 64 != 0 || (a.sh_rows > 0 && a.shK % 64 != 0))))
+    return hipErrorInvalidValue;
   if (a.act == GD_F32) {
     switch (a.epi) {
       case EPI_SWIGLU: return launch_f32<EPI_SWIGLU>(a, s);

@@ -457,12 +457,24 @@ constexpr int widen_group(int i) {
   return r > l ? r : l;
 }
 
+// Wide A (64-column planes, a K-blocked A only): swizzle of a 128-byte LDS
+// row, chunk c of row r at c ^ swz8(r): the 16 rows of one fragment read
+// (one chunk each) cover all 64 banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
 // One tile (or K-piece of a tile) in the full, half or quarter layout.
-template <int BN, int WN, int EPI, int LAY, int WDT>
+// WIDE: A in 64-column planes (GemmArgs::a_blk == 2).  Each A load then
+// brings a row's 128 bytes, the A of two consecutive stages, so the ring
+// holds A as two pair buffers (32 KB each: row r's bytes 0-63 the even
+// stage, 64-127 the odd one) beside four B buffers; the same 128 KB.
+template <int BN, int WN, int EPI, int LAY, int WDT, bool WIDE>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, const Seg& sg, const Work& wk,
                                          int ncol0, char* lds, float* lds_sc) {
   using C = BigCfg<BN, WN, LAY, 16>;
   using M = BigMem<BN, WN, LAY, WDT>;
+  constexpr int LA = WIDE ? 2 * M::A_LOADS : M::A_LOADS;  // A loads of one refill (WIDE: a pair of stages)
+  constexpr int A_PAIR = BM * 128;                         // LDS bytes of a pair's A (WIDE)
+  static_assert(!WIDE || 2 * A_PAIR + STAGES * M::B_BYTES <= STAGES * M::STAGE_BYTES, "wide ring");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int K = sg.K;
@@ -470,7 +482,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // logits) the blockIdx.y-th of ksplit ranges
   const int KT_all = K / BK;
   const int np = wk.s * a.ksplit, pi = wk.k0num * a.ksplit + (int)blockIdx.y;
-  const int kt0 = pi * KT_all / np, kt1 = (pi + 1) * KT_all / np;
+  // WIDE: K a multiple of 64 and pieces start on even stages (whole pairs)
+  const int kt0 = WIDE ? 2 * (pi * (KT_all / 2) / np) : pi * KT_all / np;
+  const int kt1 = WIDE ? 2 * ((pi + 1) * (KT_all / 2) / np) : (pi + 1) * KT_all / np;
 
   // Direct loads go through buffer resources: a block-uniform descriptor
   // (SGPRs) per operand, a 32-bit per-lane byte offset fixed across stages
@@ -485,21 +499,25 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // a_prows rows, no row map) spans all planes: a lane's offset is its row's
   // 64 bytes in plane 0 and a stage adds its plane, so a load of the stage's
   // 32-column slice reads consecutive rows as one contiguous run.
-  const int a_plane = sg.a_prows * BK * 2;  // 0: row-major
-  const int a_step = a_plane ? a_plane : BK * 2;  // bytes from one stage's slice to the next
+  // WIDE: planes of 64 columns, a lane's offset its row's 128 bytes in plane
+  // 0 (slot s of a pair's tile is row s / 8, physical chunk s % 8) and a
+  // refill of a pair adds its plane.
+  constexpr int APW = WIDE ? 64 : BK;  // A plane width (columns)
+  const int a_plane = sg.a_prows * APW * 2;  // 0: row-major
+  const int a_step = a_plane ? a_plane : BK * 2;  // bytes from one refill's slice to the next
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      a_plane ? uniform_rsrc(sg.A, (K / BK) * a_plane)
+      a_plane ? uniform_rsrc(sg.A, (K / APW) * a_plane)
       : sg.amap ? uniform_rsrc(sg.A, a.a_map_rows * K * 2)
                 : uniform_rsrc(sg.A + (size_t)ti.row0 * K * 2, ti.nrows * K * 2);
-  uint32_t a_off[M::A_LOADS];
+  uint32_t a_off[LA];
 #pragma unroll
-  for (int j = 0; j < M::A_LOADS; ++j) {
-    const int s = (wave * M::A_LOADS + j) * 64 + lane;
-    const int r = s / CH, c = (s % CH) ^ swz(r);
+  for (int j = 0; j < LA; ++j) {
+    const int s = (wave * LA + j) * 64 + lane;
+    const int r = WIDE ? s / 8 : s / CH, c = WIDE ? (s % 8) ^ swz8(r) : (s % CH) ^ swz(r);
     const int rr = min(r, ti.nrows - 1);
     if (a_plane) {
       const int ar = sg.amap ? sg.amap[ti.row0 + rr] : ti.row0 + rr;
-      a_off[j] = (uint32_t)(ar * BK + c * 8) * 2u;
+      a_off[j] = (uint32_t)(ar * APW + c * 8) * 2u;
     } else {
       const int ar = sg.amap ? sg.amap[ti.row0 + rr] : rr;
       a_off[j] = (uint32_t)(ar * K + c * 8) * 2u;
@@ -554,21 +572,45 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
     bf16x8 w[C::TW], x[C::TA];
   };
   u32x2 w8[C::TW];  // fp8: raw weight codes between their read and widening
-  auto read_one = [&](Frags& F, const char* L, auto POS) {
+  // A stage's LDS: its A (WIDE: the pair buffer and HALF, the stage's half
+  // of each row) and its B.
+  auto read_one = [&](Frags& F, const char* LA_, const char* LB_, auto HALF, auto POS) {
     constexpr int q = frag_order<C::TW, C::TA, WDT>(decltype(POS)::value);
     if constexpr (q < C::TW) {
       const int wr = wave_wrow<BN, WN, LAY, EPI, 16>(wave, q) + rl;
       if constexpr (WDT == GD_FP8)
-        w8[q] = *(const u32x2*)(L + M::A_BYTES + f8_off(wr, kc >> 1) + (kc & 1) * 8);
+        w8[q] = *(const u32x2*)(LB_ + f8_off(wr, kc >> 1) + (kc & 1) * 8);
       else
-        F.w[q] = *(const bf16x8*)(L + M::A_BYTES + 2 * lds_off(wr, kc));
+        F.w[q] = *(const bf16x8*)(LB_ + 2 * lds_off(wr, kc));
     } else {
-      F.x[q - C::TW] = *(const bf16x8*)(L + 2 * lds_off(arow + (q - C::TW) * 16 + rl, kc));
+      const int r = arow + (q - C::TW) * 16 + rl;
+      if constexpr (WIDE)
+        F.x[q - C::TW] = *(const bf16x8*)(LA_ + r * 128 + (((decltype(HALF)::value * 4 + kc) ^ swz8(r)) << 4));
+      else
+        F.x[q - C::TW] = *(const bf16x8*)(LA_ + 2 * lds_off(r, kc));
     }
   };
   auto widen = [&](Frags& F, auto I) {
     constexpr int i = decltype(I)::value;
     F.w[i] = e4m3x8_to_bf16(w8[i][0], w8[i][1]);
+  };
+  // WIDE: load l of the A refill of pair pp (stages 2 pp, 2 pp + 1 of the
+  // piece; pairs past the end re-load the last one) into pair buffer pp % 2,
+  // and load j of stage kt's B into B buffer kt % 4.
+  auto issue_a2 = [&](int pp, auto LDX) {
+    constexpr int l = decltype(LDX)::value;
+    const int ps = kt0 / 2 + min(pp, KT / 2 - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        a_rsrc, (lds_ptr_t)(lds + (pp & 1) * A_PAIR + (wave * LA + l) * 1024), 16, a_off[l], ps * a_step, 0, 0);
+  };
+  auto issue_b2 = [&](int kt, auto JDX) {
+    constexpr int j = decltype(JDX)::value;
+    const int ks = kt0 + min(kt, KT - 1);
+    const lds_ptr_t dst = (lds_ptr_t)(lds + 2 * A_PAIR + (kt & 3) * M::B_BYTES + (wave * M::B_LOADS + j) * 1024);
+    if (b_w3[j])
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b1_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b0_rsrc, dst, 16, b_off[j], ks * b_step, 0, 0);
   };
   // load l of a stage: its A loads, then its B loads
   auto issue_one = [&](int kt, int buf, auto LDX) {
@@ -610,28 +652,55 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
   // A stage's loads are issued three stages before the barrier that waits
   // for them.  Stages past the end re-load the last k-slice into buffers
   // never read again, so every wait is a constant.
+  //   WIDE: a pair buffer frees at the barrier of the pair's odd stage, so
+  //     odd stage kt refills it with the A of stages kt+3 and kt+4 (two and
+  //     three stages of lead); every stage refills its B buffer with stage
+  //     kt+4's B.  The waits follow from that order.
   static_assert(STAGES == 4, "pipeline is laid out for 4 stages");
   static_assert(M::LOADS <= kNG - kGB && 3 * M::LOADS < 64, "loads per stage");
+  static_assert(!WIDE || (LA + M::B_LOADS <= kNG - kGB && LA + 3 * M::B_LOADS < 64), "wide loads per stage");
 
   const bool scaled = WDT == GD_FP8 && EPI != EPI_BIAS_F32 && sg.s0 != nullptr && wk.slot < 0;
   if (scaled) stage_scales<BN, EPI, C::NTHR>(sg, ncol0, lds_sc, wave);
-  static_for<0, STAGES>([&](auto S) {
-    static_for<0, M::LOADS>([&](auto J) { issue_one(decltype(S)::value, decltype(S)::value, J); });
-  });
-  wait_vmcnt<3 * M::LOADS>();  // stage 0 (and the scales) landed
+  if constexpr (WIDE) {
+    static_for<0, LA>([&](auto J) { issue_a2(0, J); });
+    static_for<0, M::B_LOADS>([&](auto J) { issue_b2(0, J); });
+    static_for<0, M::B_LOADS>([&](auto J) { issue_b2(1, J); });
+    static_for<0, LA>([&](auto J) { issue_a2(1, J); });
+    static_for<0, M::B_LOADS>([&](auto J) { issue_b2(2, J); });
+    static_for<0, M::B_LOADS>([&](auto J) { issue_b2(3, J); });
+    wait_vmcnt<LA + 3 * M::B_LOADS>();  // stage 0 (and the scales) landed
+  } else {
+    static_for<0, STAGES>([&](auto S) {
+      static_for<0, M::LOADS>([&](auto J) { issue_one(decltype(S)::value, decltype(S)::value, J); });
+    });
+    wait_vmcnt<3 * M::LOADS>();  // stage 0 (and the scales) landed
+  }
   barrier_only();
 
+  // stage u's LDS (u = kt % 4: every address a constant)
+  auto a_lds = [&](auto U) -> const char* {
+    constexpr int u = decltype(U)::value;
+    return WIDE ? lds + ((u >> 1) & 1) * A_PAIR : lds + u * M::STAGE_BYTES;
+  };
+  auto b_lds = [&](auto U) -> const char* {
+    constexpr int u = decltype(U)::value;
+    return WIDE ? lds + 2 * A_PAIR + u * M::B_BYTES : lds + u * M::STAGE_BYTES + M::A_BYTES;
+  };
   Frags F[2];
-  static_for<0, NDS>([&](auto R) { read_one(F[0], lds, R); });
+  static_for<0, NDS>([&](auto R) { read_one(F[0], a_lds(IC<0>{}), b_lds(IC<0>{}), IC<0>{}, R); });
   if constexpr (WDT == GD_FP8) static_for<0, C::TW>([&](auto I) { widen(F[0], I); });
   // unrolled by the ring depth: stage kt = k4 + u sits in buffer u, so
   // every LDS address is a constant
   for (int k4 = 0; k4 < KT; k4 += STAGES) {
     static_for<0, STAGES>([&](auto U) {
-      constexpr int u = decltype(U)::value, cur = u & 1;
+      constexpr int u = decltype(U)::value, cur = u & 1, un = (u + 1) % STAGES;
       const int kt = k4 + u;
       if (kt >= KT) return;
-      const char* Ln = lds + ((u + 1) % STAGES) * M::STAGE_BYTES;
+      const char* LAn = a_lds(IC<un>{});
+      const char* LBn = b_lds(IC<un>{});
+      // WIDE: loads after this stage's barrier (odd stages also refill A)
+      constexpr int NL = WIDE ? ((u & 1) ? LA : 0) + M::B_LOADS : M::LOADS;
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, kGB>([&](auto G) {
         constexpr int g = decltype(G)::value;
@@ -639,14 +708,28 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const TileInfo& ti, 
         __builtin_amdgcn_sched_barrier(0);
       });
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      wait_vmcnt<2 * M::LOADS>();
+      if constexpr (!WIDE)
+        wait_vmcnt<2 * M::LOADS>();
+      else if constexpr (u & 1)
+        wait_vmcnt<2 * M::B_LOADS>();
+      else
+        wait_vmcnt<LA + 2 * M::B_LOADS>();
       barrier_only();
       __builtin_amdgcn_sched_barrier(0);
       static_for<kGB, kNG>([&](auto G) {
-        constexpr int g = decltype(G)::value;
+        constexpr int g = decltype(G)::value, l = g - kGB;
         mfma_range(F[cur], IC<g * NMF / kNG>{}, IC<(g + 1) * NMF / kNG>{});
-        issue_one(kt + 4, u, IC<g - kGB>{});
-        static_for<read_pos<NDS>(g), read_pos<NDS>(g + 1)>([&](auto R) { read_one(F[cur ^ 1], Ln, R); });
+        if constexpr (!WIDE) {
+          issue_one(kt + 4, u, IC<l>{});
+        } else if constexpr (l < NL) {
+          if constexpr ((u & 1) && l < LA)
+            issue_a2((kt + 3) / 2, IC<l>{});
+          else
+            issue_b2(kt + 4, IC<l - ((u & 1) ? LA : 0)>{});
+        }
+        static_for<read_pos<NDS>(g), read_pos<NDS>(g + 1)>([&](auto R) {
+          read_one(F[cur ^ 1], LAn, LBn, IC<un & 1>{}, R);
+        });
         if constexpr (WDT == GD_FP8)
           static_for<0, C::TW>([&](auto I) {
             if constexpr (widen_group<C::TW, C::TA, WDT>(decltype(I)::value) == g) widen(F[cur ^ 1], I);
@@ -686,10 +769,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   if (!tile_info(a, wk.mt, BM, ti, sg)) return;
   const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
   if (ncol0 >= sg.N) return;
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (sg.a_wide) {  // A in 64-column planes (checked by the launcher: K % 64 == 0)
+      switch (tile_layout(ti.nrows)) {
+        case 2: big_tile<BN, WN, EPI, 2, WDT, true>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+        case 1: big_tile<BN, WN, EPI, 1, WDT, true>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+        default: big_tile<BN, WN, EPI, 0, WDT, true>(a, ti, sg, wk, ncol0, lds, lds_sc);
+      }
+      return;
+    }
+  }
   switch (tile_layout(ti.nrows)) {
-    case 2: big_tile<BN, WN, EPI, 2, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
-    case 1: big_tile<BN, WN, EPI, 1, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
-    default: big_tile<BN, WN, EPI, 0, WDT>(a, ti, sg, wk, ncol0, lds, lds_sc);
+    case 2: big_tile<BN, WN, EPI, 2, WDT, false>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    case 1: big_tile<BN, WN, EPI, 1, WDT, false>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
+    default: big_tile<BN, WN, EPI, 0, WDT, false>(a, ti, sg, wk, ncol0, lds, lds_sc);
   }
 #endif
 }

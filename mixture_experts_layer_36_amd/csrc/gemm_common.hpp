@@ -24,6 +24,7 @@ struct Seg {
   int N, K;
   const int32_t* amap;      // routed rows through the row map (NULL: rows in order)
   int a_prows;              // A K-blocked with planes of a_prows rows (0: row-major)
+  int a_wide;               // ... of 64 columns (else 32)
   int c_prows;              // C K-blocked likewise (0: row-major)
   int b_blk;                // B0/B1 K-blocked with planes of N rows
 };
@@ -60,6 +61,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.K = a.shK;
     sg.amap = nullptr;
     sg.a_prows = a.sh_a_blk ? a.sh_rows : 0;
+    sg.a_wide = a.sh_a_blk == 2;
     sg.c_prows = a.c_blk ? a.sh_rows : 0;
     sg.b_blk = 0;
     return ti.nrows > 0;
@@ -83,6 +85,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.K = a.K;
   sg.amap = a.a_map;
   sg.a_prows = a.a_blk ? (a.a_map ? a.a_map_rows : a.rows) : 0;
+  sg.a_wide = a.a_blk == 2;
   sg.c_prows = a.c_blk ? a.rows : 0;
   sg.b_blk = a.b_blk;
   return ti.nrows > 0;

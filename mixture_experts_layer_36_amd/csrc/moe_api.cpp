@@ -258,17 +258,21 @@ bool fuse_gather(const moe_desc* d) {
   return !gather_blocked(d) && size_t(d->T) * size_t(d->d) * act_bytes(d) < (size_t(1) << 31);
 }
 // With the fused gather on the prefill kernel in bf16, the layer first copies
-// x into K-blocked planes in token order ([d/32][T][32]); the gate-up GEMM
+// x into K-blocked planes in token order ([d/64][T][64]); the gate-up GEMM
 // reads its routed rows from them through perm_token and the shared
-// segment's rows in order.  A tile's rows are an expert's tokens in
-// increasing order, so for a popular expert neighbouring rows are mostly
-// neighbouring tokens, whose 64-byte pieces of a plane share cache lines;
-// the copy is x-sized (not T*k*d like x_perm), so it stays in the Infinity
-// Cache.  DeepSeek-V3-shaped prefill: gate-up 8314 -> 7557 us for a 77 us
-// copy; the Qwen-shaped layer: neutral.
+// segment's rows in order.  The copy is x-sized (not T*k*d like x_perm), so
+// it stays in the Infinity Cache.  With 32-column planes (DeepSeek-V3-shaped
+// prefill: gate-up 8314 -> 7557 us for a 77 us copy) a row's piece of a plane
+// was half a cache line: a tile's rows are an expert's tokens in increasing
+// order, so neighbouring rows share a line only when both tokens chose the
+// expert (78% of the bytes fetched were used on that layer, 72% on the
+// Qwen-shaped one).  With 64-column planes (d is a multiple of 128) each
+// piece is a whole 128-byte line, and the gate-up GEMM loads two stages' A
+// per load.
 bool x_blocked(const moe_desc* d) {
   return d->act == MOE_BF16 && !d->dispatch_fp8 && fuse_gather(d) && block_m(d) == 256;
 }
+
 // The layer's h between the routed GEMMs in K-blocked planes (GemmArgs::c_blk
 // then a_blk): when the prefill kernel runs both in bf16, so each stage of the
 // down projection reads one contiguous run per 32-column slice.  The matrices
@@ -364,7 +368,7 @@ moe_status run_dispatch(const moe_desc* d, const int32_t* idx, const void* x, in
   MOE_TRY(dev(rr ? launch_dispatch_reroute(a, *rr, s) : launch_dispatch_index(a, s)));
   if (x_perm == nullptr) return MOE_OK;  // fused gather: GEMM1 reads x through perm_token
   // the gather stops at offsets[E] (the rows kept), read on the device
-  if (blocked) return dev(launch_gather_rows_blocked(x, perm_token, int(n_assign(d)), offsets + d->E, d->d, x_perm, s));
+  if (blocked) return dev(launch_gather_rows_blocked(x, perm_token, int(n_assign(d)), offsets + d->E, d->d, 32, x_perm, s));
   return dev(launch_gather_rows(x, perm_token, int(n_assign(d)), offsets + d->E, int(d->d * act_bytes(d)),
                                 x_perm, s));
 }
@@ -404,8 +408,8 @@ struct SharedSeg {
 moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map, const int32_t* offsets,
                          const void* w1, const void* w3, const float* s1, const float* s3, void* h,
                          const FfnWs& ws, hipStream_t s, const SharedSeg* sh = nullptr,
-                         const uint8_t* a_scales = nullptr, bool h_blk = false, bool a_blk = false,
-                         bool sh_a_blk = false) {
+                         const uint8_t* a_scales = nullptr, bool h_blk = false, int a_blk = 0,
+                         int sh_a_blk = 0) {
   GemmArgs g{};
   g.b_blk = d->w_layout == MOE_W_KBLOCKED;
   g.a_blk = a_blk;
@@ -785,7 +789,7 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   // token order when the gather is fused, else gathered), as codes when the
   // GEMM takes fp8 activations, else as bf16 values
   const bool xb = x_blocked(d);
-  if (xb) MOE_TRY(dev(launch_gather_rows_blocked(x, nullptr, d->T, nullptr, d->d, w.xb, s)));
+  if (xb) MOE_TRY(dev(launch_gather_rows_blocked(x, nullptr, d->T, nullptr, d->d, 64, w.xb, s)));
   const void* a_rows = xb ? w.xb : fg ? x : w.x_perm;
   const uint8_t* a_scales = nullptr;
   if (d->dispatch_fp8) {
@@ -809,8 +813,11 @@ moe_status moe_layer_forward(const moe_desc* d, const void* x, const void* w_rou
   MOE_TRY(run_tables(d, w.offsets, w.ffn, s, fused));
   const bool hb = h_blocked(d);
   MOE_TRY(record(trace, 2, s));
+  // A (and the shared segment's x) K-blocked: 64-column planes for the copy
+  // of x, 32 for the gathered x_perm
+  const int ablk = xb ? 2 : gb ? 1 : 0;
   MOE_TRY(run_ffn_gemm1(d, a_rows, fg ? w.perm_token : nullptr, w.offsets, w1, w3, s1, s3, w.h, w.ffn, s,
-                        fused ? &sh : nullptr, a_scales, hb, gb || xb, xb));
+                        fused ? &sh : nullptr, a_scales, hb, ablk, xb ? ablk : 0));
   MOE_TRY(record(trace, 3, s));
   MOE_TRY(run_ffn_gemm2(d, w.h, w.offsets, w2, s2, w.y_perm, w.ffn, s, fused ? &sh : nullptr, hb));
   MOE_TRY(record(trace, 4, s));

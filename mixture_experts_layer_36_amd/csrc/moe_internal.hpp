@@ -142,10 +142,11 @@ hipError_t launch_segment_rows(const int32_t* offsets, int E, int32_t* rows, hip
 // row count, nullable), rows of row_bytes (multiple of 16).
 hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
                               int row_bytes, void* x_perm, hipStream_t s);
-// The same rows into the K-blocked planes of GemmArgs::a_blk (P = rows): bf16,
-// d a multiple of 32; perm_token NULL copies x's rows in order.
+// The same rows into the K-blocked planes of GemmArgs::a_blk (P = rows) of
+// width pw = 32 or 64: bf16, d a multiple of pw; perm_token NULL copies x's
+// rows in order.
 hipError_t launch_gather_rows_blocked(const void* x, const int32_t* perm_token, int rows, const int32_t* rows_dev,
-                                      int d, void* x_perm, hipStream_t s);
+                                      int d, int pw, void* x_perm, hipStream_t s);
 
 // The block-scaled E4M3 dispatch payload (fp8_payload.hip): bf16 rows cut
 // into blocks of 32 elements, each block one E8M0 scale 2^s (s smallest with
@@ -232,13 +233,14 @@ struct GemmArgs {
   const uint8_t* a_scales;
   int a_sstride;
   // Prefill kernel only, bf16: K-blocked operands.  A K-blocked matrix of P
-  // rows and K columns is K/32 planes of [P][32] elements, element (r, k) at
-  // (k / 32) * P * 32 + r * 32 + k % 32, so the 32-column slice of a tile's
-  // rows is one contiguous run.  a_blk: A in this layout with P = rows, or,
-  // with a row map, P = a_map_rows (the map indexes the planes' rows);
-  // sh_a_blk: the extra segment's shA with P = sh_rows.  c_blk (SwiGLU
-  // only): C with P = rows and shC with P = sh_rows.  Each matrix must stay
-  // under 2^31 bytes.
+  // rows and K columns is K/W planes of [P][W] elements (plane width W = 32,
+  // or 64 for the wide form), element (r, k) at (k / W) * P * W + r * W +
+  // k % W, so the W-column slice of a tile's rows is one contiguous run.
+  // a_blk: 0, or A in this layout with W = 32 (1) or 64 (2, SwiGLU only, K a
+  // multiple of 64), P = rows, or, with a row map, P = a_map_rows (the map
+  // indexes the planes' rows); sh_a_blk: likewise the extra segment's shA
+  // with P = sh_rows.  c_blk (SwiGLU only): C with W = 32 and P = rows, and
+  // shC with P = sh_rows.  Each matrix must stay under 2^31 bytes.
   int a_blk;
   int sh_a_blk;
   int c_blk;

@@ -107,6 +107,10 @@ CASES = {
     # 1040: 16 rows, with the group limit and a shared expert)
     "router_big_e256_qtail": QWEN_FP8_SKEW.scaled(T=1050, d=512, f=128, E=256, k=4),
     "router_big_dsv3_qtail": DSV3_PREFILL_SKEW.scaled(T=1040, d=512, f=128, E=256, f_shared=128),
+    # the token-order K-blocked copy of x (64-column planes, read two stages
+    # per load) at d = 1024: the last wave's tiles split along K into pieces
+    # of whole stage pairs
+    "xblk_wide_split": DSV3_PREFILL_SKEW.scaled(T=1100, d=1024, f=256, E=16, k=4, f_shared=0),
     # group limits in the selection kernel: groups of 64 and of 2 (64 groups)
     # ranked in registers, groups of 48 (not a power of two) through LDS
     "group_g64": DSV3_PREFILL_SKEW.scaled(T=64, d=256, f=256, E=256, n_group=4, topk_group=2, f_shared=0),
