@@ -104,6 +104,20 @@ def parse():
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="summarise rocprofv3 --pmc counter CSVs under DIR (no GPU): per kernel, the mean of "
                         "each counter over the dispatches of the timed steps (--warmup / --steps as above)")
+    p.add_argument("--write-traffic", metavar="WORKLOAD", default=None,
+                   help="(no GPU) HBM bytes per launch of --kernel from rocprofv3 --pmc FETCH_SIZE (--fetch DIR) "
+                        "and WRITE_SIZE (--write DIR) passes of the timed steps, each scaled by what the same "
+                        "counter reads for --calibrate-copy (--copy-fetch DIR, --copy-write DIR); written into "
+                        "profiles/traffic.json with the kernel source hash, and the algorithmic bytes from the "
+                        "experts the --bench-line JSON of the same build touched")
+    p.add_argument("--kernel", default=None, help="with --write-traffic: kernel name substring ('*': every kernel "
+                                                  "the --pmc runs collected, i.e. those of one layer step)")
+    p.add_argument("--fetch", default=None)
+    p.add_argument("--write", default=None)
+    p.add_argument("--copy-fetch", default=None)
+    p.add_argument("--copy-write", default=None)
+    p.add_argument("--bench-line", default=None)
+    p.add_argument("--profile", default=None, help="with --write-traffic: the trace summary the entry refers to")
     p.add_argument("--summarize-trace", metavar="DIR", default=None,
                    help="summarise a rocprofv3 --kernel-trace CSV under DIR (no GPU): per-kernel calls and "
                         "average, and the steady-state average over the timed steps given by --warmup and "
@@ -131,13 +145,14 @@ def progress(msg: str):
 
 # ------------------------------------------------------------ algorithmic work
 
-def layer_bytes(w, counts) -> float:
+def layer_bytes(w, counts=None, touched=None) -> float:
     """Algorithmic HBM bytes of one layer forward: x, router weight and bias,
     the touched experts' weights (+ scales), the shared expert, out, and the
     routing outputs (topk idx + w)."""
     ab = 4 if w.act == "f32" else 2
     wb = {"f32": 4, "bf16": 2, "e4m3": 1}[w.wdt]
-    touched = int((counts > 0).sum())
+    if touched is None:
+        touched = int((counts > 0).sum())
     per_expert = 3 * w.d * w.f * wb + (2 * w.f + w.d) * 4 * (w.wdt == "e4m3")
     b = w.T * w.d * ab * 2 + w.E * w.d * ab + w.E * 4 + touched * per_expert
     b += 3 * w.d * w.f_shared * ab + 8 * w.T * w.k
@@ -166,6 +181,93 @@ def gathers_blocked(w) -> bool:
     rows = w.T * w.k
     return (w.act == "bf16" and not w.dispatch_fp8 and w.f >= 4096 and rows >= 1024
             and rows // w.E >= 128 and rows * w.d * 2 < (1 << 31))
+
+
+def gate_up_bytes(w, touched: int) -> tuple:
+    """Algorithmic HBM (read, write) bytes of the gate-up launch: the routed
+    rows of x (T*k of them, as the fp8 payload where the launch takes it) and
+    the touched experts' W1 and W3 (+ fp8 scales)
+    read, h written; with the shared expert fused into the launch, also x and
+    its W1, W3 read and its h written."""
+    ab = 4 if w.act == "f32" else 2
+    wb = {"f32": 4, "bf16": 2, "e4m3": 1}[w.wdt]
+    rows = w.T * w.k
+    # a routed row: bf16 x, or (fp8 x fp8 gate-up) its E4M3 codes and E8M0 scale row
+    row_b = w.d + (w.d // 32 + 15) // 16 * 16 if fp8_gate_up(w) else w.d * ab
+    rd = rows * row_b + touched * (2 * w.f * w.d * wb + 2 * w.f * 4 * (w.wdt == "e4m3"))
+    wr = rows * w.f * ab
+    if shared_fused(w):
+        rd += w.T * w.d * ab + 2 * w.f_shared * w.d * ab
+        wr += w.T * w.f_shared * ab
+    return float(rd), float(wr)
+
+
+def _counter_per_step(d: str, counter: str, kernel: str, warmup: int, steps: int) -> float:
+    """Sum of `counter` over the dispatches of the kernels whose name holds
+    `kernel` ('*': all) in the timed steps of a --pmc run, divided by steps: the
+    value per launch when one such kernel runs per step."""
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}  # kernel -> {dispatch: value}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter or (kernel != "*" and kernel not in row["Kernel_Name"]):
+                    continue
+                dd = per.setdefault(row["Kernel_Name"], {})
+                key = (f, int(row["Dispatch_Id"]))
+                dd[key] = dd.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernel {kernel!r} under {d}")
+    total = 0.0
+    for name, dd in per.items():
+        v = [x for _, x in sorted(dd.items())]
+        if len(v) % (warmup + steps):
+            raise SystemExit(f"{name}: {len(v)} dispatches do not split into {warmup} + {steps} steps")
+        total += sum(v[len(v) // (warmup + steps) * warmup:])
+    return total / steps
+
+
+def write_traffic(args):
+    """profiles/traffic.json entry of one workload (see --write-traffic)."""
+    from synth import BY_NAME
+    name = args.write_traffic
+    w = BY_NAME[name.split("+")[0]]
+    if name.endswith("+dispatch_fp8"):
+        w = w.scaled(dispatch_fp8=True)
+    fetch = _counter_per_step(args.fetch, "FETCH_SIZE", args.kernel, args.warmup, args.steps)
+    write = _counter_per_step(args.write, "WRITE_SIZE", args.kernel, args.warmup, args.steps)
+    # the copy calibration: the 3 launches of the runtime's 1 GiB device copy
+    cf = _counter_per_step(args.copy_fetch, "FETCH_SIZE", "copyBuffer", 0, 3)
+    cw = _counter_per_step(args.copy_write, "WRITE_SIZE", "copyBuffer", 0, 3)
+    n = 1 << 30
+    rf, wf = n / (cf * 1024), n / (cw * 1024)
+    ent = {"kernel": args.kernel if args.kernel != "*" else "whole layer (all kernels of one moe_layer_forward)",
+           "source_hash": kernel_source_hash(),
+           "read_bytes": round(fetch * 1024 * rf), "write_bytes": round(write * 1024 * wf),
+           "fetch_size_kib": fetch, "write_size_kib": write,
+           "copy_calibration": {"bytes": n, "read_factor": rf, "write_factor": wf}}
+    ent["bytes_per_launch"] = ent["read_bytes"] + ent["write_bytes"]
+    if args.bench_line:
+        with open(args.bench_line) as fh:
+            line = json.loads(fh.read().strip().splitlines()[-1])
+        touched = line["load"]["experts_touched"]
+        if args.kernel == "*":
+            ent["algorithmic_bytes"] = layer_bytes(w, touched=touched)
+        else:
+            ent["algorithmic_read_bytes"], ent["algorithmic_write_bytes"] = gate_up_bytes(w, touched)
+    if args.profile:
+        ent["profile"] = args.profile
+    tr = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+    tr[name] = ent
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(tr, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({name: ent}, indent=1))
 
 
 def stage_bytes(w, has_bias: bool, kept: int) -> dict:
@@ -726,6 +828,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.warmup, args.steps)
+        return
+    if args.write_traffic:
+        write_traffic(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "

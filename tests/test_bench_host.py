@@ -1,6 +1,8 @@
 """bench.py's host logic, without a GPU: the one-GPU refusal, the rocprofv3
 trace summary (steady-state averages over the timed steps) and the
 algorithmic-work formulas the roofline divides by."""
+import argparse
+import json
 import os
 import subprocess
 import sys
@@ -81,3 +83,38 @@ def test_power_summary_window_and_unavailable_readings():
     r = bench.PowerSampler.summarize(samples, 0.5, 3.0, cap_w=1400.0)
     assert r == {"socket_power_w_median": 1395.0, "gfxclk_mhz_median": 1650.0, "power_cap_w": 1400.0, "samples": 3}
     assert bench.PowerSampler.summarize(samples, 5.0, 6.0) is None
+
+
+def test_write_traffic_scales_by_the_copy_and_keeps_timed_steps(tmp_path, monkeypatch):
+    # gate-up kernel G once per step (1 warm-up + 2 timed), one other kernel O;
+    # the copy run: one fill kernel and 3 copies of 1 GiB whose counters read
+    # half the bytes (read factor 2) and all of them (write factor 1)
+    def pmc(d, counter, rows):
+        d.mkdir()
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        lines += [f"{i},\"{k}\",{counter},{v}" for i, (k, v) in enumerate(rows)]
+        (d / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    G = "gemm_big_kernel<256, 2, 1, 1>(moe::GemmArgs)"
+    pmc(tmp_path / "f", "FETCH_SIZE", [(G, 9e9), ("O", 1.0), (G, 100.0), ("O", 1.0), (G, 300.0), ("O", 1.0)])
+    pmc(tmp_path / "w", "WRITE_SIZE", [(G, 9e9), (G, 10.0), (G, 30.0)])
+    gib_kib = float(1 << 20)
+    pmc(tmp_path / "cf", "FETCH_SIZE", [("fill", 5.0)] + [("__amd_rocclr_copyBuffer", gib_kib / 2)] * 3)
+    pmc(tmp_path / "cw", "WRITE_SIZE", [("fill", 5.0)] + [("__amd_rocclr_copyBuffer", gib_kib)] * 3)
+    line = tmp_path / "line.json"
+    line.write_text('{"load": {"experts_touched": 76}}\n')
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    args = argparse.Namespace(write_traffic="dsv3_prefill_skew_bf16", kernel="gemm_big_kernel<256, 2, 1, 1>",
+                              fetch=str(tmp_path / "f"), write=str(tmp_path / "w"), copy_fetch=str(tmp_path / "cf"),
+                              copy_write=str(tmp_path / "cw"), bench_line=str(line), profile=None, warmup=1, steps=2)
+    bench.write_traffic(args)
+    ent = json.loads(out.read_text())["dsv3_prefill_skew_bf16"]
+    assert ent["fetch_size_kib"] == 200.0 and ent["write_size_kib"] == 20.0
+    assert ent["copy_calibration"]["read_factor"] == 2.0 and ent["copy_calibration"]["write_factor"] == 1.0
+    assert ent["read_bytes"] == 200 * 1024 * 2 and ent["write_bytes"] == 20 * 1024
+    assert ent["source_hash"] == bench.kernel_source_hash()
+    w = BY_NAME["dsv3_prefill_skew_bf16"]
+    # routed rows + 76 experts' W1, W3 + the fused shared expert's x, W1, W3
+    rd = w.T * w.k * w.d * 2 + 76 * 2 * w.f * w.d * 2 + w.T * w.d * 2 + 2 * w.f_shared * w.d * 2
+    assert ent["algorithmic_read_bytes"] == rd == 6635388928
+    assert ent["algorithmic_write_bytes"] == (w.T * w.k * w.f + w.T * w.f_shared) * 2
