@@ -61,6 +61,9 @@ CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_36_amd", "lib", "libmoe_ca
 DEFAULT_WORKLOAD = "dsv3_prefill_skew_bf16"
 DECODE_WORKLOAD = "dsv3_decode_bf16"
 DECODE_WORKLOADS = {"dsv3_decode_bf16"}
+# the decode leg times this many steps per prefill step: at least 100 with the
+# default 20 (a decode step is ~4 ms)
+DECODE_STEPS_PER_STEP = 5
 EVICT_BYTES = 512 << 20
 XCDS = 8  # MI355X: 8 XCDs of 32 compute units
 # oracle tokens timed per workload: about 10 s of float64 compute on a
@@ -889,13 +892,13 @@ def main():
         # the decode-shaped layer, bound by HBM bandwidth: its own steps
         # (more of them: a step is ~4 ms), no cold repetitions
         wd = BY_NAME[DECODE_WORKLOAD]
-        d_rec, _, _ = measure(wd, DEFAULT_SEED[wd.name], args, steps=4 * args.steps, warmup=args.warmup,
-                              cold=False)
+        d_rec, _, _ = measure(wd, DEFAULT_SEED[wd.name], args, steps=DECODE_STEPS_PER_STEP * args.steps,
+                              warmup=args.warmup, cold=False)
         r = d_rec["roofline"]
         if ceil:
             r["frac_of_measured_read_ceiling"] = round(r["achieved"] / ceil["stream_read_gbs"], 4)
         line["decode"] = {"metric": "MoE-layer tokens/s per MI355X; decode % HBM BW",
-                          "value": d_rec["value"], "unit": "tokens/s", "steps": 4 * args.steps,
+                          "value": d_rec["value"], "unit": "tokens/s", "steps": DECODE_STEPS_PER_STEP * args.steps,
                           "ms_per_step": d_rec["ms_per_step"], "config": d_rec["config"], "roofline": r,
                           "stages_us": d_rec["stages_us"], "stages_gbps": d_rec["stages_gbps"],
                           "load": d_rec["load"], "sustained": d_rec["sustained"]}
