@@ -836,7 +836,7 @@ def main():
         write_traffic(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch  # noqa: F401
