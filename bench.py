@@ -232,6 +232,21 @@ def _counter_per_step(d: str, counter: str, kernel: str, warmup: int, steps: int
     return total / steps
 
 
+# How the counter passes behind profiles/traffic.json are taken (repository
+# root, on the GPU); <wl> is the workload, <flags> e.g. --dispatch-fp8.
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_f> -o run -- python3 bench.py --calibrate-copy",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_w> -o run -- python3 bench.py --calibrate-copy",
+    "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex gemm_big --output-format csv -d <f> -o run -- python3 bench.py "
+    "--no-cpu-baseline --no-decode-leg --no-cold --no-ceilings --sustain-seconds 0 --workload <wl> <flags> --steps 2 "
+    "--warmup 1   (WRITE_SIZE into <w> likewise; the decode layer: --kernel-include-regex 'moe::' "
+    "--kernel-exclude-regex 'pack_kblocked|segment_rows')",
+    "python bench.py --write-traffic <wl>[+dispatch_fp8] --kernel '<gate-up kernel name>' (or '*') --fetch <f> "
+    "--write <w> --copy-fetch <copy_f> --copy-write <copy_w> --bench-line <that workload's bench.py JSON line> "
+    "--warmup 1 --steps 2",
+]
+
+
 def write_traffic(args):
     """profiles/traffic.json entry of one workload (see --write-traffic)."""
     from synth import BY_NAME
@@ -266,6 +281,7 @@ def write_traffic(args):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
             tr = json.load(fh)
+    tr["_commands"] = TRAFFIC_COMMANDS
     tr[name] = ent
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(tr, fh, indent=1)
