@@ -230,11 +230,11 @@ struct Work {
 // pieces follow, again an equal share per XCD, so they all run in the last
 // wave.
 [[maybe_unused]] __device__ __forceinline__ bool big_work(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu,
-                                         int BMv, Work& w) {
+                                         int BMv, Work& w, int bid) {
   const int m_real = real_mtiles(a, BMv);
   const int R = m_real * n_tiles;
   const SplitPlan p = split_plan(R, kt_plan, n_cu, a.partial ? a.partial_slots : 0);
-  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int x = bid & 7, i = bid >> 3;
   int L;
   w.slot = -1;
   w.k0num = 0;
@@ -256,6 +256,52 @@ struct Work {
   }
   tile_coords(L, m_real, n_tiles, w.mt, w.nt);
   return true;
+}
+
+// Block bid's tile, K-piece and rows: from its record when a schedule kernel
+// wrote one for every block of the launch (gridDim.x <= sched_cap), else
+// derived here.  A record holds mt, nt, k0num, slot, s, e, row0, nrows (mt < 0:
+// no work); one that does not fit the segment it names is treated as empty.
+template <int BMv>
+__device__ __forceinline__ bool big_block(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu, int ncols,
+                                          Work& wk, TileInfo& ti, Seg& sg) {
+  if (a.sched != nullptr && a.tile_table != nullptr && (int)gridDim.x <= a.sched_cap) {
+    const int4* r = (const int4*)(a.sched + (size_t)blockIdx.x * kSchedInts);
+    const int4 r0 = r[0], r1 = r[1];
+    wk.mt = __builtin_amdgcn_readfirstlane(r0.x);
+    wk.nt = __builtin_amdgcn_readfirstlane(r0.y);
+    wk.k0num = __builtin_amdgcn_readfirstlane(r0.z);
+    wk.slot = __builtin_amdgcn_readfirstlane(r0.w);
+    wk.s = __builtin_amdgcn_readfirstlane(r1.x);
+    ti.e = __builtin_amdgcn_readfirstlane(r1.y);
+    ti.row0 = __builtin_amdgcn_readfirstlane(r1.z);
+    ti.nrows = __builtin_amdgcn_readfirstlane(r1.w);
+    if (wk.mt < 0 || ti.e < 0 || ti.e > a.E || ti.nrows <= 0 || ti.nrows > BMv || ti.row0 < 0) return false;
+    if (ti.row0 + ti.nrows > (ti.e == a.E ? a.sh_rows : a.rows)) return false;
+    tile_seg(a, ti, sg);
+    return wk.nt * ncols < sg.N;
+  }
+  if (!big_work(a, n_tiles, kt_plan, n_cu, BMv, wk, blockIdx.x)) return false;
+  if (!tile_info(a, wk.mt, BMv, ti, sg)) return false;
+  return wk.nt * ncols < sg.N;
+}
+
+// One thread per block of the GEMM launch: the record big_block reads.
+__global__ __launch_bounds__(256) void big_sched_kernel(GemmArgs a, int n_tiles, int kt_plan, int n_cu, int BMv,
+                                                        int ncols, int nb) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= nb) return;
+  Work wk;
+  TileInfo ti;
+  Seg sg;
+  int4 r0 = make_int4(-1, 0, 0, -1), r1 = make_int4(1, 0, 0, 0);
+  if (big_work(a, n_tiles, kt_plan, n_cu, BMv, wk, b) && tile_info(a, wk.mt, BMv, ti, sg) && wk.nt * ncols < sg.N) {
+    r0 = make_int4(wk.mt, wk.nt, wk.k0num, wk.slot);
+    r1 = make_int4(wk.s, ti.e, ti.row0, ti.nrows);
+  }
+  int4* r = (int4*)(a.sched + (size_t)b * kSchedInts);
+  r[0] = r0;
+  r[1] = r1;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -773,12 +819,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + SC];
   float* lds_sc = (float*)(lds + MAIN);
   Work wk;
-  if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
   Seg sg;
-  if (!tile_info(a, wk.mt, BM, ti, sg)) return;
-  const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
-  if (ncol0 >= sg.N) return;
+  constexpr int NCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  if (!big_block<BM>(a, n_tiles, kt_plan, n_cu, NCOLS, wk, ti, sg)) return;
+  const int ncol0 = wk.nt * NCOLS;
   if constexpr (EPI == EPI_SWIGLU) {
     if (sg.a_wide) {  // A in 64-column planes (checked by the launcher: K % 64 == 0)
       switch (tile_layout(ti.nrows)) {
@@ -1063,12 +1108,11 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
   __shared__ __attribute__((aligned(1024))) char lds[MAIN + BN * 4];  // + the tile's channel scales
   float* lds_sc = (float*)(lds + MAIN);
   Work wk;
-  if (!big_work(a, n_tiles, kt_plan, n_cu, BM, wk)) return;
   TileInfo ti;
   Seg sg;
-  if (!tile_info(a, wk.mt, BM, ti, sg)) return;
-  const int ncol0 = wk.nt * (EPI == EPI_SWIGLU ? BN / 2 : BN);
-  if (ncol0 >= sg.N) return;
+  constexpr int NCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  if (!big_block<BM>(a, n_tiles, kt_plan, n_cu, NCOLS, wk, ti, sg)) return;
+  const int ncol0 = wk.nt * NCOLS;
   switch (tile_layout(ti.nrows)) {
     case 2: big_tile_fp8<BN, WN, EPI, 2>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
     case 1: big_tile_fp8<BN, WN, EPI, 1>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
@@ -1207,6 +1251,15 @@ hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   // whole tiles plus at most one wave of pieces, 8 XCD shares rounded up
   int nb = n_slots * n_tiles + (n_cu > 0 ? n_cu + 8 : 0);
   nb = (nb + 7) & ~7;
+  // Each block's tile resolved ahead by one thread per block (the tile
+  // table's real m-tile count, the grouped order and split plan, the table
+  // entry and the segment's offsets), so a GEMM block starts from one record
+  // instead of a chain of dependent loads and divisions.
+  if (a.sched != nullptr && a.tile_table != nullptr && a.ksplit == 1 && nb <= a.sched_cap)
+    hipLaunchKernelGGL(big_sched_kernel, dim3((nb + 255) / 256), dim3(256), 0, s, a, n_tiles, kt_plan, n_cu, BM,
+                       ncol, nb);
+  else
+    a.sched = nullptr;
   if constexpr (FP8ACT)
     hipLaunchKernelGGL((gemm_big_fp8_kernel<BN, WN, EPI>), dim3(nb), dim3(128 * WN), 0, s, a, n_tiles, kt_plan,
                        n_cu);

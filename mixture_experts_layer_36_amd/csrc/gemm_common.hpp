@@ -36,22 +36,10 @@ __device__ __forceinline__ int a_row(const Seg& sg, int row0, int r) {
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == GD_F32 ? 4 : dt == GD_BF16 ? 2 : 1; }
 
-// m-tile slot -> (segment, first row, rows in the tile) and its operands;
-// false for empty slots.
-__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti, Seg& sg) {
-  int tile;
-  if (a.tile_table == nullptr) {
-    ti.e = 0;
-    tile = mt;
-  } else {
-    const int code = a.tile_table[mt];
-    if (code < 0) return false;
-    ti.e = code >> kTableExpertShift;
-    tile = code & kTableTileMask;
-  }
+// The operands of segment ti.e (a.E with a tile table: the extra, shared
+// segment), from the arguments alone.
+__device__ __forceinline__ void tile_seg(const GemmArgs& a, const TileInfo& ti, Seg& sg) {
   if (a.tile_table != nullptr && ti.e == a.E) {  // the extra (shared) segment
-    ti.row0 = tile * BM;
-    ti.nrows = min(BM, a.sh_rows - ti.row0);
     sg.A = (const char*)a.shA;
     sg.B0 = (const char*)a.shB0;
     sg.B1 = (const char*)a.shB1;
@@ -64,15 +52,7 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
     sg.a_wide = a.sh_a_blk == 2;
     sg.c_prows = a.c_blk ? a.sh_rows : 0;
     sg.b_blk = 0;
-    return ti.nrows > 0;
-  }
-  if (a.tile_table == nullptr) {
-    ti.row0 = tile * BM;
-    ti.nrows = min(BM, a.rows - ti.row0);
-  } else {
-    const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
-    ti.row0 = lo + tile * BM;
-    ti.nrows = min(BM, hi - ti.row0);
+    return;
   }
   const size_t woff = (size_t)ti.e * a.N * a.K * dtype_bytes(a.wdt);
   sg.A = (const char*)a.A;
@@ -88,7 +68,40 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, Til
   sg.a_wide = a.a_blk == 2;
   sg.c_prows = a.c_blk ? a.rows : 0;
   sg.b_blk = a.b_blk;
+}
+
+// m-tile slot -> (segment, first row, rows in the tile); false for empty
+// slots.
+__device__ __forceinline__ bool tile_rows(const GemmArgs& a, int mt, int BM, TileInfo& ti) {
+  int tile;
+  if (a.tile_table == nullptr) {
+    ti.e = 0;
+    tile = mt;
+  } else {
+    const int code = a.tile_table[mt];
+    if (code < 0) return false;
+    ti.e = code >> kTableExpertShift;
+    tile = code & kTableTileMask;
+  }
+  if (a.tile_table != nullptr && ti.e == a.E) {  // the extra (shared) segment
+    ti.row0 = tile * BM;
+    ti.nrows = min(BM, a.sh_rows - ti.row0);
+  } else if (a.tile_table == nullptr) {
+    ti.row0 = tile * BM;
+    ti.nrows = min(BM, a.rows - ti.row0);
+  } else {
+    const int lo = a.offsets[ti.e], hi = a.offsets[ti.e + 1];
+    ti.row0 = lo + tile * BM;
+    ti.nrows = min(BM, hi - ti.row0);
+  }
   return ti.nrows > 0;
+}
+
+// m-tile slot -> its rows and operands; false for empty slots.
+__device__ __forceinline__ bool tile_info(const GemmArgs& a, int mt, int BM, TileInfo& ti, Seg& sg) {
+  if (!tile_rows(a, mt, BM, ti)) return false;
+  tile_seg(a, ti, sg);
+  return true;
 }
 
 // Number of real m-tiles: the tile table stores it after its n_slots entries.

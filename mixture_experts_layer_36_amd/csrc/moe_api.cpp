@@ -186,6 +186,8 @@ struct FfnWs {
   int n_slots;
   float* partial;     // K-split partial sums of the prefill kernel (NULL: not used)
   int partial_slots;
+  int32_t* sched;     // block records of the prefill kernel (NULL: not used)
+  int sched_cap;
 };
 struct LayerWs {
   RouteWs route;
@@ -235,9 +237,20 @@ FfnWs carve_ffn(Carve& c, const moe_desc* d, bool with_shared) {
   w.table = c.take<int32_t>(sizeof(int32_t) * size_t(w.n_slots + 1));
   w.partial = nullptr;
   w.partial_slots = 0;
+  w.sched = nullptr;
+  w.sched_cap = 0;
   if (block_m(d) == 256) {  // the prefill kernel splits its last wave of tiles
     w.partial = c.take<float>(kPartialSlotBytes * kPartialSlots);
     w.partial_slots = kPartialSlots;
+    // one record per block of either routed GEMM: n-tiles of at least 128
+    // output columns, plus a wave of K-pieces (at most one per compute unit;
+    // 2048 covers any CU count the split plan can use)
+    const int cols = std::max(std::max(d->f, d->f_shared), d->d);
+    const int64_t cap = int64_t(w.n_slots) * ((cols + 127) / 128) + 2048;
+    if (cap < (int64_t(1) << 30)) {
+      w.sched = c.take<int32_t>(sizeof(int32_t) * kSchedInts * size_t(cap));
+      w.sched_cap = int(cap);
+    }
   }
   return w;
 }
@@ -437,6 +450,8 @@ moe_status run_ffn_gemm1(const moe_desc* d, const void* A, const int32_t* a_map,
   g.n_slots = ws.n_slots;
   g.partial = ws.partial;
   g.partial_slots = ws.partial_slots;
+  g.sched = ws.sched;
+  g.sched_cap = ws.sched_cap;
   g.B0 = w1;
   g.B1 = w3;
   g.s0 = s1;
@@ -474,6 +489,8 @@ moe_status run_ffn_gemm2(const moe_desc* d, const void* h, const int32_t* offset
   g.n_slots = ws.n_slots;
   g.partial = ws.partial;
   g.partial_slots = ws.partial_slots;
+  g.sched = ws.sched;
+  g.sched_cap = ws.sched_cap;
   g.B0 = w2;
   g.s0 = s2;
   g.N = d->d;

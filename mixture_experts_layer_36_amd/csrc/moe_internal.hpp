@@ -247,7 +247,15 @@ struct GemmArgs {
   // Routed weights B0/B1 in the K-blocked layout (P = N per expert matrix);
   // the extra segment's weights are row-major.  bf16 / fp8 weights only.
   int b_blk;
+  // Prefill kernel with a tile table: room for sched_cap block records of
+  // kSchedInts ints.  A schedule kernel resolves each block's tile (m-tile,
+  // n-tile, K-piece, segment, rows) before the GEMM launch, and each GEMM
+  // block then reads its record instead of deriving it.  NULL, or fewer
+  // records than blocks: every block derives its own.
+  int32_t* sched;
+  int sched_cap;
 };
+constexpr int kSchedInts = 8;
 
 // Row-major [mats][rows][cols] -> K-blocked [mats][cols/32][rows][32] of
 // elem_bytes-byte elements (1 or 2).
