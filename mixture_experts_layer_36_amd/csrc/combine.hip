@@ -9,10 +9,12 @@
 // Figure 2).  No atomics: a token gathers its own k rows through inv_pos, so
 // the result is deterministic.  The sum runs j = 0..k-1, then the shared row;
 // an assignment dropped for capacity (inv_pos = -1) contributes nothing.
-// One block per token row, sized so a row takes two passes of 16-byte loads
-// and stores (448 threads for d = 7168: 3.5 passes of 256 left the last one
-// half idle; DeepSeek-V3-shaped prefill combine 430 -> 421 us); HBM-bound; a
-// thread has its k row loads in flight together.  The expert rows are read once and
+// One block per token row, a thread per 16-byte chunk of the row: one pass
+// of loads and stores (896 threads for d = 7168, 512 for d = 4096).  Against
+// 256-thread blocks (3.5 passes at d = 7168, the last one half idle) and
+// two-pass blocks, the DeepSeek-V3-shaped prefill combine went 430 -> 421 ->
+// 400 us and the Qwen-shaped one 108 -> 104 us.  HBM-bound; a thread has its
+// k row loads in flight together.  The expert rows are read once and
 // the output written once, so both go non-temporal (kept out of the caches
 // the next layer's data would use): DeepSeek-V3-shaped prefill combine
 // 473 -> 411 us, Qwen-shaped 123 -> 99 us.
@@ -27,7 +29,7 @@ constexpr int kMaxK = 16;
 // the shared row's) are issued before the first is consumed: one 16-byte
 // load per row in flight per thread rather than one in all.
 template <int KM>
-__global__ __launch_bounds__(512) void combine_bf16_kernel(CombineArgs a) {
+__global__ __launch_bounds__(1024) void combine_bf16_kernel(CombineArgs a) {
   __shared__ int s_row[kMaxK];
   __shared__ float s_g[kMaxK];
   const int t = blockIdx.x;
@@ -111,12 +113,12 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  // bf16: two passes over the row's 16-byte chunks, whole wavefronts, at
-  // least 64 threads (the first k threads stage the token's rows and gates)
-  // and at most 512
+  // bf16: a thread per 16-byte chunk of the row (more passes past 1024),
+  // whole wavefronts, at least 64 threads (the first k threads stage the
+  // token's rows and gates)
   const int nvec = a.d / 8;
-  int thr = ((nvec + 1) / 2 + 63) / 64 * 64;
-  thr = thr < 64 ? 64 : thr > 512 ? 512 : thr;
+  int thr = (nvec + 63) / 64 * 64;
+  thr = thr < 64 ? 64 : thr > 1024 ? 1024 : thr;
   if (a.act != GD_BF16)
     hipLaunchKernelGGL(combine_f32_kernel, dim3(a.T), dim3(256), 0, s, a);
   else if (a.k <= 2)
