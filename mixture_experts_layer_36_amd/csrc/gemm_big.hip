@@ -61,7 +61,14 @@
 //   * every buffer descriptor is built from block-uniform values stated
 //     uniform (readfirstlane): otherwise the compiler cannot prove a base
 //     computed on the vector unit uniform and wraps each load through it in a
-//     loop over distinct lane values.
+//     loop over distinct lane values;
+//   * with a tile table, a schedule kernel resolves every block's tile ahead
+//     of the launch (big_sched_kernel), so a block starts from one 32-byte
+//     record rather than three dependent loads and the integer divisions of
+//     the grouped order and split plan (DeepSeek-V3-shaped layer -0.6%);
+//   * the tile's outputs (h planes, y rows) go out with non-temporal stores:
+//     each is read once, by a later launch, and kept out of L2 they leave it
+//     to the operand tiles the blocks of an XCD share.
 #include <atomic>
 
 #include "gemm_common.hpp"
