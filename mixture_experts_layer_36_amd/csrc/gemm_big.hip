@@ -265,13 +265,19 @@ struct Work {
   return true;
 }
 
+// Rows per m-tile: 256, or a.m_tile (128) for a launch without a tile table
+// (the router logits, whose plan picks 128-row tiles where 256-row ones would
+// need short K ranges to fill the GPU).
+__host__ __device__ __forceinline__ int m_tile_rows(const GemmArgs& a) {
+  return (a.tile_table == nullptr && a.m_tile == BM / 2) ? BM / 2 : BM;
+}
+
 // Block bid's tile, K-piece and rows: from its record when a schedule kernel
 // wrote one for every block of the launch (gridDim.x <= sched_cap), else
 // derived here.  A record holds mt, nt, k0num, slot, s, e, row0, nrows (mt < 0:
 // no work); one that does not fit the segment it names is treated as empty.
-template <int BMv>
-__device__ __forceinline__ bool big_block(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu, int ncols,
-                                          Work& wk, TileInfo& ti, Seg& sg) {
+[[maybe_unused]] __device__ __forceinline__ bool big_block(const GemmArgs& a, int n_tiles, int kt_plan, int n_cu,
+                                                           int BMv, int ncols, Work& wk, TileInfo& ti, Seg& sg) {
   if (a.sched != nullptr && a.tile_table != nullptr && (int)gridDim.x <= a.sched_cap) {
     const int4* r = (const int4*)(a.sched + (size_t)blockIdx.x * kSchedInts);
     const int4 r0 = r[0], r1 = r[1];
@@ -829,7 +835,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_kernel(GemmArgs a, int n
   TileInfo ti;
   Seg sg;
   constexpr int NCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  if (!big_block<BM>(a, n_tiles, kt_plan, n_cu, NCOLS, wk, ti, sg)) return;
+  if (!big_block(a, n_tiles, kt_plan, n_cu, m_tile_rows(a), NCOLS, wk, ti, sg)) return;
   const int ncol0 = wk.nt * NCOLS;
   if constexpr (EPI == EPI_SWIGLU) {
     if (sg.a_wide) {  // A in 64-column planes (checked by the launcher: K % 64 == 0)
@@ -1118,7 +1124,7 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm_big_fp8_kernel(GemmArgs a, i
   TileInfo ti;
   Seg sg;
   constexpr int NCOLS = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  if (!big_block<BM>(a, n_tiles, kt_plan, n_cu, NCOLS, wk, ti, sg)) return;
+  if (!big_block(a, n_tiles, kt_plan, n_cu, BM, NCOLS, wk, ti, sg)) return;
   const int ncol0 = wk.nt * NCOLS;
   switch (tile_layout(ti.nrows)) {
     case 2: big_tile_fp8<BN, WN, EPI, 2>(a, ti, sg, wk, ncol0, lds, lds_sc); break;
@@ -1243,7 +1249,7 @@ int device_cus() {
 template <int BN, int EPI, int WDT, bool FP8ACT = false, int WN = MOE_BIG_WN>
 hipError_t launch_big(const GemmArgs& a_in, hipStream_t s) {
   GemmArgs a = a_in;
-  const int n_slots = a.tile_table ? a.n_slots : (a.rows + BM - 1) / BM;
+  const int n_slots = a.tile_table ? a.n_slots : (a.rows + m_tile_rows(a) - 1) / m_tile_rows(a);
   const int ncol = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int n_tiles = (gemm_max_cols(a) + ncol - 1) / ncol;
   const int kt_plan = (a.sh_rows > 0 ? min(a.K, a.shK) : a.K) / (FP8ACT ? BK8 : BK);

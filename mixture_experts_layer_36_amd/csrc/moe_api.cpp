@@ -140,6 +140,32 @@ struct RouteWs {
   float* cand_w;
 };
 
+// The router GEMM on the prefill kernel: tiles of 256 rows (or 128), 256 or
+// 128 experts wide, K split until one wave of the GPU is filled, each range
+// at least 8 stages of 32 and the partial sums at most twice the input.
+// 128-row tiles where 256-row ones would need ranges shorter than 32 stages:
+// the tile's fixed cost then outweighs its loop (Qwen-shaped route, 16-stage
+// ranges: 52 -> 43 us on 128-row tiles; DeepSeek-V3-shaped, 56-stage ranges:
+// 141 -> 152 us on them).
+struct RouterPlan {
+  int rows, ksplit;
+};
+RouterPlan big_router_plan(const moe_desc* d) {
+  const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
+  const int64_t part_bytes = int64_t(d->T) * d->E * 4;
+  const int bn = d->E % 256 == 0 ? 256 : 128;
+  RouterPlan p{256, 1};
+  for (int rows : {256, 128}) {
+    const int64_t tiles = int64_t((d->T + rows - 1) / rows) * ((d->E + bn - 1) / bn);
+    int64_t want = (256 + tiles - 1) / tiles;
+    want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
+    want = std::min<int64_t>(want, std::max<int64_t>(1, d->d / 256));
+    p = RouterPlan{rows, int(std::max<int64_t>(1, std::min<int64_t>(want, 16)))};
+    if ((d->d / 32) / p.ksplit >= 32) break;
+  }
+  return p;
+}
+
 // Split-K factor of the router GEMM: enough blocks to fill the GPU when T*E
 // is small (decode, few experts), bounded so the fp32 partial sums stay small
 // next to the inputs.  K / ksplit stays a multiple of the 64-wide k step.
@@ -154,17 +180,7 @@ int route_splits(const moe_desc* d) {
   const int bm = gemm_block_m(g);
   const int64_t in_bytes = (int64_t(d->T) + d->E) * d->d * 2;
   const int64_t part_bytes = int64_t(d->T) * d->E * 4;
-  if (bm == 256) {
-    // 256-row tiles, 256 or 128 wide: split K until one wave of the GPU is
-    // filled, each range at least 8 stages of 32, the partial sums at most
-    // twice the input
-    const int bn = d->E % 256 == 0 ? 256 : 128;
-    const int64_t tiles = int64_t((d->T + 255) / 256) * ((d->E + bn - 1) / bn);
-    int64_t want = (256 + tiles - 1) / tiles;
-    want = std::min<int64_t>(want, std::max<int64_t>(1, 2 * in_bytes / std::max<int64_t>(part_bytes, 1)));
-    want = std::min<int64_t>(want, std::max<int64_t>(1, d->d / 256));
-    return int(std::max<int64_t>(1, std::min<int64_t>(want, 16)));
-  }
+  if (bm == 256) return big_router_plan(d).ksplit;
   const int64_t tiles = int64_t((d->T + 127) / 128) * ((d->E + 127) / 128);
   const int64_t kmax = d->d / 64;
   int64_t want = (1024 + tiles - 1) / tiles;
@@ -364,6 +380,7 @@ moe_status run_route(const moe_desc* d, const void* x, const void* wr, const flo
   g.wdt = gemm_dtype(d->act);
   g.epi = EPI_BIAS_F32;
   g.ksplit = ws.ksplit;
+  g.m_tile = big_router_plan(d).rows;  // used by the prefill kernel only
   MOE_TRY(dev(launch_gemm(g, s)));
   RouteSelectArgs r{ws.z, ws.ksplit, d->T, d->E, d->k, d->score, d->renorm, d->n_group, d->topk_group,
                     idx, w, ws.cand_idx, ws.cand_w};

@@ -254,6 +254,9 @@ struct GemmArgs {
   // records than blocks: every block derives its own.
   int32_t* sched;
   int sched_cap;
+  // Prefill kernel without a tile table (the router logits): rows per m-tile,
+  // 256 or 128 (0: 256).
+  int m_tile;
 };
 constexpr int kSchedInts = 8;
 
