@@ -248,3 +248,16 @@ def test_noalloc_dispatch_validates_before_touching_a_gpu():
     assert lib.moe_dispatch_noalloc(ctypes.byref(rr), ok, ok, ok, ok, ok, ok, ok, null) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_dispatch_noalloc(ctypes.byref(_good()), ok, ok, null, ok, ok, ok, ok, null) == \
         moe.MOE_ERR_INVALID
+
+
+def test_router_plan_on_the_prefill_kernel():
+    # The route stage's workspace is the router's K-split partial sums,
+    # ksplit x T x E fp32.  The DeepSeek-V3-shaped prefill layer keeps
+    # 256-row router tiles with K split four ways (ranges of 56 stages); the
+    # Qwen-shaped layer takes 128-row tiles and four ranges of 32 stages,
+    # where filling the GPU with 256-row tiles would have needed eight ranges
+    # of 16.
+    from synth import BY_NAME
+    for name in ("dsv3_prefill_skew_bf16", "qwen_moe_fp8_skew"):
+        w = BY_NAME[name]
+        assert moe.workspace_size(moe.Desc.from_attrs(w), moe.STAGE_ROUTE) == 4 * w.T * w.E * 4, name
